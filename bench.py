@@ -1,0 +1,251 @@
+"""Benchmark of the scheduled-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the whole hot path on one batch of synthetic input that
+is already resident in HBM: the GPU schedule build from lane (0, 0)'s keys
+(centroids, distances, MST + elder rule + top-k + CSR) followed by the
+scheduled attention forward over every lane.  Prints ONE JSON line.
+
+value = visited-block flops (4 * 64 * 64 * D per visited block and lane, full
+tiles) / step time, in TFLOP/s.  The attention kernel is also timed on its own
+(HIP events on the stream it runs on, around every launch in the timed region)
+for the roofline entry, and the same kernel over the dense causal CSR gives the
+sparse-vs-dense-CSR speedup.  The fp64 CPU oracle is timed on a bounded sample
+of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scheduled-attn fwd effective TFLOP/s (% MFMA peak) + sparse/dense-CSR speedup"
+PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_causal_amd", "csrc", "attention_fwd.hip")
+
+
+def _kernel_hash() -> str:
+    with open(ATTN_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per attention launch from a committed rocprofv3 --pmc summary,
+    only if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"attention_fwd_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256_16") != _kernel_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the oracle on the host: schedule build (all pairs) + dense masked
+    attention lane by lane until the time budget is used (at least one lane)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    ql, kl, vl = (t.reshape(-1, w.S, w.D) for t in (q, k, v))
+    t0 = time.perf_counter()
+    if w.dense:
+        rp, ci = oracle.dense_causal_schedule(w.nb)
+    else:
+        rp, ci, _ = oracle.build_schedule(kl[0], 64, w.sink, w.local_radius, w.topk)
+    lanes = 0
+    for lane in range(ql.shape[0]):
+        oracle.masked_attention(ql[lane], kl[lane], vl[lane], rp, ci, 64)
+        lanes += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = lanes * int(ci.shape[0]) * 4 * 64 * 64 * w.D
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"schedule build + {lanes} of {ql.shape[0]} lanes (all {w.S} rows each) in {dt:.1f} s; "
+                  f"visited-block flops of those lanes / wall time; host has {os.cpu_count()} cpus",
+        "seconds": dt,
+        "lanes": lanes,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import block_sparse_causal_amd as tsa
+    import workloads
+
+    name = args.workload or workloads.BENCH_WORKLOAD
+    w = workloads.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q_cpu, k_cpu, v_cpu = workloads.make_qkv(w)
+    q, k, v = (t.to(dev) for t in (q_cpu, k_cpu, v_cpu))
+    keys = k.reshape(-1, w.S, w.D)[0]
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    if w.dense:
+        bufs = None
+        rp, ci = tsa.dense_causal_schedule(w.nb, dev)
+
+        def step():
+            tsa.dense_causal_schedule(w.nb, dev)
+    else:
+        bufs = tsa.ScheduleBuffers(w.S, w.D, w.sink, w.local_radius, w.topk, dev)
+        rp, ci = bufs.row_ptr, bufs.col_idx
+
+        def step():
+            tsa.build_schedule_into(keys, bufs)
+
+    def attention():
+        tsa.scheduled_attention(q, k, v, rp, ci, out=out)
+
+    print(f"# workload {name}: shape {w.shape} {w.dtype}; warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+        attention()
+    torch.cuda.synchronize()
+    nnz = int(rp[-1].item())
+    lanes = w.lanes
+    flops = lanes * nnz * 4 * 64 * 64 * w.D
+    diag = w.nb
+    flops_exact = lanes * 4 * w.D * (64 * 64 * (nnz - diag) + diag * (64 * 65 // 2))
+
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step()
+        ev_a[i].record(stream)
+        attention()
+        ev_b[i].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = start.elapsed_time(end) / args.steps
+    attn_ms_each = sorted(a.elapsed_time(b) for a, b in zip(ev_a, ev_b))
+    attn_ms = sum(attn_ms_each) / len(attn_ms_each)
+    print(f"# timed {args.steps} steps in {wall:.3f} s wall", file=sys.stderr, flush=True)
+
+    # Same kernel over the dense causal CSR at the same shape (like-for-like baseline).
+    drp, dci = tsa.dense_causal_schedule(w.nb, dev)
+    for _ in range(max(3, args.warmup // 2)):
+        tsa.scheduled_attention(q, k, v, drp, dci, out=out)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(5, args.steps // 2)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for _ in range(reps):
+        tsa.scheduled_attention(q, k, v, drp, dci, out=out)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = d0.elapsed_time(d1) / reps
+    if not bool(torch.isfinite(out).all()):
+        print("non-finite output", file=sys.stderr)
+        return 1
+
+    peak = PEAK_TFLOPS[w.dtype]
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    value = flops / (step_ms * 1e-3) / 1e12
+    traffic = _traffic(name)
+    nnz_dense = w.nb * (w.nb + 1) // 2
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "shape": list(w.shape),
+            "block": 64,
+            "sink": None if w.dense else w.sink,
+            "local_radius": None if w.dense else w.local_radius,
+            "topk": None if w.dense else w.topk,
+            "schedule": "dense causal CSR" if w.dense else "topology (GPU-built each step)",
+            "nnz_blocks": nnz,
+            "dense_blocks": nnz_dense,
+            "parallelism": "single GPU",
+        },
+        "frac_of_peak": round(value / peak, 4),
+        "attention_ms": round(attn_ms, 5),
+        "attention_ms_min": round(attn_ms_each[0], 5),
+        "builder_ms": round(step_ms - attn_ms, 5),
+        "attention_tflops": round(attn_tflops, 3),
+        "attention_frac_of_peak": round(attn_tflops / peak, 4),
+        "attention_tflops_causal_exact": round(flops_exact / (attn_ms * 1e-3) / 1e12, 3),
+        "dense_csr_ms": round(dense_ms, 5),
+        "sparse_vs_dense_csr_speedup": round(dense_ms / attn_ms, 3),
+        "ideal_speedup": round(nnz_dense / nnz, 3),
+        "dense_csr_tflops": round(lanes * nnz_dense * 4 * 64 * 64 * w.D / (dense_ms * 1e-3) / 1e12, 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / peak, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"# timing the fp64 oracle for about {args.cpu_budget:.0f} s", file=sys.stderr, flush=True)
+        cb = _cpu_baseline(w, q_cpu, k_cpu, v_cpu, args.cpu_budget)
+        result["cpu_baseline"] = {key: cb[key] for key in ("value", "unit", "cores", "kind", "sample")}
+        result["cpu_baseline"]["value"] = round(cb["value"], 6)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

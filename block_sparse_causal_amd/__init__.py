@@ -1,0 +1,280 @@
+"""Topology-scheduled block-sparse causal attention for AMD Instinct MI355X.
+
+Thin Python binding over ``libtsa.so`` (C ABI in ``include/tsa.h``).  This module
+only marshals arguments: it turns torch tensors into device pointers, sizes and
+the current HIP stream, allocates outputs and workspaces with torch, and maps
+status codes to exceptions.  Every step of the computation runs in the HIP
+kernels of the library.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+
+Operations (pages "Add topology-derived sparse attention kernel",
+triton-lang/kernels PR 22, Summary):
+
+* ``build_schedule``       sink + local window + top-k salient key blocks -> CSR
+* ``dense_causal_schedule`` the lower-triangular CSR
+* ``scheduled_attention``  forward causal attention over a CSR block schedule
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BLOCK",
+    "TsaError",
+    "library_path",
+    "schedule_max_nnz",
+    "build_schedule",
+    "ScheduleBuffers",
+    "build_schedule_into",
+    "dense_causal_schedule",
+    "scheduled_attention",
+]
+
+BLOCK = 64
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libtsa.so")
+
+TSA_OK = 0
+_STATUS_NAMES = {
+    -1: "TSA_ERR_INVALID_ARG",
+    -2: "TSA_ERR_UNSUPPORTED",
+    -3: "TSA_ERR_SHAPE",
+    -4: "TSA_ERR_SCHEDULE",
+    -5: "TSA_ERR_DEVICE",
+    -6: "TSA_ERR_HIP",
+}
+_DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+
+
+class TsaError(RuntimeError):
+    """A libtsa call failed inside the HIP runtime."""
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m block_sparse_causal_amd.build` "
+            "(this package has no non-HIP code path)"
+        )
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.tsa_version.restype = ctypes.c_int
+    lib.tsa_version.argtypes = []
+    lib.tsa_last_error.restype = ctypes.c_char_p
+    lib.tsa_last_error.argtypes = []
+    lib.tsa_schedule_max_nnz.restype = i64
+    lib.tsa_schedule_max_nnz.argtypes = [i64, i32, i32, i32]
+    lib.tsa_build_schedule_workspace_bytes.restype = sz
+    lib.tsa_build_schedule_workspace_bytes.argtypes = [i64, i64, i32]
+    lib.tsa_build_schedule.restype = ctypes.c_int
+    lib.tsa_build_schedule.argtypes = [
+        vp, i32, i64, i64, i32, i32, i32, i32, vp, vp, i64, vp, vp, sz, ctypes.POINTER(i64), vp
+    ]
+    lib.tsa_dense_causal_schedule.restype = ctypes.c_int
+    lib.tsa_dense_causal_schedule.argtypes = [i64, vp, vp, i64, vp]
+    lib.tsa_scheduled_attention_fwd.restype = ctypes.c_int
+    lib.tsa_scheduled_attention_fwd.argtypes = [
+        vp, vp, vp, vp, i32, i64, i64, i64, i64, vp, vp, i64, i32, ctypes.c_float, vp
+    ]
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    """Path of the loaded native library."""
+    return _LIB_PATH
+
+
+def _check(status: int, what: str) -> None:
+    if status == TSA_OK:
+        return
+    msg = _lib.tsa_last_error().decode(errors="replace")
+    name = _STATUS_NAMES.get(status, str(status))
+    if status == -6:
+        raise TsaError(f"{what}: {name}: {msg}")
+    raise ValueError(f"{what}: {name}: {msg}")
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else None)
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be float16 or bfloat16, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def schedule_max_nnz(nb: int, sink: int, local_radius: int, topk: int) -> int:
+    """Upper bound on the entries a built schedule can hold (host arithmetic in libtsa)."""
+    n = _lib.tsa_schedule_max_nnz(nb, sink, local_radius, topk)
+    if n < 0:
+        _check(-1, "schedule_max_nnz")
+    return int(n)
+
+
+def build_schedule(keys: torch.Tensor, block: int = BLOCK, sink: int = 1, local_radius: int = 1,
+                   topk: int = 2, return_salience: bool = False):
+    """Topology-derived CSR schedule from the keys of lane (0, 0).
+
+    keys: [S, D] or [B, H, S, D] float16/bfloat16 on a GPU.  Returns int32
+    (row_ptr [nb+1], col_idx [nnz]) on the keys' device, plus the fp64 salience
+    [nb] when ``return_salience``.  Waits for the stream to read back nnz.
+    """
+    if not isinstance(keys, torch.Tensor):
+        raise TypeError("keys must be a torch.Tensor")
+    if keys.dim() == 4:
+        keys = keys[0, 0]
+    if keys.dim() != 2:
+        raise ValueError(f"keys must be [S, D] or [B, H, S, D], got {tuple(keys.shape)}")
+    if not keys.is_cuda:
+        raise ValueError("keys must be on a GPU device")
+    if not keys.is_contiguous():
+        raise ValueError("keys (lane 0, 0) must be contiguous")
+    code = _dtype_code(keys, "keys")
+    S, D = keys.shape
+    dev = keys.device
+    nb = -(-S // BLOCK)
+    cap = schedule_max_nnz(nb, sink, local_radius, topk) if min(sink, local_radius, topk) >= 0 else 0
+    ws_bytes = _lib.tsa_build_schedule_workspace_bytes(S, D, block)
+    with torch.cuda.device(dev):
+        row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        sal = torch.empty(max(nb, 1), dtype=torch.float64, device=dev) if return_salience else None
+        ws = torch.empty(max(int(ws_bytes), 1) + 256, dtype=torch.uint8, device=dev)
+        base = ws.data_ptr()
+        aligned = (base + 255) // 256 * 256
+        nnz = ctypes.c_int64(0)
+        status = _lib.tsa_build_schedule(
+            _ptr(keys), code, S, D, block, sink, local_radius, topk, _ptr(row_ptr),
+            _ptr(col_idx), cap, _ptr(sal), ctypes.c_void_p(aligned), int(ws_bytes),
+            ctypes.byref(nnz), _stream(dev),
+        )
+    _check(status, "build_schedule")
+    out = (row_ptr, col_idx[: nnz.value])
+    if return_salience:
+        out = out + (sal[:nb],)
+    return out
+
+
+class ScheduleBuffers:
+    """Preallocated device buffers for repeated schedule builds of one shape.
+
+    Holds row_ptr [nb+1], col_idx at its capacity bound, an optional salience
+    [nb] and the builder workspace, so ``build_schedule_into`` allocates
+    nothing and never waits for the stream.
+    """
+
+    def __init__(self, S: int, D: int, sink: int, local_radius: int, topk: int, device,
+                 salience: bool = False):
+        dev = torch.device(device)
+        self.S, self.D, self.sink, self.local_radius, self.topk = S, D, sink, local_radius, topk
+        self.nb = -(-S // BLOCK)
+        self.capacity = schedule_max_nnz(self.nb, sink, local_radius, topk)
+        self.ws_bytes = int(_lib.tsa_build_schedule_workspace_bytes(S, D, BLOCK))
+        if self.ws_bytes == 0 and self.nb > 0:
+            _check(-2, "ScheduleBuffers: unsupported size")
+        self.row_ptr = torch.empty(self.nb + 1, dtype=torch.int32, device=dev)
+        self.col_idx = torch.empty(max(self.capacity, 1), dtype=torch.int32, device=dev)
+        self.salience = torch.empty(max(self.nb, 1), dtype=torch.float64, device=dev) if salience else None
+        self._ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=dev)
+        self.ws_ptr = (self._ws.data_ptr() + 255) // 256 * 256
+
+
+def build_schedule_into(keys: torch.Tensor, bufs: ScheduleBuffers) -> None:
+    """Queue a schedule build into ``bufs`` on the current stream (no host wait).
+
+    keys: [S, D] (lane 0, 0) float16/bfloat16, contiguous, matching ``bufs``.
+    Entries past row_ptr[nb] in ``bufs.col_idx`` are unspecified.
+    """
+    if keys.dim() == 4:
+        keys = keys[0, 0]
+    if tuple(keys.shape) != (bufs.S, bufs.D) or not keys.is_contiguous() or not keys.is_cuda:
+        raise ValueError("keys must be a contiguous GPU tensor of the buffers' [S, D]")
+    code = _dtype_code(keys, "keys")
+    with torch.cuda.device(keys.device):
+        status = _lib.tsa_build_schedule(
+            _ptr(keys), code, bufs.S, bufs.D, BLOCK, bufs.sink, bufs.local_radius, bufs.topk,
+            _ptr(bufs.row_ptr), _ptr(bufs.col_idx), bufs.capacity, _ptr(bufs.salience),
+            ctypes.c_void_p(bufs.ws_ptr), bufs.ws_bytes, None, _stream(keys.device),
+        )
+    _check(status, "build_schedule_into")
+
+
+def dense_causal_schedule(nb: int, device) -> tuple[torch.Tensor, torch.Tensor]:
+    """Lower-triangular CSR for nb blocks on ``device`` (int32 row_ptr, col_idx)."""
+    dev = torch.device(device)
+    nnz = nb * (nb + 1) // 2
+    with torch.cuda.device(dev):
+        row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        status = _lib.tsa_dense_causal_schedule(nb, _ptr(row_ptr), _ptr(col_idx), nnz, _stream(dev))
+    _check(status, "dense_causal_schedule")
+    return row_ptr, col_idx[:nnz]
+
+
+def scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                        col_idx: torch.Tensor, block: int = BLOCK, sm_scale: float | None = None,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """Forward scheduled attention; returns a tensor of q's shape and dtype.
+
+    q, k, v: [S, D] or [B, H, S, D], one float16/bfloat16 dtype, contiguous, on
+    one GPU.  row_ptr/col_idx: int32 CSR on the same device, shared by every
+    (b, h) lane.  sm_scale defaults to 1/sqrt(D).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share a shape, got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    code = _dtype_code(q, "q")
+    if q.dim() == 2:
+        B, H, (S, D) = 1, 1, q.shape
+    elif q.dim() == 4:
+        B, H, S, D = q.shape
+    else:
+        raise ValueError(f"q must be [S, D] or [B, H, S, D], got {tuple(q.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32, got {t.dtype}")
+        if t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 1-D tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q is on {q.device}")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    nb = -(-S // BLOCK)
+    if row_ptr.numel() != nb + 1:
+        raise ValueError(f"row_ptr must have nb+1 = {nb + 1} entries for S={S}, got {row_ptr.numel()}")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
+    scale = 0.0 if sm_scale is None else float(sm_scale)
+    if sm_scale is not None and scale <= 0:
+        raise ValueError("sm_scale must be positive")
+    with torch.cuda.device(q.device):
+        status = _lib.tsa_scheduled_attention_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), code, B, H, S, D, _ptr(row_ptr), _ptr(col_idx),
+            col_idx.numel(), block, scale, _stream(q.device),
+        )
+    _check(status, "scheduled_attention")
+    return out

@@ -1,0 +1,31 @@
+// Internal launchers of libtsa (not part of the C ABI).  Each returns the
+// hipError_t of its launch; argument checking is done by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsa {
+
+// Scheduled attention forward over `lanes` lanes of [S, D] (D = 64 or 128).
+hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* out,
+                                bool bf16, int64_t lanes, int64_t S, int D,
+                                const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                float scale_log2, hipStream_t stream);
+
+// Schedule builder: centroids -> distances -> MST -> elder rule -> top-k -> CSR.
+struct ScheduleWorkspace {
+  double* centroids;  // [nb, D]
+  double* dist;       // [nb, nb], only when nb > kLdsDistBlocks
+};
+constexpr int kLdsDistBlocks = 128;  // distance matrix kept in LDS up to this many blocks
+size_t schedule_workspace_bytes(int64_t nb, int64_t D);
+hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t D, int sink,
+                                 int local_radius, int topk, int32_t* row_ptr, int32_t* col_idx,
+                                 int64_t col_capacity, double* salience, void* workspace,
+                                 hipStream_t stream);
+
+hipError_t launch_dense_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,
+                                 hipStream_t stream);
+
+}  // namespace tsa

@@ -1,0 +1,216 @@
+// C ABI of libtsa: argument checking, error reporting and dispatch to the HIP
+// launchers.  Every check that needs no GPU runs before any HIP call, so the
+// validation paths are usable (and tested) on hosts without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/tsa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return TSA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TSA_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+// The pointer must be device (or managed) memory that lives on the current device.
+int check_device_ptr(const void* p, const char* name) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipPointerAttribute_t attr;
+  e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return fail(TSA_ERR_DEVICE, "%s is not a HIP allocation", name);
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(TSA_ERR_DEVICE, "%s is not device memory", name);
+  if (attr.device != dev)
+    return fail(TSA_ERR_DEVICE, "%s lives on device %d, current device is %d", name, attr.device,
+                dev);
+  return TSA_OK;
+}
+
+int64_t row_cap(int32_t sink, int32_t local_radius, int32_t topk) {
+  return (int64_t)sink + (int64_t)local_radius + 1 + (int64_t)topk;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tsa_version(void) { return 100; }
+
+const char* tsa_last_error(void) { return g_last_error.c_str(); }
+
+int64_t tsa_schedule_max_nnz(int64_t nb, int32_t sink, int32_t local_radius, int32_t topk) {
+  if (nb < 0 || sink < 0 || local_radius < 0 || topk < 0) {
+    fail(TSA_ERR_INVALID_ARG, "tsa_schedule_max_nnz: arguments must be >= 0");
+    return -1;
+  }
+  const int64_t cap = row_cap(sink, local_radius, topk);
+  // rows i < cap hold i + 1 entries; the remaining rows hold cap entries
+  const int64_t full = nb < cap ? nb : cap;
+  return full * (full + 1) / 2 + (nb - full) * cap;
+}
+
+size_t tsa_build_schedule_workspace_bytes(int64_t S, int64_t D, int32_t block) {
+  if (S < 0 || D <= 0 || block != TSA_BLOCK) return 0;
+  const int64_t nb = (S + TSA_BLOCK - 1) / TSA_BLOCK;
+  if (nb > TSA_MAX_SCHEDULE_BLOCKS) return 0;
+  return tsa::schedule_workspace_bytes(nb, D) + 256;
+}
+
+int tsa_build_schedule(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
+                       int32_t sink, int32_t local_radius, int32_t topk, int32_t* row_ptr,
+                       int32_t* col_idx, int64_t col_capacity, double* salience, void* workspace,
+                       size_t workspace_bytes, int64_t* nnz_host, void* stream) {
+  if (dtype != TSA_F16 && dtype != TSA_BF16)
+    return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: dtype must be TSA_F16 or TSA_BF16");
+  if (S < 0 || D <= 0)
+    return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: need S >= 0 and D > 0 (S=%lld D=%lld)",
+                (long long)S, (long long)D);
+  if (sink < 0 || local_radius < 0 || topk < 0)
+    return fail(TSA_ERR_INVALID_ARG,
+                "tsa_build_schedule: sink, local_radius and topk must be >= 0 (%d, %d, %d)", sink,
+                local_radius, topk);
+  if (block != TSA_BLOCK)
+    return fail(TSA_ERR_UNSUPPORTED, "tsa_build_schedule: block must be %d, got %d", TSA_BLOCK,
+                block);
+  const int64_t nb = (S + TSA_BLOCK - 1) / TSA_BLOCK;
+  if (nb > TSA_MAX_SCHEDULE_BLOCKS)
+    return fail(TSA_ERR_UNSUPPORTED, "tsa_build_schedule: %lld blocks exceed the limit of %d",
+                (long long)nb, TSA_MAX_SCHEDULE_BLOCKS);
+  if (D > (int64_t(1) << 20))
+    return fail(TSA_ERR_SHAPE, "tsa_build_schedule: D=%lld too large", (long long)D);
+  if (row_ptr == nullptr) return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: row_ptr is NULL");
+  const int64_t need = tsa_schedule_max_nnz(nb, sink, local_radius, topk);
+  if (col_capacity < need)
+    return fail(TSA_ERR_SCHEDULE, "tsa_build_schedule: col_capacity %lld < required %lld",
+                (long long)col_capacity, (long long)need);
+  if (need > INT32_MAX)
+    return fail(TSA_ERR_SHAPE, "tsa_build_schedule: schedule would exceed int32 offsets");
+  if (nb > 0) {
+    if (keys == nullptr || col_idx == nullptr || workspace == nullptr)
+      return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: keys, col_idx and workspace must be non-NULL");
+    const size_t ws = tsa::schedule_workspace_bytes(nb, D);
+    if (workspace_bytes < ws)
+      return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: workspace of %zu bytes < required %zu",
+                  workspace_bytes, ws);
+    if (((uintptr_t)workspace) % 256 != 0)
+      return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: workspace must be 256-byte aligned");
+  }
+  int rc;
+  if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
+  if (nb > 0) {
+    if ((rc = check_device_ptr(keys, "keys")) != TSA_OK) return rc;
+    if ((rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
+    if ((rc = check_device_ptr(workspace, "workspace")) != TSA_OK) return rc;
+    if (salience && (rc = check_device_ptr(salience, "salience")) != TSA_OK) return rc;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = tsa::launch_build_schedule(keys, dtype == TSA_BF16, S, D, sink, local_radius, topk,
+                                            row_ptr, col_idx, col_capacity, salience, workspace, st);
+  if (e != hipSuccess) return hip_fail(e, "schedule kernels");
+  if (nnz_host) {
+    int32_t n = 0;
+    e = hipMemcpyAsync(&n, row_ptr + nb, sizeof n, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "reading nnz");
+    *nnz_host = n;
+  }
+  return ok();
+}
+
+int tsa_dense_causal_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,
+                              int64_t col_capacity, void* stream) {
+  if (nb < 0) return fail(TSA_ERR_INVALID_ARG, "tsa_dense_causal_schedule: nb must be >= 0");
+  const int64_t need = nb * (nb + 1) / 2;
+  if (need > INT32_MAX)
+    return fail(TSA_ERR_SHAPE, "tsa_dense_causal_schedule: %lld entries exceed int32 offsets",
+                (long long)need);
+  if (col_capacity < need)
+    return fail(TSA_ERR_SCHEDULE, "tsa_dense_causal_schedule: col_capacity %lld < %lld",
+                (long long)col_capacity, (long long)need);
+  if (row_ptr == nullptr || (nb > 0 && col_idx == nullptr))
+    return fail(TSA_ERR_INVALID_ARG, "tsa_dense_causal_schedule: NULL output");
+  int rc;
+  if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
+  if (nb > 0 && (rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
+  hipError_t e = tsa::launch_dense_schedule(nb, row_ptr, col_idx, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dense schedule kernel");
+  return ok();
+}
+
+int tsa_scheduled_attention_fwd(const void* q, const void* k, const void* v, void* out,
+                                int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                                const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                int32_t block, float sm_scale, void* stream) {
+  if (dtype != TSA_F16 && dtype != TSA_BF16)
+    return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: dtype must be TSA_F16 or TSA_BF16");
+  if (B < 0 || H < 0 || S < 0 || nnz < 0)
+    return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: B, H, S and nnz must be >= 0");
+  if (block != TSA_BLOCK)
+    return fail(TSA_ERR_UNSUPPORTED, "tsa_scheduled_attention_fwd: block must be %d, got %d",
+                TSA_BLOCK, block);
+  if (D != 64 && D != 128)
+    return fail(TSA_ERR_UNSUPPORTED, "tsa_scheduled_attention_fwd: head dim must be 64 or 128, got %lld",
+                (long long)D);
+  if (std::isnan(sm_scale) || std::isinf(sm_scale))
+    return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: sm_scale must be finite");
+  if (S > INT32_MAX - TSA_BLOCK)
+    return fail(TSA_ERR_SHAPE, "tsa_scheduled_attention_fwd: S=%lld too large", (long long)S);
+  if (B > 0 && H > INT64_MAX / B)
+    return fail(TSA_ERR_SHAPE, "tsa_scheduled_attention_fwd: B*H overflows");
+  const int64_t lanes = B * H;
+  if (lanes > 0 && S > 0 && lanes > INT64_MAX / (S * D))
+    return fail(TSA_ERR_SHAPE, "tsa_scheduled_attention_fwd: B*H*S*D overflows");
+  const int64_t nb = (S + TSA_BLOCK - 1) / TSA_BLOCK;
+  if (lanes == 0 || S == 0) return ok();  // empty problem: nothing to read or write
+  if (!q || !k || !v || !out || !row_ptr || (nnz > 0 && !col_idx))
+    return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: NULL pointer argument");
+  const size_t bytes = (size_t)(lanes * S * D) * 2;
+  const char* o0 = (const char*)out;
+  const char* ins[3] = {(const char*)q, (const char*)k, (const char*)v};
+  for (const char* p : ins)
+    if (o0 < p + bytes && p < o0 + bytes)
+      return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: out overlaps an input");
+  int rc;
+  if ((rc = check_device_ptr(q, "q")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(k, "k")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(v, "v")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(out, "out")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
+  if (nnz > 0 && (rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
+  const double scale = sm_scale > 0.0f ? (double)sm_scale : 1.0 / std::sqrt((double)D);
+  const float scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
+  (void)nb;
+  hipError_t e = tsa::launch_attention_fwd(q, k, v, out, dtype == TSA_BF16, lanes, S, (int)D,
+                                           row_ptr, col_idx, nnz, scale_log2, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
+}
+
+}  // extern "C"

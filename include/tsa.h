@@ -1,0 +1,163 @@
+/*
+ * tsa.h -- C ABI of libtsa: topology-scheduled block-sparse causal attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the pages "Add topology-derived sparse attention
+ * kernel" (triton-lang/kernels pull request 22) and its mirror page:
+ *   - a forward-only causal attention that consumes a CSR block schedule
+ *     (Summary, first bullet), for [S, D] and [B, H, S, D] inputs with one
+ *     schedule shared by every batch/head lane (third bullet), whose output has
+ *     the input dtype (fourth bullet);
+ *   - a schedule builder that takes sink blocks, local-window blocks and the
+ *     top-k key blocks ranked by a 0D-persistence salience of the key-block
+ *     centroids (second bullet), elder-rule salience as described in the
+ *     mirror page's Rust-port commit note, computed from MST edges as in its
+ *     schedule.py commit note;
+ *   - the dense causal CSR used as the like-for-like baseline (Local benchmark).
+ *
+ * Conventions shared by every entry point
+ *   - All functions are callable from C; none throws.  Status: 0 = TSA_OK,
+ *     negative = error.  On error nothing has been written to any output and
+ *     tsa_last_error() returns a message (thread-local, valid until the next
+ *     call on the same thread).
+ *   - Arguments are checked before any GPU work (the pages' "validate ... before
+ *     launch", Summary, fifth bullet): sizes and parameters first (no GPU call),
+ *     then every device pointer must be device memory on the current HIP device.
+ *   - Device pointers are owned by the caller; libtsa allocates nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is queued on it asynchronously unless a *_host output asks for a value
+ *     back, in which case the call waits for the stream.
+ *   - Tensors are dense row-major: [S, D] or [B, H, S, D] with D contiguous.
+ *     A lane is one (b, h) pair; lane l = b*H + h starts at element l*S*D.
+ *   - CSR schedule: row_ptr int32 [nb+1], col_idx int32 [nnz], nb = ceil(S/64).
+ *     Row i lists the key blocks query block i visits, strictly ascending,
+ *     each in 0..i.
+ */
+#ifndef TSA_H
+#define TSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define TSA_OK 0
+#define TSA_ERR_INVALID_ARG (-1) /* null pointer, negative size or parameter, bad dtype */
+#define TSA_ERR_UNSUPPORTED (-2) /* block != 64, head dim not 64/128, too many blocks */
+#define TSA_ERR_SHAPE (-3)       /* sizes that overflow or do not fit together */
+#define TSA_ERR_SCHEDULE (-4)    /* CSR arguments inconsistent (nnz, capacity) */
+#define TSA_ERR_DEVICE (-5)      /* a pointer is not device memory of the current device */
+#define TSA_ERR_HIP (-6)         /* a HIP runtime call or kernel launch failed */
+
+/* Element types of q/k/v/out and of the builder's keys. */
+#define TSA_F16 0
+#define TSA_BF16 1
+
+/* The only supported block size (rows per query block and per key block). */
+#define TSA_BLOCK 64
+/* Largest number of key blocks the schedule builder accepts (S <= 262144). */
+#define TSA_MAX_SCHEDULE_BLOCKS 4096
+
+/* Library version, e.g. 100 for 0.1.0. */
+int tsa_version(void);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* tsa_last_error(void);
+
+/*
+ * Upper bound on the entries the builder can emit for nb query blocks:
+ * sum over rows i of min(i + 1, sink + local_radius + 1 + topk).  Host-only.
+ * Returns -1 (and sets the error) for negative arguments.
+ */
+int64_t tsa_schedule_max_nnz(int64_t nb, int32_t sink, int32_t local_radius, int32_t topk);
+
+/*
+ * Device workspace, in bytes, that tsa_build_schedule needs for keys [S, D]
+ * and the given block size (256-byte aligned start required).  Host-only.
+ * Returns 0 for invalid sizes.
+ */
+size_t tsa_build_schedule_workspace_bytes(int64_t S, int64_t D, int32_t block);
+
+/*
+ * Build the topology-derived CSR schedule from one lane of keys.
+ * (PR page, Summary, second bullet; mirror page, Rust-port and schedule.py
+ * commit notes.)
+ *
+ *   keys        device, [S, D] of `dtype` (TSA_F16 / TSA_BF16), row-major.
+ *               For [B, H, S, D] inputs pass lane (0, 0).
+ *   block       must be 64.  nb = ceil(S / 64); a partial last block's centroid
+ *               is the mean of its valid rows.
+ *   sink, local_radius, topk   >= 0.  Row i lists every block j <= i with
+ *               j < sink, or j >= i - local_radius, or j among the topk blocks
+ *               of highest salience (ties: lower index; topk >= nb: all).
+ *   Salience: centroids c_j (fp64 mean of the block's keys); the minimum
+ *               spanning tree of the complete graph with Euclidean distances;
+ *               its edges taken in ascending (length, lower, higher index)
+ *               order through a union-find where the smaller component is
+ *               absorbed (equal sizes: the root with the larger index) and the
+ *               absorbed root's salience is the edge length.  One block, the
+ *               last survivor, scores 0.
+ *   row_ptr     device int32 [nb + 1], written.
+ *   col_idx     device int32 [col_capacity], entries [0, nnz) written.
+ *               col_capacity must be >= tsa_schedule_max_nnz(nb, sink,
+ *               local_radius, topk), so the build can never overflow it.
+ *   salience    device double [nb] or NULL; written when not NULL.
+ *   workspace   device, >= tsa_build_schedule_workspace_bytes(S, D, 64) bytes,
+ *               256-byte aligned; contents on return are unspecified.
+ *   nnz_host    host int64 or NULL.  When not NULL the call waits for the
+ *               stream and stores row_ptr[nb] (the number of entries) there.
+ *   S == 0 builds an empty schedule (row_ptr = {0}).
+ * Exact input ties between distances make the MST, and so the salience, depend
+ * on tie order; the result is then a valid elder-rule salience for one of the
+ * tied orders.
+ */
+int tsa_build_schedule(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
+                       int32_t sink, int32_t local_radius, int32_t topk, int32_t* row_ptr,
+                       int32_t* col_idx, int64_t col_capacity, double* salience, void* workspace,
+                       size_t workspace_bytes, int64_t* nnz_host, void* stream);
+
+/*
+ * The dense causal (lower-triangular) CSR for nb blocks: row i lists 0..i.
+ * (PR page, Summary: "dense causal CSR layout"; Local benchmark: the dense CSR
+ * path visits every causal block.)  row_ptr int32 [nb + 1] and col_idx int32
+ * [col_capacity >= nb*(nb+1)/2], both device memory.
+ */
+int tsa_dense_causal_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,
+                              int64_t col_capacity, void* stream);
+
+/*
+ * Forward scheduled attention.  (PR page, Summary, first, third and fourth
+ * bullets; mirror page, Rust-port commit note: running row max and denominator
+ * rescaled by exp(m_prev - m_new), one score tile live at a time.)
+ *
+ *   q, k, v, out  device, [B, H, S, D] row-major of `dtype` (out has q's dtype).
+ *                 [S, D] inputs are B = H = 1.  out must not overlap q, k, v.
+ *   D             64 or 128.
+ *   row_ptr, col_idx  device int32 CSR with nb = ceil(S/64) rows; `nnz` is the
+ *                 number of readable col_idx entries.  Row i must list key
+ *                 blocks strictly ascending within 0..i.  For memory safety the
+ *                 kernel clamps row bounds to [0, nnz] and skips entries that
+ *                 are negative, greater than i, or not greater than the
+ *                 previous accepted entry.
+ *   block         must be 64.
+ *   sm_scale      softmax scale; <= 0 selects 1/sqrt(D).
+ * For query row t in block i the output is the softmax-weighted mean of v over
+ * keys u <= t whose block is listed in row i; a row with no such key is 0.
+ * Scores and running statistics are fp32; the probabilities are rounded to the
+ * input dtype for the P*V product (the denominator is summed from the same
+ * rounded values); the output is rounded to nearest even.
+ * B, H or S equal to 0 is a valid empty call.
+ */
+int tsa_scheduled_attention_fwd(const void* q, const void* k, const void* v, void* out,
+                                int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                                const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                int32_t block, float sm_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSA_H */

@@ -1,0 +1,128 @@
+"""The C ABI library on any host: it loads, exports every declared entry point,
+and its host-side logic (capacity bound, workspace size, argument checks that
+precede any GPU call) behaves as include/tsa.h states.  No compute call is made.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import block_sparse_causal_amd as tsa
+
+    return tsa._lib
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for required in ("tsa_build_schedule", "tsa_scheduled_attention_fwd", "tsa_dense_causal_schedule",
+                     "tsa_schedule_max_nnz", "tsa_build_schedule_workspace_bytes", "tsa_last_error",
+                     "tsa_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_library_file_is_in_tree():
+    import block_sparse_causal_amd as tsa
+
+    assert os.path.dirname(tsa.library_path()) == os.path.join(ROOT, "block_sparse_causal_amd")
+
+
+@pytest.mark.parametrize("nb,s,r,k", [(16, 1, 1, 2), (64, 1, 1, 8), (64, 1, 2, 16), (512, 2, 4, 32),
+                                      (0, 1, 1, 1), (5, 0, 0, 0), (3, 10, 10, 10)])
+def test_max_nnz_bound(lib, nb, s, r, k):
+    brute = sum(min(i + 1, s + r + 1 + k) for i in range(nb))
+    assert lib.tsa_schedule_max_nnz(nb, s, r, k) == brute
+
+
+def test_max_nnz_bound_holds_for_oracle_schedules(lib):
+    import oracle
+
+    rng = np.random.default_rng(0)
+    for _ in range(20):
+        nb = int(rng.integers(1, 40))
+        s, r, k = (int(x) for x in rng.integers(0, 6, 3))
+        rp, _, _ = oracle.build_schedule(rng.standard_normal((64 * nb, 4)), 64, s, r, k)
+        assert rp[-1] <= lib.tsa_schedule_max_nnz(nb, s, r, k)
+
+
+def test_max_nnz_rejects_negative(lib):
+    assert lib.tsa_schedule_max_nnz(4, -1, 0, 0) == -1
+    assert b"must be" in lib.tsa_last_error()
+
+
+def test_workspace_bytes(lib):
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 64) >= 64 * 64 * 8 + 64 * 64 * 8
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 32) == 0
+    assert lib.tsa_build_schedule_workspace_bytes(64 * 5000, 64, 64) == 0
+
+
+def _fwd(lib, **kw):
+    args = dict(q=None, k=None, v=None, out=None, dtype=0, B=1, H=1, S=128, D=64, row_ptr=None,
+                col_idx=None, nnz=3, block=64, scale=0.0, stream=None)
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lib.tsa_scheduled_attention_fwd(
+        vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["out"]), args["dtype"], args["B"], args["H"],
+        args["S"], args["D"], vp(args["row_ptr"]), vp(args["col_idx"]), args["nnz"], args["block"],
+        args["scale"], vp(args["stream"]))
+
+
+def test_attention_argument_checks_before_gpu(lib):
+    assert _fwd(lib, dtype=5) == -1
+    assert _fwd(lib, B=-1) == -1
+    assert _fwd(lib, block=32) == -2
+    assert _fwd(lib, D=96) == -2
+    assert b"64 or 128" in lib.tsa_last_error()
+    assert _fwd(lib, scale=float("nan")) == -1
+    assert _fwd(lib) == -1  # NULL pointers for a non-empty problem
+    assert _fwd(lib, S=0) == 0  # empty problem is a no-op
+    assert _fwd(lib, B=0) == 0
+    assert lib.tsa_last_error() == b""
+
+
+def test_attention_rejects_overlapping_output(lib):
+    base = 1 << 40  # never dereferenced: the overlap check precedes any GPU call
+    st = _fwd(lib, q=base, k=base + (1 << 20), v=base + (2 << 20), out=base + 64, row_ptr=base, col_idx=base)
+    assert st == -1 and b"overlap" in lib.tsa_last_error()
+
+
+def test_builder_argument_checks_before_gpu(lib):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+
+    def call(dtype=0, S=1024, D=64, block=64, s=1, r=1, k=2, cap=1000, ws=1 << 20):
+        return lib.tsa_build_schedule(vp(None), dtype, S, D, block, s, r, k, vp(None), vp(None), cap,
+                                      vp(None), vp(None), ws, None, vp(None))
+
+    assert call(dtype=3) == -1
+    assert call(S=-1) == -1
+    assert call(s=-2) == -1
+    assert call(block=128) == -2
+    assert call(S=64 * 4097) == -2
+    assert call() == -1  # NULL row_ptr
+    assert b"row_ptr" in lib.tsa_last_error()
+
+
+def test_dense_schedule_argument_checks_before_gpu(lib):
+    vp = ctypes.c_void_p
+    assert lib.tsa_dense_causal_schedule(-1, vp(None), vp(None), 0, vp(None)) == -1
+    assert lib.tsa_dense_causal_schedule(10, vp(None), vp(None), 54, vp(None)) == -4
+    assert lib.tsa_dense_causal_schedule(10, vp(None), vp(None), 55, vp(None)) == -1
+    assert lib.tsa_dense_causal_schedule(70000, vp(None), vp(None), 1 << 40, vp(None)) == -3

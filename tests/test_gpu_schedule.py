@@ -1,0 +1,133 @@
+"""Parity of the HIP schedule builder with the fp64 all-pairs oracle.
+
+CSR row_ptr/col_idx must be bit-identical on inputs without near-ties (the
+workload seeds are checked for that in test_workloads.py); salience must match
+to a relative 1e-12 (fp64 distances summed in a different order).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tsa():
+    import block_sparse_causal_amd as mod
+
+    return mod
+
+
+def _compare(tsa, keys_cpu, sink, radius, topk, label=""):
+    rp_o, ci_o, sal_o = oracle.build_schedule(keys_cpu, 64, sink, radius, topk)
+    rp, ci, sal = tsa.build_schedule(keys_cpu.to("cuda:0"), 64, sink, radius, topk, return_salience=True)
+    assert rp.device.type == "cuda" and rp.dtype == torch.int32 and ci.dtype == torch.int32
+    rp, ci, sal = rp.cpu().numpy(), ci.cpu().numpy(), sal.cpu().numpy()
+    assert np.array_equal(rp, rp_o), label
+    assert np.array_equal(ci, ci_o), label
+    assert np.allclose(sal, sal_o, rtol=1e-12, atol=0), (label, np.max(np.abs(sal - sal_o)))
+    assert np.count_nonzero(sal == 0) == (1 if sal.shape[0] > 0 else 0)
+    return rp, ci
+
+
+@pytest.mark.parametrize("name", [n for n, w in workloads.WORKLOADS.items() if not w.dense])
+def test_workload_schedules_bit_exact(tsa, name):
+    w = workloads.WORKLOADS[name]
+    _, k, _ = workloads.make_qkv(w)
+    keys = k.reshape(-1, w.S, w.D)[0].contiguous()
+    rp, ci = _compare(tsa, keys, w.sink, w.local_radius, w.topk, name)
+    print(f"{name}: nnz {ci.shape[0]} of {w.nb * (w.nb + 1) // 2} causal blocks")
+
+
+def test_page_configuration_count_range(tsa):
+    """16 blocks, sink 1, radius 1, top-2: 45 + a term in [0, 27] (pages' port: 56 of 136)."""
+    counts = []
+    for seed in range(10):
+        keys = workloads.random_normal((1024, 64), "fp16", 1000 + seed)
+        rp, _ = _compare(tsa, keys, 1, 1, 2, f"seed {seed}")
+        counts.append(int(rp[-1]))
+    assert all(45 <= c <= 72 for c in counts), counts
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_small_configurations(tsa, seed):
+    rng = np.random.default_rng(seed)
+    nb = int(rng.integers(1, 21))
+    S = 64 * nb - int(rng.integers(0, 64)) if nb > 1 else int(rng.integers(1, 65))
+    D = int(rng.choice([8, 64, 128]))
+    dt = "bf16" if seed % 2 else "fp16"
+    sink, radius, topk = (int(x) for x in rng.integers(0, 5, 3))
+    keys = workloads.random_normal((S, D), dt, 2000 + seed, std=float(rng.choice([0.5, 1.0, 3.0])))
+    _compare(tsa, keys, sink, radius, topk, f"seed {seed} nb {nb} S {S}")
+
+
+@pytest.mark.parametrize("nb", [65, 130, 300, 700])
+def test_multi_slot_sizes(tsa, nb):
+    keys = workloads.random_normal((64 * nb - 5, 32), "bf16", 3000 + nb)
+    _compare(tsa, keys, 2, 3, 17, f"nb {nb}")
+
+
+def test_topk_at_least_nb_gives_dense(tsa):
+    keys = workloads.random_normal((64 * 9, 64), "fp16", 7)
+    rp, ci = tsa.build_schedule(keys.to("cuda:0"), 64, 0, 0, 9)
+    drp, dci = oracle.dense_causal_schedule(9)
+    assert np.array_equal(rp.cpu().numpy(), drp) and np.array_equal(ci.cpu().numpy(), dci)
+
+
+def test_four_dim_keys_use_lane_zero(tsa):
+    k = workloads.random_normal((2, 3, 64 * 10, 64), "bf16", 8)
+    a = tsa.build_schedule(k.to("cuda:0"), 64, 1, 1, 3)
+    b = tsa.build_schedule(k[0, 0].contiguous().to("cuda:0"), 64, 1, 1, 3)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_empty_keys_give_empty_schedule(tsa):
+    keys = torch.empty(0, 64, dtype=torch.float16, device="cuda:0")
+    rp, ci = tsa.build_schedule(keys, 64, 1, 1, 2)
+    assert rp.cpu().tolist() == [0] and ci.numel() == 0
+
+
+def test_hand_worked_elder_examples_on_gpu(tsa):
+    from conftest import read_golden_rows
+
+    for row in read_golden_rows("elder_rule_line_examples.txt"):
+        pos, expect = row.split("|")
+        xs = [float(x) for x in pos.split()]
+        keys = torch.zeros(64 * len(xs), 64, dtype=torch.float16)
+        for j, x in enumerate(xs):
+            keys[64 * j : 64 * (j + 1), 0] = x
+        _, _, sal = tsa.build_schedule(keys.to("cuda:0"), 64, 0, 0, 0, return_salience=True)
+        assert sal.cpu().tolist() == [float(x) for x in expect.split()]
+
+
+@pytest.mark.parametrize("nb", [0, 1, 16, 64, 128, 517])
+def test_dense_schedule(tsa, nb):
+    rp, ci = tsa.dense_causal_schedule(nb, "cuda:0")
+    drp, dci = oracle.dense_causal_schedule(nb)
+    assert np.array_equal(rp.cpu().numpy(), drp) and np.array_equal(ci.cpu().numpy(), dci)
+
+
+def test_builder_validation(tsa):
+    keys = torch.zeros(128, 64, dtype=torch.float16, device="cuda:0")
+    with pytest.raises(ValueError, match="UNSUPPORTED"):
+        tsa.build_schedule(keys, 32, 1, 1, 2)
+    with pytest.raises(ValueError, match="INVALID_ARG"):
+        tsa.build_schedule(keys, 64, -1, 1, 2)
+    with pytest.raises(TypeError):
+        tsa.build_schedule(keys.float(), 64, 1, 1, 2)
+    big = torch.zeros(64 * 4097, 8, dtype=torch.float16, device="cuda:0")
+    with pytest.raises(ValueError, match="UNSUPPORTED"):
+        tsa.build_schedule(big, 64, 1, 1, 2)
+
+
+def test_builder_then_attention_end_to_end(tsa):
+    w = workloads.WORKLOADS["single_s1024_d64_f16"]
+    q, k, v = workloads.make_qkv(w)
+    rp, ci = tsa.build_schedule(k.to("cuda:0"), 64, w.sink, w.local_radius, w.topk)
+    out = tsa.scheduled_attention(q.to("cuda:0"), k.to("cuda:0"), v.to("cuda:0"), rp, ci)
+    rp_o, ci_o, _ = oracle.build_schedule(k, 64, w.sink, w.local_radius, w.topk)
+    want = oracle.masked_attention(q, k, v, rp_o, ci_o, 64)
+    assert float(np.max(np.abs(out.cpu().double().numpy() - want))) <= 2e-3
