@@ -103,6 +103,8 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy 10 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -113,6 +115,16 @@ def main() -> int:
 
     import block_sparse_causal_amd as tsa
     import workloads
+
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_launch": 256 << 20,
+                          "copy_calibration_bytes_written_per_launch": 256 << 20}))
+        return 0
 
     name = args.workload or workloads.BENCH_WORKLOAD
     w = workloads.WORKLOADS[name]

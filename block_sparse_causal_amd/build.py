@@ -34,6 +34,9 @@ COMMON = [
     "-target-feature",
     "-Xclang",
     "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no AGPR copies around VALU work)
+    "-mllvm",
+    "-amdgpu-mfma-vgpr-form=1",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

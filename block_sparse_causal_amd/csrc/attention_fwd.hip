@@ -100,6 +100,24 @@ __device__ __forceinline__ int swap_bits23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// Byte offset, inside one tile, of the 16-byte chunk `c` (8 elements) of row `r`.
+// K rows use chunk ^ (r & 7); V rows use chunk ^ 2*t(r & 3), where t spreads the
+// four key rows that one transposing read touches over distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_chunk_offset(int r, int c) {
+  return r * (D * 2) + 16 * (c ^ (r & 7));
+}
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  if (D == 64) return 2 * (r & 3);
+  const int t = (0x6530 >> (4 * (r & 3))) & 0xF;  // 0, 3, 5, 6
+  return 2 * t;
+}
+template <int D>
+__device__ __forceinline__ int v_chunk_offset(int r, int c) {
+  return r * (D * 2) + 16 * (c ^ v_swizzle<D>(r));
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -107,23 +125,29 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t nnz,
     int S, int nb, int64_t lane_base, float scale_log2) {
   using E = Elem<BF16>;
-  constexpr int kStepsD = D / 16;           // 16-deep steps of Q.K^T
-  constexpr int kTilesD = D / 32;           // 32-row tiles of O^T
-  constexpr int kRowBytes = D * 2;          // bytes per K row in LDS
-  constexpr int kChunksPerRow = D / 8;      // 16-byte chunks per K row
-  constexpr int kLoads = kBlock * D / 8 / kThreads;  // 16-byte loads per thread per tile
-  constexpr int kVPairs = kLoads / 4;       // (4 keys x 8 dims) V pieces per thread
+  constexpr int kStepsD = D / 16;                  // 16-deep steps of Q.K^T
+  constexpr int kTilesD = D / 32;                  // 32-row tiles of O^T
+  constexpr int kRowBytes = D * 2;
+  constexpr int kTileBytes = kBlock * kRowBytes;   // one K or V tile
+  constexpr int kChunksPerRow = D / 8;
+  constexpr int kFillOps = 2 * kTileBytes / (16 * 64) / 2;  // 16-byte-per-lane fills per wave per stage
+  // Lazy rescale: the running max used for the exponent moves only when a row's
+  // max exceeds it by more than this many powers of two (P then stays <= 2^8).
+  constexpr float kRescaleSlack = 8.0f;
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[kBlock * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_vt[D * kBlock * 2];
+  // Two stages, each [K tile | V tile]; distinct objects so that the compiler
+  // can tell loads into one stage from reads of the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[2 * kTileBytes];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;   // wave
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave (uniform)
   const int l = tid & 63;   // lane in wave
   const int h = l >> 5;     // half-wave
   const int n = l & 31;     // query column within the wave's 32 rows
+  const int g = l >> 4;     // 16-lane group
+  const int gi = l & 15;
 
-  // Workgroup -> (lane, query block).  Hardware places workgroup b on XCD b % 8.
   const uint32_t G = gridDim.x;
   const uint32_t bid = blockIdx.x;
   const uint32_t logical = (G % 8u == 0u) ? (bid % 8u) * (G / 8u) + bid / 8u : bid;
@@ -131,80 +155,80 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   const int i = nb - 1 - (int)(logical % (uint32_t)nb);
 
   const int64_t lane_off = lane * (int64_t)S * D;
-  const uint16_t* qg = q + lane_off;
   const uint16_t* kg = k + lane_off;
   const uint16_t* vg = v + lane_off;
-  uint16_t* og = out + lane_off;
 
   // Q^T operands: lane holds query row qrow, dims 16c + 8h .. +7 for step c.
   const int qrow = i * kBlock + 32 * w + n;
+  const int qrow_c = qrow < S ? qrow : S - 1;
   u32x4 qop[kStepsD];
 #pragma unroll
-  for (int c = 0; c < kStepsD; ++c) {
-    qop[c] = (qrow < S) ? *(const u32x4*)(qg + (int64_t)qrow * D + 16 * c + 8 * h) : u32x4{0, 0, 0, 0};
-  }
+  for (int c = 0; c < kStepsD; ++c)
+    qop[c] = *(const u32x4*)(q + lane_off + (int64_t)qrow_c * D + 16 * c + 8 * h);
 
-  // CSR row bounds, clamped to the readable entries.
+  // CSR row bounds, clamped to the readable entries.  The row's column indices
+  // are read 64 at a time into one register per lane and handed out with
+  // readlane, so walking the row costs no memory latency per block.
   int64_t p = row_ptr[i];
   int64_t end = row_ptr[i + 1];
   p = p < 0 ? 0 : (p > nnz ? nnz : p);
   end = end < p ? p : (end > nnz ? nnz : end);
-  // Next accepted key block after `last` (strictly ascending, within 0..i), or -1.
+  int64_t win = p;  // first entry held in `cols`
+  int cols = (p + l < end) ? col_idx[p + l] : -1;
   auto next_block = [&](int last) -> int {
     while (p < end) {
-      const int c = col_idx[p++];
+      if (p - win >= 64) {
+        win = p;
+        cols = (p + l < end) ? col_idx[p + l] : -1;
+      }
+      const int c = __builtin_amdgcn_readlane(cols, (int)(p - win));
+      ++p;
       if (c > last && c <= i) return c;
     }
     return -1;
   };
 
-  u32x4 kreg[kLoads];
-  u32x4 vreg[kLoads];
-  auto load_tile = [&](int j) {
+  // Queue the copy of K and V block j into one stage: every lane moves 16 bytes
+  // per op straight from global memory into LDS (no registers in between).
+  // Rows past S are clamped to row S-1 (finite values that the causal mask or
+  // a zero probability removes).
+  // Per-lane byte offset, inside a block's rows, of the 16 bytes each fill op
+  // moves; the ops of a wave alternate between the K and the V tile.
+  uint32_t fill_off[kFillOps];
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it) {
-      const int id = it * kThreads + tid;
-      const int row = id / kChunksPerRow, cb = id % kChunksPerRow;
-      const int grow = j * kBlock + row;
-      kreg[it] = (grow < S) ? *(const u32x4*)(kg + (int64_t)grow * D + 8 * cb) : u32x4{0, 0, 0, 0};
-    }
+  for (int op = 0; op < kFillOps; ++op) {
+    const int chunk = (op * 2 + w) * 64 + l;  // 16-byte chunk index within [K | V]
+    const bool is_v = chunk >= kBlock * kChunksPerRow;
+    const int cc = is_v ? chunk - kBlock * kChunksPerRow : chunk;
+    const int r = cc / kChunksPerRow, pc = cc % kChunksPerRow;
+    const int key = is_v ? r : ((r & 32) | swap_bits23(r & 31));
+    const int c = is_v ? (pc ^ v_swizzle<D>(r)) : (pc ^ (r & 7));
+    fill_off[op] = (uint32_t)(key * kRowBytes + 16 * c);
+  }
+  // Queue the copy of K and V block j into one stage: every lane moves 16 bytes
+  // per op straight from global memory into LDS (no registers in between).
+  auto fill = [&](int j, uint8_t* stage) {
+    const char* kb = (const char*)(kg + (int64_t)j * kBlock * D);
+    const char* vb = (const char*)(vg + (int64_t)j * kBlock * D);
+    const int lim = S - j * kBlock;  // rows of this block that exist
+    if (lim >= kBlock) {
 #pragma unroll
-    for (int pi = 0; pi < kVPairs; ++pi) {
-      const int id = pi * kThreads + tid;
-      const int a = id & 15, b = id >> 4;  // keys 4a .. 4a+3, dims 8b .. 8b+7
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int grow = j * kBlock + 4 * a + r;
-        vreg[pi * 4 + r] = (grow < S) ? *(const u32x4*)(vg + (int64_t)grow * D + 8 * b) : u32x4{0, 0, 0, 0};
+      for (int op = 0; op < kFillOps; ++op) {
+        const bool is_v = (op * 2 + w) * 64 >= kBlock * kChunksPerRow;  // uniform per op
+        __builtin_amdgcn_global_load_lds((const void*)((is_v ? vb : kb) + fill_off[op]),
+                                         (__attribute__((address_space(3))) void*)(stage + (op * 2 + w) * 1024),
+                                         16, 0, 0);
       }
-    }
-  };
-  auto store_tile = [&]() {
+    } else {  // partial last block: rows past S are clamped to row S-1
 #pragma unroll
-    for (int it = 0; it < kLoads; ++it) {
-      const int id = it * kThreads + tid;
-      const int row = id / kChunksPerRow, cb = id % kChunksPerRow;
-      const int rho = (row & 32) | swap_bits23(row & 31);
-      *(u32x4*)(lds_k + rho * kRowBytes + 16 * (cb ^ (rho & 7))) = kreg[it];
-    }
-#pragma unroll
-    for (int pi = 0; pi < kVPairs; ++pi) {
-      const int id = pi * kThreads + tid;
-      const int a = id & 15, b = id >> 4;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * b + e;
-        const uint32_t r0 = vreg[pi * 4 + 0][e >> 1], r1 = vreg[pi * 4 + 1][e >> 1];
-        const uint32_t r2 = vreg[pi * 4 + 2][e >> 1], r3 = vreg[pi * 4 + 3][e >> 1];
-        u32x2 val;
-        if (e & 1) {
-          val[0] = (r0 >> 16) | (r1 & 0xffff0000u);
-          val[1] = (r2 >> 16) | (r3 & 0xffff0000u);
-        } else {
-          val[0] = (r0 & 0xffffu) | (r1 << 16);
-          val[1] = (r2 & 0xffffu) | (r3 << 16);
-        }
-        *(u32x2*)(lds_vt + d * (kBlock * 2) + 16 * ((a >> 1) ^ (d & 7)) + 8 * (a & 1)) = val;
+      for (int op = 0; op < kFillOps; ++op) {
+        const bool is_v = (op * 2 + w) * 64 >= kBlock * kChunksPerRow;
+        uint32_t off = fill_off[op];
+        const int key = (int)(off / kRowBytes);
+        if (key >= lim) off -= (uint32_t)((key - (lim - 1)) * kRowBytes);
+        __builtin_amdgcn_global_load_lds((const void*)((is_v ? vb : kb) + off),
+                                         (__attribute__((address_space(3))) void*)(stage + (op * 2 + w) * 1024),
+                                         16, 0, 0);
       }
     }
   };
@@ -212,31 +236,25 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   f32x16 o[kTilesD];
 #pragma unroll
   for (int dt = 0; dt < kTilesD; ++dt) o[dt] = f32x16{};
-  float m_run = -__builtin_inff();  // running max, in log2 units
+  float m_use = -__builtin_inff();  // exponent offset in use (log2 units)
   float l_run = 0.0f;               // this half-wave's share of the denominator
 
-  int j = next_block(-1);
-  if (j >= 0) load_tile(j);
-  while (j >= 0) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();  // tile j is in LDS
-    const int j_next = next_block(j);
-    if (j_next >= 0) load_tile(j_next);  // in flight during the math below
-
-    // S^T = K . Q^T for key halves t = 0, 1.
-    f32x16 s[2];
+  auto compute = [&](int j, const uint8_t* stage, bool first) {
+    const uint8_t* ks = stage;
+    const uint8_t* vs = stage + kTileBytes;
+    // S^T = K . Q^T for key halves t = 0, 1: all K operands are read first, then
+    // the two independent accumulation chains are interleaved.
+    u32x4 ka[2][kStepsD];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = f32x16{};
-      const uint8_t* krow = lds_k + (32 * t + n) * kRowBytes;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int c = 0; c < kStepsD; ++c) {
-        const u32x4 a = *(const u32x4*)(krow + 16 * ((2 * c + h) ^ (n & 7)));
-        s[t] = E::mfma(a, qop[c], s[t]);
-      }
-    }
-
+      for (int c = 0; c < kStepsD; ++c)
+        ka[t][c] = *(const u32x4*)(ks + k_chunk_offset<D>(32 * t + n, 2 * c + h));
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) s[t] = E::mfma(ka[t][c], qop[c], s[t]);
     if (j == i) {  // diagonal block: key position must not exceed query position
       const int qpos = 32 * w + n;
 #pragma unroll
@@ -247,66 +265,100 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
           if (kpos > qpos) s[t][r] = -__builtin_inff();
         }
     }
-
     float mx = s[0][0];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    mx = max_with_other_half(mx);
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
-    // P = exp2(s * scale_log2 - m), rounded to the input type; B operands of P.V.
+    mx = max_with_other_half(mx) * scale_log2;
+    const bool grow = mx > m_use + kRescaleSlack;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m_use;
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+      m_use = m_new;
+      if (!first) {  // before the first block O and l are still zero
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
+      }
+    }
     u32x4 pb[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * g + 2 * x], scale_log2, -m_new));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * g + 2 * x + 1], scale_log2, -m_new));
-          pb[2 * t + g][x] = E::pack(p0, p1);
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * gg + 2 * x], scale_log2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * gg + 2 * x + 1], scale_log2, -m_use));
+          pb[2 * t + gg][x] = E::pack(p0, p1);
         }
-    l_run *= alpha;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int x = 0; x < 4; ++x) l_run = E::add_pair(pb[c][x], l_run);
-
-    if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
-    }
-
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T; V^T operands come from row-major V through transposing reads:
+    // lane (group g, index gi) gets keys kb .. kb+3 of head dim 32dt + 16(g&1) + gi.
 #pragma unroll
     for (int dt = 0; dt < kTilesD; ++dt) {
-      const uint8_t* vrow = lds_vt + (32 * dt + n) * (kBlock * 2);
+      const int dchunk = 4 * dt + 2 * (g & 1) + ((gi & 3) >> 1);
+      const int dbyte = 8 * (gi & 1);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const u32x4 a = *(const u32x4*)(vrow + 16 * ((2 * c + h) ^ (n & 7)));
+        u32x4 a;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = 16 * c + 8 * (g >> 1) + 4 * t + (gi >> 2);
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vs + v_chunk_offset<D>(r, dchunk) + dbyte));
+          const u32x2 xx = __builtin_bit_cast(u32x2, x);
+          a[2 * t] = xx[0];
+          a[2 * t + 1] = xx[1];
+        }
         o[dt] = E::mfma(a, pb[c], o[dt]);
       }
     }
-    j = j_next;
+  };
+
+  int j = next_block(-1);
+  if (j >= 0) {
+    fill(j, stage0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    bool first = true;
+    while (true) {
+      int jn = next_block(j);
+      if (jn >= 0) fill(jn, stage1);
+      compute(j, stage0, first);
+      first = false;
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (jn < 0) break;
+      j = jn;
+      jn = next_block(j);
+      if (jn >= 0) fill(jn, stage0);
+      compute(j, stage1, false);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (jn < 0) break;
+      j = jn;
+    }
   }
 
   // Epilogue: O / l, rounded to the input type.  Rows with no visible key get 0.
   const float l_tot = sum_with_other_half(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (qrow < S) {
-    uint16_t* orow = og + (int64_t)qrow * D;
+    uint16_t* orow = out + lane_off + (int64_t)qrow * D;
 #pragma unroll
     for (int dt = 0; dt < kTilesD; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int gg = 0; gg < 4; ++gg) {
         u32x2 val;
-        val[0] = E::pack(o[dt][4 * g + 0] * inv, o[dt][4 * g + 1] * inv);
-        val[1] = E::pack(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-        *(u32x2*)(orow + 32 * dt + 8 * g + 4 * h) = val;
+        val[0] = E::pack(o[dt][4 * gg + 0] * inv, o[dt][4 * gg + 1] * inv);
+        val[1] = E::pack(o[dt][4 * gg + 2] * inv, o[dt][4 * gg + 3] * inv);
+        *(u32x2*)(orow + 32 * dt + 8 * gg + 4 * h) = val;
       }
   }
 }
