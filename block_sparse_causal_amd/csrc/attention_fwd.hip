@@ -5,30 +5,34 @@
 // row lists; one schedule is shared by every batch/head lane; the output keeps
 // the input dtype.  The block loop keeps a running row max and denominator and
 // rescales by exp(m_prev - m_new) (mirror page, Rust-port commit note), so one
-// 64x64 score tile is live at a time.
+// score tile is live at a time.
 //
 // Work decomposition
-//   One workgroup = one (lane, query block) pair, 128 threads = 2 waves; wave w
-//   owns query rows 32w .. 32w+31 of the block.  Workgroup ids are remapped so
-//   that each of the 8 XCDs receives a contiguous range of lanes (its L2 then
-//   holds those lanes' K/V), and within a lane query blocks run longest-row
-//   first (descending block index).
+//   One workgroup = one (lane, query block) pair, 256 threads = 4 waves.  Wave w
+//   owns query half qh = w & 1 (rows 32qh .. 32qh+31) and key half kh = w >> 1
+//   (keys 32kh .. 32kh+31 of every visited block); each wave keeps its own
+//   running max, denominator and O, and the two key halves of a query half are
+//   merged once at the end.  Workgroup ids are remapped so that each of the 8
+//   XCDs receives a contiguous range of lanes (its L2 then holds those lanes'
+//   K/V); within a lane, query blocks run longest-row first.
 //
 // Contractions (v_mfma_f32_32x32x16_{f16,bf16}, fp32 accumulation)
-//   S^T = K . Q^T : A = K tile rows (keys) from LDS, B = Q^T held in registers.
-//     The result puts one query per lane column, so row statistics need only
-//     in-lane reductions plus one exchange between the two half-waves.
-//   O^T += V^T . P^T : A = V^T rows (head dims) from LDS, B = P^T straight from
-//     the S^T result registers.  For this to line up, key 32t + pi(m) is placed
-//     in MFMA row m of score tile t, where pi swaps bits 2 and 3 of m; then the
-//     registers 8g .. 8g+7 of tile t of half-wave h hold keys
-//     16(2t+g) + 8h + 0..7 in order, exactly the B operand of P.V step 2t+g.
+//   S^T = K . Q^T : A = K rows (keys) from LDS, B = Q^T held in registers.  The
+//     result puts one query per lane column, so row statistics need only in-lane
+//     reductions plus one exchange between the two half-waves.
+//   O^T += V^T . P^T : A = V^T (head dims x keys) read from row-major V in LDS
+//     with transposing reads (ds_read_b64_tr_b16); B = P^T straight from the S^T
+//     result registers.  For this to line up, key 32kh + pi(m) is placed in MFMA
+//     row m of the score tile, where pi swaps bits 2 and 3 of m; registers
+//     8g .. 8g+7 of half-wave h then hold keys 16g + 8h + 0..7 of the half in
+//     order, exactly the B operand of P.V step g.
 //
-// LDS (per workgroup, one stage): K tile [64][D] in MFMA row order, V^T tile
-// [D][64].  Each 16-byte chunk index within a row is XORed with (row & 7) so
-// both the staging writes and the MFMA operand reads are free of bank
-// conflicts.  The next tile's global loads are issued into registers before the
-// current tile's math and written to LDS after it.
+// Data movement: K and V tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, no registers in between) through a ring of stages;
+// the copy of the next block is in flight while the current one is computed.
+// 16-byte chunks inside a row are XOR-swizzled by row so that the operand reads
+// spread over the LDS banks.  Probabilities use a lazy rescale: the exponent
+// offset moves only when a row max exceeds it by more than 2^8.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,7 +50,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 64;
-constexpr int kThreads = 128;
+constexpr int kThreads = 256;  // 4 waves: 2 query halves x 2 key halves
 
 // Element-type specific pieces: the MFMA, the fp32 -> 2 x 16-bit pack (round to
 // nearest even) and a pairwise add of a packed pair into an fp32 sum.
@@ -118,6 +122,57 @@ __device__ __forceinline__ int v_chunk_offset(int r, int c) {
   return r * (D * 2) + 16 * (c ^ v_swizzle<D>(r));
 }
 
+// Stages of the K/V ring: three at head dim 64 (48 KB of LDS per workgroup),
+// two at 128 (64 KB), which keeps two or three workgroups resident per CU.
+template <int D>
+struct Stages {
+  static constexpr int value = 2;
+};
+
+// s_waitcnt immediate that waits until at most `n` vector memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
+// Wait until at most `later` stages' copies (kFillOps operations each) remain.
+template <int kStages, int kFillOps>
+__device__ __forceinline__ void wait_copies(int later) {
+  if (kStages >= 3 && later >= 1) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kFillOps));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  }
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16), issued through asm so that the
+// compiler does not order it behind the in-flight global->LDS copies of other
+// stages; the values may only be used after lds_wait_all().  Within each
+// 16-lane group, lane i receives element i % 4 of the 8-byte pieces addressed by
+// lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4.
+template <int kOffset>
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOffset));
+  return r;
+}
+// Wait for every outstanding LDS read of this wave; the values pass through the
+// asm statement so that no use of them can be scheduled above the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait_all(u32x2 (&x)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int e = 0; e < N; ++e) asm volatile("" : "+v"(x[e]));
+}
+
+// Workgroup barrier for the K/V ring.  Each wave has already waited (s_waitcnt)
+// for exactly the copies the next step reads, so the barrier must not drain the
+// copies still in flight, which a fenced __syncthreads() would.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -130,21 +185,26 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   constexpr int kRowBytes = D * 2;
   constexpr int kTileBytes = kBlock * kRowBytes;   // one K or V tile
   constexpr int kChunksPerRow = D / 8;
-  constexpr int kFillOps = 2 * kTileBytes / (16 * 64) / 2;  // 16-byte-per-lane fills per wave per stage
-  // Lazy rescale: the running max used for the exponent moves only when a row's
-  // max exceeds it by more than this many powers of two (P then stays <= 2^8).
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kFillOps = 2 * kTileBytes / 1024 / kWaves;  // 1 KB fill ops per wave per stage
+  // Lazy rescale: the exponent offset moves only when a row's max exceeds it by
+  // more than this many powers of two (P then stays <= 2^8).
   constexpr float kRescaleSlack = 8.0f;
 
-  // Two stages, each [K tile | V tile]; distinct objects so that the compiler
-  // can tell loads into one stage from reads of the other.
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[2 * kTileBytes];
+  // A ring of kStages stages, each [K tile | V tile].  The copy of block n+kStages-1
+  // is in flight while block n is computed.  Stage indices are compile-time
+  // constants everywhere (the loop is unrolled by kStages), so the compiler can
+  // tell copies into one stage from reads of another.
+  constexpr int kStages = Stages<D>::value;
+  __shared__ __attribute__((aligned(1024))) uint8_t stages[kStages][2 * kTileBytes];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave (uniform)
-  const int l = tid & 63;   // lane in wave
+  const int qh = w & 1;     // query half: rows 32qh .. 32qh+31 of the block
+  const int kh = w >> 1;    // key half: keys 32kh .. 32kh+31 of every visited block
+  const int l = tid & 63;
   const int h = l >> 5;     // half-wave
-  const int n = l & 31;     // query column within the wave's 32 rows
+  const int n = l & 31;     // query column
   const int g = l >> 4;     // 16-lane group
   const int gi = l & 15;
 
@@ -159,45 +219,42 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   const uint16_t* vg = v + lane_off;
 
   // Q^T operands: lane holds query row qrow, dims 16c + 8h .. +7 for step c.
-  const int qrow = i * kBlock + 32 * w + n;
+  const int qrow = i * kBlock + 32 * qh + n;
   const int qrow_c = qrow < S ? qrow : S - 1;
   u32x4 qop[kStepsD];
 #pragma unroll
   for (int c = 0; c < kStepsD; ++c)
     qop[c] = *(const u32x4*)(q + lane_off + (int64_t)qrow_c * D + 16 * c + 8 * h);
 
-  // CSR row bounds, clamped to the readable entries.  The row's column indices
-  // are read 64 at a time into one register per lane and handed out with
-  // readlane, so walking the row costs no memory latency per block.
-  int64_t p = row_ptr[i];
-  int64_t end = row_ptr[i + 1];
-  p = p < 0 ? 0 : (p > nnz ? nnz : p);
-  end = end < p ? p : (end > nnz ? nnz : end);
-  int64_t win = p;  // first entry held in `cols`
+  // CSR row bounds, clamped to the readable entries (the C ABI caps entries at
+  // int32 range).  The row's column indices are read 64 at a time into one
+  // register per lane and handed out with readlane; a reload drains the memory
+  // counter right away, so no other read of the window ever waits on memory.
+  int p = (int)min((int64_t)max(row_ptr[i], 0), nnz);
+  const int end = (int)max(min((int64_t)row_ptr[i + 1], nnz), (int64_t)p);
+  int win = p;
   int cols = (p + l < end) ? col_idx[p + l] : -1;
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
   auto next_block = [&](int last) -> int {
     while (p < end) {
       if (p - win >= 64) {
         win = p;
         cols = (p + l < end) ? col_idx[p + l] : -1;
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
       }
-      const int c = __builtin_amdgcn_readlane(cols, (int)(p - win));
+      const int c = __builtin_amdgcn_readlane(cols, p - win);
       ++p;
       if (c > last && c <= i) return c;
     }
     return -1;
   };
 
-  // Queue the copy of K and V block j into one stage: every lane moves 16 bytes
-  // per op straight from global memory into LDS (no registers in between).
-  // Rows past S are clamped to row S-1 (finite values that the causal mask or
-  // a zero probability removes).
   // Per-lane byte offset, inside a block's rows, of the 16 bytes each fill op
-  // moves; the ops of a wave alternate between the K and the V tile.
+  // moves.  Op o of wave w fills the 1 KB piece (o * kWaves + w) of [K | V].
   uint32_t fill_off[kFillOps];
 #pragma unroll
   for (int op = 0; op < kFillOps; ++op) {
-    const int chunk = (op * 2 + w) * 64 + l;  // 16-byte chunk index within [K | V]
+    const int chunk = (op * kWaves + w) * 64 + l;
     const bool is_v = chunk >= kBlock * kChunksPerRow;
     const int cc = is_v ? chunk - kBlock * kChunksPerRow : chunk;
     const int r = cc / kChunksPerRow, pc = cc % kChunksPerRow;
@@ -214,20 +271,20 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     if (lim >= kBlock) {
 #pragma unroll
       for (int op = 0; op < kFillOps; ++op) {
-        const bool is_v = (op * 2 + w) * 64 >= kBlock * kChunksPerRow;  // uniform per op
+        const bool is_v = (op * kWaves + w) * 64 >= kBlock * kChunksPerRow;  // uniform
         __builtin_amdgcn_global_load_lds((const void*)((is_v ? vb : kb) + fill_off[op]),
-                                         (__attribute__((address_space(3))) void*)(stage + (op * 2 + w) * 1024),
+                                         (__attribute__((address_space(3))) void*)(stage + (op * kWaves + w) * 1024),
                                          16, 0, 0);
       }
     } else {  // partial last block: rows past S are clamped to row S-1
 #pragma unroll
       for (int op = 0; op < kFillOps; ++op) {
-        const bool is_v = (op * 2 + w) * 64 >= kBlock * kChunksPerRow;
+        const bool is_v = (op * kWaves + w) * 64 >= kBlock * kChunksPerRow;
         uint32_t off = fill_off[op];
         const int key = (int)(off / kRowBytes);
         if (key >= lim) off -= (uint32_t)((key - (lim - 1)) * kRowBytes);
         __builtin_amdgcn_global_load_lds((const void*)((is_v ? vb : kb) + off),
-                                         (__attribute__((address_space(3))) void*)(stage + (op * 2 + w) * 1024),
+                                         (__attribute__((address_space(3))) void*)(stage + (op * kWaves + w) * 1024),
                                          16, 0, 0);
       }
     }
@@ -237,129 +294,165 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
 #pragma unroll
   for (int dt = 0; dt < kTilesD; ++dt) o[dt] = f32x16{};
   float m_use = -__builtin_inff();  // exponent offset in use (log2 units)
-  float l_run = 0.0f;               // this half-wave's share of the denominator
+  float l_run = 0.0f;               // this lane's share of the denominator
 
-  auto compute = [&](int j, const uint8_t* stage, bool first) {
+  auto compute = [&](int j, const uint8_t* stage) {
+    // On the diagonal block the key half above the query half is fully masked.
+    if (j == i && kh > qh) return;
     const uint8_t* ks = stage;
     const uint8_t* vs = stage + kTileBytes;
-    // S^T = K . Q^T for key halves t = 0, 1: all K operands are read first, then
-    // the two independent accumulation chains are interleaved.
-    u32x4 ka[2][kStepsD];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int c = 0; c < kStepsD; ++c)
-        ka[t][c] = *(const u32x4*)(ks + k_chunk_offset<D>(32 * t + n, 2 * c + h));
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    // S^T (32 keys of this half x 32 queries) = K . Q^T.
+    u32x4 ka[kStepsD];
 #pragma unroll
     for (int c = 0; c < kStepsD; ++c)
+      ka[c] = *(const u32x4*)(ks + k_chunk_offset<D>(32 * kh + n, 2 * c + h));
+    f32x16 s = f32x16{};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) s[t] = E::mfma(ka[t][c], qop[c], s[t]);
-    if (j == i) {  // diagonal block: key position must not exceed query position
-      const int qpos = 32 * w + n;
+    for (int c = 0; c < kStepsD; ++c) s = E::mfma(ka[c], qop[c], s);
+    if (j == i && kh == qh) {  // diagonal sub-tile: key position must not exceed query position
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kpos = 32 * t + 16 * (r >> 3) + 8 * h + (r & 7);
-          if (kpos > qpos) s[t][r] = -__builtin_inff();
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int kpos = 16 * (r >> 3) + 8 * h + (r & 7);
+        if (kpos > n) s[r] = -__builtin_inff();
+      }
     }
-    float mx = s[0][0];
+    float mx = s[0];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = max_with_other_half(mx) * scale_log2;
     const bool grow = mx > m_use + kRescaleSlack;
     if (__ballot(grow)) {
       const float m_new = grow ? mx : m_use;
       const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
       m_use = m_new;
-      if (!first) {  // before the first block O and l are still zero
-        l_run *= alpha;
+      l_run *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
+    }
+    // V^T operands for O^T += V^T . P^T over this half's two 16-key chunks come
+    // from row-major V through transposing reads: lane (group g, index gi) gets
+    // keys kb .. kb+3 of head dim 32dt + 16(g&1) + gi.  They are issued now and
+    // land while the softmax runs.
+    u32x2 va[kTilesD * 4];
+    {
+      const uint32_t vbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)vs;
+      // byte offset of (key row r, head dim d0) for this lane, with the row swizzle
+      const int r0 = 32 * kh + 8 * (g >> 1) + (gi >> 2);  // key row for chunk 2kh, first read
+      const uint32_t lane_addr = vbase + (uint32_t)(r0 * kRowBytes + 8 * (gi & 1));
+      const int sw = v_swizzle<D>(r0);  // rows r0 + 4t + 16gg share r0's swizzle (same r & 3)
+#pragma unroll
+      for (int dt = 0; dt < kTilesD; ++dt) {
+        const int dchunk = 4 * dt + 2 * (g & 1) + ((gi & 3) >> 1);
+        const uint32_t a = lane_addr + 16u * (uint32_t)(dchunk ^ sw);
+        va[dt * 4 + 0] = lds_read_tr16<0>(a);
+        va[dt * 4 + 1] = lds_read_tr16<4 * kRowBytes>(a);
+        va[dt * 4 + 2] = lds_read_tr16<16 * kRowBytes>(a);
+        va[dt * 4 + 3] = lds_read_tr16<20 * kRowBytes>(a);
       }
     }
-    u32x4 pb[4];
+    u32x4 pb[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * gg + 2 * x], scale_log2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * gg + 2 * x + 1], scale_log2, -m_use));
-          pb[2 * t + gg][x] = E::pack(p0, p1);
-        }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) l_run = E::add_pair(pb[c][x], l_run);
-    // O^T += V^T . P^T; V^T operands come from row-major V through transposing reads:
-    // lane (group g, index gi) gets keys kb .. kb+3 of head dim 32dt + 16(g&1) + gi.
-#pragma unroll
-    for (int dt = 0; dt < kTilesD; ++dt) {
-      const int dchunk = 4 * dt + 2 * (g & 1) + ((gi & 3) >> 1);
-      const int dbyte = 8 * (gi & 1);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 a;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r = 16 * c + 8 * (g >> 1) + 4 * t + (gi >> 2);
-          typedef short s16x4 __attribute__((ext_vector_type(4)));
-          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vs + v_chunk_offset<D>(r, dchunk) + dbyte));
-          const u32x2 xx = __builtin_bit_cast(u32x2, x);
-          a[2 * t] = xx[0];
-          a[2 * t + 1] = xx[1];
-        }
-        o[dt] = E::mfma(a, pb[c], o[dt]);
+      for (int x = 0; x < 4; ++x) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * gg + 2 * x], scale_log2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * gg + 2 * x + 1], scale_log2, -m_use));
+        pb[gg][x] = E::pack(p0, p1);
       }
-    }
-  };
-
-  int j = next_block(-1);
-  if (j >= 0) {
-    fill(j, stage0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    bool first = true;
-    while (true) {
-      int jn = next_block(j);
-      if (jn >= 0) fill(jn, stage1);
-      compute(j, stage0, first);
-      first = false;
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-      if (jn < 0) break;
-      j = jn;
-      jn = next_block(j);
-      if (jn >= 0) fill(jn, stage0);
-      compute(j, stage1, false);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-      if (jn < 0) break;
-      j = jn;
-    }
-  }
-
-  // Epilogue: O / l, rounded to the input type.  Rows with no visible key get 0.
-  const float l_tot = sum_with_other_half(l_run);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  if (qrow < S) {
-    uint16_t* orow = out + lane_off + (int64_t)qrow * D;
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) l_run = E::add_pair(pb[gg][x], l_run);
+    lds_wait_all(va);
 #pragma unroll
     for (int dt = 0; dt < kTilesD; ++dt)
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        u32x2 val;
-        val[0] = E::pack(o[dt][4 * gg + 0] * inv, o[dt][4 * gg + 1] * inv);
-        val[1] = E::pack(o[dt][4 * gg + 2] * inv, o[dt][4 * gg + 3] * inv);
-        *(u32x2*)(orow + 32 * dt + 8 * gg + 4 * h) = val;
+      for (int gg = 0; gg < 2; ++gg) {
+        const u32x2 lo = va[dt * 4 + 2 * gg], hi = va[dt * 4 + 2 * gg + 1];
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        o[dt] = E::mfma(a, pb[gg], o[dt]);
       }
+  };
+
+  // Ring schedule.  blk[t] is the block held by stage t (-1: none).  At stage t:
+  // wait until stage t's copy has landed (later copies may stay in flight),
+  // barrier, queue the next block into the stage computed one step ago, compute.
+  int blk[kStages];
+  blk[0] = next_block(-1);
+#pragma unroll
+  for (int t = 1; t < kStages; ++t) blk[t] = -1;
+  if (blk[0] >= 0) {
+    fill(blk[0], stages[0]);
+#pragma unroll
+    for (int t = 1; t < kStages - 1; ++t) {
+      blk[t] = blk[t - 1] >= 0 ? next_block(blk[t - 1]) : -1;
+      if (blk[t] >= 0) fill(blk[t], stages[t]);
+    }
+    int last = blk[kStages - 2];  // most recently queued block (-1: row exhausted)
+    bool done = false;
+    while (!done) {
+#pragma unroll
+      for (int t = 0; t < kStages; ++t) {
+        if (!done) {
+          // copies queued after stage t's: blocks in stages t+1 .. t+kStages-2
+          int later = 0;
+#pragma unroll
+          for (int u = 1; u < kStages - 1; ++u) later += blk[(t + u) % kStages] >= 0 ? 1 : 0;
+          wait_copies<kStages, kFillOps>(later);
+          ring_barrier();
+          const int refill = (t + kStages - 1) % kStages;
+          const int jn = last >= 0 ? next_block(last) : -1;
+          blk[refill] = jn;
+          last = jn;
+          if (jn >= 0) fill(jn, stages[refill]);
+          compute(blk[t], stages[t]);
+          done = blk[(t + 1) % kStages] < 0;
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with the stages before they hold the merge
+  }
+
+  // Merge the two key halves of each query half, then O / l rounded to the
+  // input type.  Rows with no visible key get 0.  The stage buffers are free
+  // here (every wave has passed the last barrier).
+  const float l_half = sum_with_other_half(l_run);
+  static_assert((kTilesD * 16 + 2) * 64 * 4 <= 2 * kTileBytes && kStages >= 2, "merge area exceeds a stage");
+  float* mrg = (float*)stages[qh % kStages];
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mrg[(dt * 16 + r) * 64 + l] = o[dt][r];
+    mrg[kTilesD * 16 * 64 + l] = m_use;
+    mrg[(kTilesD * 16 + 1) * 64 + l] = l_half;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m_b = mrg[kTilesD * 16 * 64 + l];
+    const float l_b = mrg[(kTilesD * 16 + 1) * 64 + l];
+    const float m = fmaxf(m_use, m_b);
+    const float fa = (m_use == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_use - m);
+    const float fb = (m_b == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_b - m);
+    const float l_tot = l_half * fa + l_b * fb;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const float ca = fa * inv, cb = fb * inv;
+    if (qrow < S) {
+      uint16_t* orow = out + lane_off + (int64_t)qrow * D;
+#pragma unroll
+      for (int dt = 0; dt < kTilesD; ++dt)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[e] = o[dt][4 * gg + e] * ca + mrg[(dt * 16 + 4 * gg + e) * 64 + l] * cb;
+          u32x2 val;
+          val[0] = E::pack(x[0], x[1]);
+          val[1] = E::pack(x[2], x[3]);
+          *(u32x2*)(orow + 32 * dt + 8 * gg + 4 * h) = val;
+        }
+    }
   }
 }
 
