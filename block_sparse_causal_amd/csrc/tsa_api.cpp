@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -115,6 +116,8 @@ int tsa_build_schedule(const void* keys, int32_t dtype, int64_t S, int64_t D, in
   if (nb > 0) {
     if (keys == nullptr || col_idx == nullptr || workspace == nullptr)
       return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: keys, col_idx and workspace must be non-NULL");
+    if (((uintptr_t)keys) % 2 != 0)
+      return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: keys must be 2-byte aligned");
     const size_t ws = tsa::schedule_workspace_bytes(nb, D);
     if (workspace_bytes < ws)
       return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: workspace of %zu bytes < required %zu",
@@ -191,6 +194,9 @@ int tsa_scheduled_attention_fwd(const void* q, const void* k, const void* v, voi
   if (lanes == 0 || S == 0) return ok();  // empty problem: nothing to read or write
   if (!q || !k || !v || !out || !row_ptr || (nnz > 0 && !col_idx))
     return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: NULL pointer argument");
+  for (const void* p : {q, k, v, (const void*)out})
+    if (((uintptr_t)p) % 16 != 0)
+      return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: q, k, v and out must be 16-byte aligned");
   const size_t bytes = (size_t)(lanes * S * D) * 2;
   const char* o0 = (const char*)out;
   const char* ins[3] = {(const char*)q, (const char*)k, (const char*)v};

@@ -134,7 +134,8 @@ int tsa_dense_causal_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,
  * rescaled by exp(m_prev - m_new), one score tile live at a time.)
  *
  *   q, k, v, out  device, [B, H, S, D] row-major of `dtype` (out has q's dtype).
- *                 [S, D] inputs are B = H = 1.  out must not overlap q, k, v.
+ *                 [S, D] inputs are B = H = 1.  out must not overlap q, k, v; all four
+ *                 must be 16-byte aligned.
  *   D             64 or 128.
  *   row_ptr, col_idx  device int32 CSR with nb = ceil(S/64) rows; `nnz` is the
  *                 number of readable col_idx entries.  Row i must list key

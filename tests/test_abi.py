@@ -69,7 +69,9 @@ def test_max_nnz_rejects_negative(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 64) >= 64 * 64 * 8 + 64 * 64 * 8
+    # centroids always; the distance matrix only when it does not stay in LDS (nb > 128)
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 64) >= 64 * 64 * 8
+    assert lib.tsa_build_schedule_workspace_bytes(64 * 200, 64, 64) >= 200 * 64 * 8 + 200 * 200 * 8
     assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 32) == 0
     assert lib.tsa_build_schedule_workspace_bytes(64 * 5000, 64, 64) == 0
 
