@@ -110,9 +110,10 @@ size_t tsa_build_schedule_workspace_bytes(int64_t S, int64_t D, int32_t block);
  *   nnz_host    host int64 or NULL.  When not NULL the call waits for the
  *               stream and stores row_ptr[nb] (the number of entries) there.
  *   S == 0 builds an empty schedule (row_ptr = {0}).
- * Exact input ties between distances make the MST, and so the salience, depend
- * on tie order; the result is then a valid elder-rule salience for one of the
- * tied orders.
+ * Edges are taken in ascending (length, lower index, higher index) order, a
+ * strict order: exactly tied distances are resolved by the block indices, as a
+ * scan of all pairs in that order resolves them, so the schedule is a function
+ * of the keys alone.
  */
 int tsa_build_schedule(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
                        int32_t sink, int32_t local_radius, int32_t topk, int32_t* row_ptr,

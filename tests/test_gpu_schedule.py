@@ -131,3 +131,44 @@ def test_builder_then_attention_end_to_end(tsa):
     rp_o, ci_o, _ = oracle.build_schedule(k, 64, w.sink, w.local_radius, w.topk)
     want = oracle.masked_attention(q, k, v, rp_o, ci_o, 64)
     assert float(np.max(np.abs(out.cpu().double().numpy() - want))) <= 2e-3
+
+
+def _compare_tied(tsa, keys_cpu, sink, radius, topk, label):
+    """Inputs with exactly tied distances: the edge order (length, lower, higher)
+    decides, on both sides, which pair is taken first."""
+    rp_o, ci_o, sal_o = oracle.build_schedule(keys_cpu, 64, sink, radius, topk)
+    rp, ci, sal = tsa.build_schedule(keys_cpu.to("cuda:0"), 64, sink, radius, topk, return_salience=True)
+    assert np.array_equal(rp.cpu().numpy(), rp_o), label
+    assert np.array_equal(ci.cpu().numpy(), ci_o), label
+    # squared distances are small integers here, so only the square root rounds
+    assert np.allclose(sal.cpu().numpy(), sal_o, rtol=1e-15, atol=0), label
+
+
+def _keys_at(points, D=64):
+    """Keys whose block j has every row equal to points[j] (zero-padded to D)."""
+    nb, p = points.shape
+    keys = torch.zeros(64 * nb, D, dtype=torch.float16)
+    keys[:, :p] = torch.from_numpy(np.repeat(points, 64, axis=0)).to(torch.float16)
+    return keys
+
+
+@pytest.mark.parametrize("nb", [1, 2, 20, 64, 100, 128, 200])
+def test_exact_ties_identical_blocks(tsa, nb):
+    # every distance is 0: the MST is the star of block 0 and every merge is a size tie
+    _compare_tied(tsa, torch.zeros(64 * nb, 64, dtype=torch.float16), 1, 1, 3, f"zeros nb {nb}")
+
+
+@pytest.mark.parametrize("nb", [20, 64, 128, 300])
+def test_exact_ties_shuffled_lattice(tsa, nb):
+    rng = np.random.default_rng(nb)
+    side = int(np.ceil(np.sqrt(nb)))
+    pts = np.array([(x, y) for x in range(side) for y in range(side)][:nb], dtype=np.float64)
+    pts = pts[rng.permutation(nb)]
+    _compare_tied(tsa, _keys_at(pts), 1, 2, 5, f"lattice nb {nb}")
+
+
+@pytest.mark.parametrize("nb", [40, 128, 260])
+def test_exact_ties_repeated_points(tsa, nb):
+    rng = np.random.default_rng(10 + nb)
+    pts = rng.integers(-2, 3, size=(nb, 3)).astype(np.float64)  # many exact duplicates
+    _compare_tied(tsa, _keys_at(pts, D=8), 2, 1, 7, f"repeats nb {nb}")
