@@ -1,6 +1,8 @@
 """Build libtsa.so in-tree with hipcc for gfx950.
 
-    python -m block_sparse_causal_amd.build        # or: python block_sparse_causal_amd/build.py
+    python block_sparse_causal_amd/build.py
+
+(run as a file: importing the package first would load the library being rebuilt)
 
 Every source under csrc/ is compiled to an object in _build/ (in parallel) and
 linked into block_sparse_causal_amd/libtsa.so.  Always rebuilds.

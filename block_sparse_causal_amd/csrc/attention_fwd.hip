@@ -51,6 +51,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 64;
 constexpr int kThreads = 256;  // 4 waves: 2 query halves x 2 key halves
+// Fourth word of a raw buffer resource on gfx9-family targets (32-bit data
+// format, no swizzle, no index stride): loads past the size read as zero.
+[[maybe_unused]] constexpr int kBufferWord3 = 0x00020000;
 
 // Element-type specific pieces: the MFMA, the fp32 -> 2 x 16-bit pack (round to
 // nearest even) and a pairwise add of a packed pair into an fp32 sum.
@@ -163,6 +166,28 @@ __device__ __forceinline__ void lds_wait_all(u32x2 (&x)[N]) {
   for (int e = 0; e < N; ++e) asm volatile("" : "+v"(x[e]));
 }
 
+// Copy one K tile and one V tile (`bytes` each, the rows that exist) into a
+// stage of [K tile | V tile] with buffer loads straight into LDS: op o of wave
+// w moves 1 KB piece (o * kWaves + w), 16 bytes per lane from byte offset
+// off[o] of its tile's rows; the piece lies in the V half exactly when o >=
+// kOpsPerTile.  Loads past `bytes` read as zero.
+// (The host pass of the kernel never runs this; the buffer builtins exist only
+// in the device pass.)
+template <int kOps, int kOpsPerTile, int kWaves>
+__host__ __device__ __forceinline__ void copy_block_to_lds(const uint16_t* kb, const uint16_t* vb,
+                                                           int bytes, const uint32_t (&off)[kOps],
+                                                           uint8_t* stage, int w) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, bytes, kBufferWord3);
+#pragma unroll
+  for (int op = 0; op < kOps; ++op)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op >= kOpsPerTile ? rv : rk,
+                                             (__attribute__((address_space(3))) void*)(stage + (op * kWaves + w) * 1024),
+                                             16, off[op], 0, 0, 0);
+#endif
+}
+
 // Workgroup barrier for the K/V ring.  Each wave has already waited (s_waitcnt)
 // for exactly the copies the next step reads, so the barrier must not drain the
 // copies still in flight, which a fenced __syncthreads() would.  The empty asm
@@ -262,32 +287,14 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     const int c = is_v ? (pc ^ v_swizzle<D>(r)) : (pc ^ (r & 7));
     fill_off[op] = (uint32_t)(key * kRowBytes + 16 * c);
   }
-  // Queue the copy of K and V block j into one stage: every lane moves 16 bytes
-  // per op straight from global memory into LDS (no registers in between).
+  // Queue the copy of K and V block j into one stage (no registers in between).
+  // Rows past S read as zeros: only the last block, on its own diagonal, has
+  // such rows, and the causal mask hides them.
   auto fill = [&](int j, uint8_t* stage) {
-    const char* kb = (const char*)(kg + (int64_t)j * kBlock * D);
-    const char* vb = (const char*)(vg + (int64_t)j * kBlock * D);
-    const int lim = S - j * kBlock;  // rows of this block that exist
-    if (lim >= kBlock) {
-#pragma unroll
-      for (int op = 0; op < kFillOps; ++op) {
-        const bool is_v = (op * kWaves + w) * 64 >= kBlock * kChunksPerRow;  // uniform
-        __builtin_amdgcn_global_load_lds((const void*)((is_v ? vb : kb) + fill_off[op]),
-                                         (__attribute__((address_space(3))) void*)(stage + (op * kWaves + w) * 1024),
-                                         16, 0, 0);
-      }
-    } else {  // partial last block: rows past S are clamped to row S-1
-#pragma unroll
-      for (int op = 0; op < kFillOps; ++op) {
-        const bool is_v = (op * kWaves + w) * 64 >= kBlock * kChunksPerRow;
-        uint32_t off = fill_off[op];
-        const int key = (int)(off / kRowBytes);
-        if (key >= lim) off -= (uint32_t)((key - (lim - 1)) * kRowBytes);
-        __builtin_amdgcn_global_load_lds((const void*)((is_v ? vb : kb) + off),
-                                         (__attribute__((address_space(3))) void*)(stage + (op * kWaves + w) * 1024),
-                                         16, 0, 0);
-      }
-    }
+    const int rows = S - j * kBlock < kBlock ? S - j * kBlock : kBlock;
+    copy_block_to_lds<kFillOps, kTileBytes / 1024 / kWaves, kWaves>(
+        kg + (int64_t)j * kBlock * D, vg + (int64_t)j * kBlock * D, rows * kRowBytes, fill_off,
+        stage, w);
   };
 
   f32x16 o[kTilesD];
