@@ -16,12 +16,13 @@
 //   centroid_kernel   one workgroup per key block: fp64 mean of its keys, stored
 //                     dimension-major (dim d of centroid j at d * nbe + j, nbe =
 //                     nb rounded up to even).
+//   distance_kernel   the nb x nb distance matrix into the workspace, one entry
+//                     per thread over many CUs.
 //   nb <= 128, one workgroup (topology_small):
-//     all-pairs distances into LDS; Boruvka rounds; MST edges ranked; the elder
-//     rule over them in rank order (one wavefront, per-block state in
-//     registers); blocks ranked by salience; CSR rows emitted.
+//     the matrix into LDS; Boruvka rounds; MST edges ranked; the elder rule
+//     over them in rank order (one wavefront, per-block state in registers);
+//     blocks ranked by salience; CSR rows emitted.
 //   nb > 128:
-//     distance_kernel   the nb x nb distance matrix into the workspace;
 //     boruvka_nearest   per block, the least edge to another component;
 //     boruvka_merge     one workgroup: per-component least edge, hooking,
 //                       pointer jumping, new labels, the new MST edges;
@@ -41,7 +42,6 @@ constexpr int kBlock = 64;
 constexpr uint32_t kNoEdge = 0xffffffffu;          // "no candidate" edge tag
 constexpr unsigned long long kNoLen = ~0ull;       // above the bits of +inf
 constexpr int kStageBytes = 16384;                 // least LDS staging of centroid dims
-constexpr size_t kMaxLdsBytes = 160 * 1024;        // LDS of one workgroup on gfx950
 constexpr int kSmallThreads = 512;
 constexpr int kLargeThreads = 1024;
 constexpr int kLargePerThread = 4;                 // blocks per thread in boruvka_merge
@@ -523,109 +523,42 @@ __device__ __forceinline__ void select_and_emit_wave(const double (&sal)[SLOTS],
 // an even count so that the staging area is 16-byte aligned.
 __host__ __device__ constexpr int small_stage_offset(int nb) { return (nb * nb + 1) & ~1; }
 
-// The whole build for nb <= kLdsDistBlocks in one workgroup of 512 threads.
-// Dynamic LDS: small_stage_offset(nb) doubles + a staging area of dc centroid
-// dims (at least kStageBytes, which later holds SmallState).
+// Everything after the distances for nb <= kLdsDistBlocks, in one workgroup of
+// 512 threads.  Dynamic LDS: small_stage_offset(nb) doubles (the distance
+// matrix) + kStageBytes (SmallState).
 template <int SLOTS>
 __global__ __launch_bounds__(kSmallThreads) void topology_small(
-    const double* __restrict__ cent_t, int64_t D, int dc, int nb, int sink, int local_radius,
-    int topk, int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_capacity,
+    const double* __restrict__ dist_g, int nb, int sink, int local_radius, int topk,
+    int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_capacity,
     double* __restrict__ salience) {
   extern __shared__ __attribute__((aligned(16))) double smem[];
   double* dist = smem;
-  double* cbuf = smem + small_stage_offset(nb);  // 16-byte aligned
-  SmallState& A = *reinterpret_cast<SmallState*>(cbuf);
+  SmallState& A = *reinterpret_cast<SmallState*>(smem + small_stage_offset(nb));  // 16-byte aligned
   const int tid = threadIdx.x;
   const double kInf = __builtin_inf();
 
-  // ---- Distances.  Thread task = a 2 x 2 tile (rows i, i+1; columns j, j+1)
-  // of the upper triangle of tiles; both (i, j) and (j, i) are written, from
-  // the same sum over d in ascending order, so the matrix is exactly symmetric.
-  // Centroid dims are staged through LDS, `dc` dims at a time.
+  // ---- Distance matrix (formed by distance_kernel) into LDS, 16 bytes a load.
   {
-    const int nbe = (nb + 1) & ~1;  // centroid row stride (even: 16-byte reads)
-    const int nt = nbe / 2;         // tiles per side
-    const int ntasks = nt * (nt + 1) / 2;
-    constexpr int kMaxTasks = (kLdsDistBlocks / 2) * (kLdsDistBlocks / 2 + 1) / 2;
-    constexpr int kPer = (kMaxTasks + kSmallThreads - 1) / kSmallThreads;
     typedef double f64x2 __attribute__((ext_vector_type(2)));
-    f64x2 acc[kPer][2];
-    int ti[kPer], tj[kPer];
-    // Task p -> tile (bi, bj), bi <= bj, row-major over the upper triangle:
-    // row bi starts at S(bi) = bi * (2 nt - bi + 1) / 2; bi is the root of
-    // S(bi) = p, rounded down, then corrected by one step either way.
-    auto row_start = [&](int b) { return b * (2 * nt - b + 1) / 2; };
+    const int n16 = nb * nb / 2;
+    const f64x2* src = (const f64x2*)dist_g;
+    f64x2* dst = (f64x2*)dist;
+    for (int e0 = 0; e0 < n16; e0 += 4 * kSmallThreads) {
+      f64x2 r[4];  // unconditional (clamped) loads, so that all four are in flight
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int p = tid + k * kSmallThreads;
-      const float q = (float)(2 * nt + 1);
-      int bi = (int)((q - __builtin_sqrtf(fmaxf(q * q - 8.0f * (float)p, 0.0f))) * 0.5f);
-      bi = bi < 0 ? 0 : (bi >= nt ? nt - 1 : bi);
-      if (row_start(bi) > p) --bi;
-      if (bi + 1 < nt && row_start(bi + 1) <= p) ++bi;
-      ti[k] = 2 * bi;
-      tj[k] = 2 * (bi + p - row_start(bi));
-      acc[k][0] = acc[k][1] = f64x2{0.0, 0.0};
-    }
-    for (int64_t d0 = 0; d0 < D; d0 += dc) {
-      const int w = (int)((D - d0) < dc ? (D - d0) : dc);
-      if (d0 > 0) __syncthreads();  // previous chunk consumed
-      {
-        const f64x2* src = (const f64x2*)(cent_t + d0 * nbe);
-        f64x2* dst = (f64x2*)cbuf;
-        const int n16 = w * nbe / 2;
-        for (int e0 = 0; e0 < n16; e0 += 4 * kSmallThreads) {
-          f64x2 r[4];  // unconditional (clamped) loads, so that all four are in flight
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int e = e0 + u * kSmallThreads + tid;
-            r[u] = src[e < n16 ? e : n16 - 1];
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int e = e0 + u * kSmallThreads + tid;
-            if (e < n16) dst[e] = r[u];
-          }
-        }
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kSmallThreads + tid;
+        r[u] = src[e < n16 ? e : n16 - 1];
       }
-      __syncthreads();
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        if (tid + k * kSmallThreads >= ntasks) continue;
-        const double* pi = cbuf + ti[k];
-        const double* pj = cbuf + tj[k];
-        f64x2 a0 = acc[k][0], a1 = acc[k][1];
-#pragma unroll 8
-        for (int d = 0; d < w; ++d) {
-          const f64x2 ci = *(const f64x2*)(pi + d * nbe);
-          const f64x2 cj = *(const f64x2*)(pj + d * nbe);
-          const f64x2 e0 = ci[0] - cj, e1 = ci[1] - cj;
-          a0[0] = __builtin_fma(e0[0], e0[0], a0[0]);
-          a0[1] = __builtin_fma(e0[1], e0[1], a0[1]);
-          a1[0] = __builtin_fma(e1[0], e1[0], a1[0]);
-          a1[1] = __builtin_fma(e1[1], e1[1], a1[1]);
-        }
-        acc[k][0] = a0;
-        acc[k][1] = a1;
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kSmallThreads + tid;
+        if (e < n16) dst[e] = r[u];
       }
     }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      if (tid + k * kSmallThreads >= ntasks) continue;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int i = ti[k] + a, j = tj[k] + b;
-          if (i < nb && j < nb) {
-            const double dd = finite_or_inf(__builtin_sqrt(acc[k][a][b]));
-            dist[i * nb + j] = dd;
-            dist[j * nb + i] = dd;
-          }
-        }
-    }
+    if ((nb & 1) && tid == 0) dist[nb * nb - 1] = dist_g[nb * nb - 1];  // odd element count
   }
-  __syncthreads();  // staging area free from here on
+  __syncthreads();
 
   // ---- Boruvka rounds.
   if (tid < nb) {
@@ -753,18 +686,49 @@ __global__ __launch_bounds__(kSmallThreads) void topology_small(
 
 // ------------------------------------------------------------------ larger schedules
 
+// One 16 x 16 tile of the distance matrix per workgroup, one entry per thread.
+// The tile's 16 + 16 centroids are staged into LDS 64 dims at a time (all loads
+// of a chunk issued before any store), then each entry sums (c_i - c_j)^2 over
+// d in ascending order, so entries (i, j) and (j, i) are bitwise equal.
+constexpr int kDistTile = 16;
+constexpr int kDistDims = 64;
 __global__ __launch_bounds__(256) void distance_kernel(const double* __restrict__ cent_t, int nb,
                                                        int64_t D, double* __restrict__ dist) {
-  const int i = blockIdx.y * 16 + threadIdx.y;
-  const int j = blockIdx.x * 16 + threadIdx.x;
-  if (i >= nb || j >= nb) return;
+  __shared__ double ct[2][kDistDims][kDistTile];  // [i rows | j rows][dim][row]
+  const int i0 = blockIdx.y * kDistTile, j0 = blockIdx.x * kDistTile;
+  const int tid = threadIdx.x;
+  const int ti = tid / kDistTile, tj = tid % kDistTile;
   const int nbe = (nb + 1) & ~1;
   double acc = 0.0;
-  for (int64_t d = 0; d < D; ++d) {
-    const double df = cent_t[d * nbe + i] - cent_t[d * nbe + j];
-    acc = __builtin_fma(df, df, acc);
+  for (int64_t d0 = 0; d0 < D; d0 += kDistDims) {
+    const int w = (int)((D - d0) < kDistDims ? (D - d0) : kDistDims);
+    __syncthreads();  // previous chunk consumed
+    // 2 x w x 16 values over 256 threads: up to 8 per thread, loaded first
+    constexpr int kPer = 2 * kDistDims * kDistTile / 256;
+    double r[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = u * 256 + tid;  // (side, d, row)
+      const int side = e / (kDistDims * kDistTile), rem = e % (kDistDims * kDistTile);
+      const int d = rem / kDistTile, row = rem % kDistTile;
+      const int blk = (side ? j0 : i0) + row;
+      const int dd = d < w ? d : w - 1;
+      r[u] = cent_t[(d0 + dd) * nbe + (blk < nb ? blk : nb - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = u * 256 + tid;
+      (&ct[0][0][0])[e] = r[u];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int d = 0; d < w; ++d) {
+      const double df = ct[0][d][ti] - ct[1][d][tj];
+      acc = __builtin_fma(df, df, acc);
+    }
   }
-  dist[(int64_t)i * nb + j] = finite_or_inf(__builtin_sqrt(acc));
+  const int i = i0 + ti, j = j0 + tj;
+  if (i < nb && j < nb) dist[(int64_t)i * nb + j] = finite_or_inf(__builtin_sqrt(acc));
 }
 
 // One wavefront per block v: the least edge from v to a block of another
@@ -1002,7 +966,7 @@ WorkspaceLayout workspace_layout(int64_t nb, int64_t D) {
   };
   const size_t n = (size_t)nb;
   L.cent = take((size_t)((nb + 1) & ~1) * (size_t)D * sizeof(double));
-  L.dist = take(nb > kLdsDistBlocks ? n * n * sizeof(double) : 0);
+  L.dist = take(n * n * sizeof(double));
   L.comp = take(n * sizeof(int));
   L.state = take(2 * sizeof(int));
   L.best_d = take(n * sizeof(double));
@@ -1043,38 +1007,30 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
+  double* dist = (double*)(ws + L.dist);
+  const unsigned tiles = (unsigned)((nb + kDistTile - 1) / kDistTile);
+  hipLaunchKernelGGL(distance_kernel, dim3(tiles, tiles), dim3(256), 0, stream, cent_t, nb, D,
+                     dist);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
   if (small) {
-    // Stage as many centroid dims as the LDS left over by the matrix allows.
-    const size_t mat = (size_t)small_stage_offset(nb) * sizeof(double);
-    const size_t row = (size_t)((nb + 1) & ~1) * sizeof(double);
-    size_t stage = (size_t)D * row;
-    if (stage > kMaxLdsBytes - mat) stage = (kMaxLdsBytes - mat) / row * row;
-    if (stage < (size_t)kStageBytes) stage = kStageBytes;
-    const int dc = (int)(stage / row);
-    const size_t lds = mat + stage;
+    const size_t lds = (size_t)small_stage_offset(nb) * sizeof(double) + kStageBytes;
     if (nb <= 64) {
       if ((err = allow_lds(topology_small<1>, lds)) != hipSuccess) return err;
-      hipLaunchKernelGGL(topology_small<1>, dim3(1), dim3(kSmallThreads), lds, stream, cent_t, D,
-                         dc, nb, sink, local_radius, topk, row_ptr, col_idx, col_capacity,
-                         salience);
+      hipLaunchKernelGGL(topology_small<1>, dim3(1), dim3(kSmallThreads), lds, stream, dist, nb,
+                         sink, local_radius, topk, row_ptr, col_idx, col_capacity, salience);
     } else {
       if ((err = allow_lds(topology_small<2>, lds)) != hipSuccess) return err;
-      hipLaunchKernelGGL(topology_small<2>, dim3(1), dim3(kSmallThreads), lds, stream, cent_t, D,
-                         dc, nb, sink, local_radius, topk, row_ptr, col_idx, col_capacity,
-                         salience);
+      hipLaunchKernelGGL(topology_small<2>, dim3(1), dim3(kSmallThreads), lds, stream, dist, nb,
+                         sink, local_radius, topk, row_ptr, col_idx, col_capacity, salience);
     }
     return hipGetLastError();
   }
 
-  double* dist = (double*)(ws + L.dist);
   double* best_d = (double*)(ws + L.best_d);
   uint32_t* best_t = (uint32_t*)(ws + L.best_t);
   double* edge_d = (double*)(ws + L.edge_d);
   uint32_t* edge_t = (uint32_t*)(ws + L.edge_t);
-  const unsigned tiles = (unsigned)((nb + 15) / 16);
-  hipLaunchKernelGGL(distance_kernel, dim3(tiles, tiles), dim3(16, 16), 0, stream, cent_t, nb, D,
-                     dist);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   const size_t merge_lds = (size_t)nb * (sizeof(unsigned long long) + sizeof(uint32_t) + 3 * sizeof(int));
   if ((err = allow_lds(boruvka_merge, merge_lds)) != hipSuccess) return err;
   int rounds = 0;
