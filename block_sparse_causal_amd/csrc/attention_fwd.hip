@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace tsa {
@@ -421,46 +423,70 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   }
 
   // Merge the two key halves of each query half, then O / l rounded to the
-  // input type.  Rows with no visible key get 0.  The stage buffers are free
-  // here (every wave has passed the last barrier).
+  // input type (rows with no visible key get 0).  The two waves of a query half
+  // split the head dims: wave kh keeps O tiles [kh, kh + 1) * kTilesD / 2 and
+  // hands the other half, unscaled, to its partner together with its (m, l);
+  // after one barrier each wave combines and stores its half.  The stage
+  // buffers are free here (every wave has passed the last barrier).
   const float l_half = sum_with_other_half(l_run);
-  static_assert((kTilesD * 16 + 2) * 64 * 4 <= 2 * kTileBytes && kStages >= 2, "merge area exceeds a stage");
-  float* mrg = (float*)stages[qh % kStages];
-  if (kh == 1) {
+  constexpr int kHalfTiles = kTilesD / 2;
+  constexpr int kSendStride = kHalfTiles * 16 + 4;  // floats per lane (16-byte aligned, padded)
+  static_assert((4 * 64 * kSendStride + 2 * 2 * 2 * 64) * 4 <= kStages * 2 * kTileBytes,
+                "merge area exceeds the ring");
+  float* const xbase = (float*)&stages[0][0];
+  float* const mlbuf = xbase + 4 * 64 * kSendStride;  // [qh][kh][m, l][lane]
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  // KH is the wave's key half as a compile-time constant, so that the O tiles
+  // are named by constants (a runtime index would put o in scratch memory).
+  auto merge = [&](auto KHc) {
+    constexpr int KH = decltype(KHc)::value;
+    float* send = xbase + ((qh * 2 + KH) * 64 + l) * kSendStride;
 #pragma unroll
-    for (int dt = 0; dt < kTilesD; ++dt)
+    for (int t = 0; t < kHalfTiles; ++t) {
+      constexpr int kSendBase = (1 - KH) * kHalfTiles;  // tiles the partner keeps
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mrg[(dt * 16 + r) * 64 + l] = o[dt][r];
-    mrg[kTilesD * 16 * 64 + l] = m_use;
-    mrg[(kTilesD * 16 + 1) * 64 + l] = l_half;
-  }
-  __syncthreads();
-  if (kh == 0) {
-    const float m_b = mrg[kTilesD * 16 * 64 + l];
-    const float l_b = mrg[(kTilesD * 16 + 1) * 64 + l];
-    const float m = fmaxf(m_use, m_b);
-    const float fa = (m_use == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_use - m);
-    const float fb = (m_b == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_b - m);
-    const float l_tot = l_half * fa + l_b * fb;
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(f32x4*)(send + t * 16 + 4 * g4) =
+            f32x4{o[kSendBase + t][4 * g4], o[kSendBase + t][4 * g4 + 1],
+                  o[kSendBase + t][4 * g4 + 2], o[kSendBase + t][4 * g4 + 3]};
+    }
+    mlbuf[((qh * 2 + KH) * 2 + 0) * 64 + l] = m_use;
+    mlbuf[((qh * 2 + KH) * 2 + 1) * 64 + l] = l_half;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    ring_barrier();
+    constexpr int PK = 1 - KH;
+    const float* recv = xbase + ((qh * 2 + PK) * 64 + l) * kSendStride;
+    const float m_p = mlbuf[((qh * 2 + PK) * 2 + 0) * 64 + l];
+    const float l_p = mlbuf[((qh * 2 + PK) * 2 + 1) * 64 + l];
+    const float m = fmaxf(m_use, m_p);
+    const float fs = (m_use == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_use - m);
+    const float fp = (m_p == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_p - m);
+    const float l_tot = l_half * fs + l_p * fp;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const float ca = fa * inv, cb = fb * inv;
+    const float cs = fs * inv, cp = fp * inv;
     if (qrow < S) {
       uint16_t* orow = out + lane_off + (int64_t)qrow * D;
 #pragma unroll
-      for (int dt = 0; dt < kTilesD; ++dt)
+      for (int t = 0; t < kHalfTiles; ++t) {
+        constexpr int kKeepBase = KH * kHalfTiles;  // tiles this wave keeps
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
+          const f32x4 y = *(const f32x4*)(recv + t * 16 + 4 * gg);
           float x[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            x[e] = o[dt][4 * gg + e] * ca + mrg[(dt * 16 + 4 * gg + e) * 64 + l] * cb;
+          for (int e = 0; e < 4; ++e) x[e] = o[kKeepBase + t][4 * gg + e] * cs + y[e] * cp;
           u32x2 val;
           val[0] = E::pack(x[0], x[1]);
           val[1] = E::pack(x[2], x[3]);
-          *(u32x2*)(orow + 32 * dt + 8 * gg + 4 * h) = val;
+          *(u32x2*)(orow + 32 * (kKeepBase + t) + 8 * gg + 4 * h) = val;
         }
+      }
     }
-  }
+  };
+  if (kh == 0)
+    merge(std::integral_constant<int, 0>{});
+  else
+    merge(std::integral_constant<int, 1>{});
 }
 
 template <int D, bool BF16>
