@@ -253,29 +253,6 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   for (int c = 0; c < kStepsD; ++c)
     qop[c] = *(const u32x4*)(q + lane_off + (int64_t)qrow_c * D + 16 * c + 8 * h);
 
-  // CSR row bounds, clamped to the readable entries (the C ABI caps entries at
-  // int32 range).  The row's column indices are read 64 at a time into one
-  // register per lane and handed out with readlane; a reload drains the memory
-  // counter right away, so no other read of the window ever waits on memory.
-  int p = (int)min((int64_t)max(row_ptr[i], 0), nnz);
-  const int end = (int)max(min((int64_t)row_ptr[i + 1], nnz), (int64_t)p);
-  int win = p;
-  int cols = (p + l < end) ? col_idx[p + l] : -1;
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-  auto next_block = [&](int last) -> int {
-    while (p < end) {
-      if (p - win >= 64) {
-        win = p;
-        cols = (p + l < end) ? col_idx[p + l] : -1;
-        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-      }
-      const int c = __builtin_amdgcn_readlane(cols, p - win);
-      ++p;
-      if (c > last && c <= i) return c;
-    }
-    return -1;
-  };
-
   // Per-lane byte offset, inside a block's rows, of the 16 bytes each fill op
   // moves.  Op o of wave w fills the 1 KB piece (o * kWaves + w) of [K | V].
   uint32_t fill_off[kFillOps];
@@ -297,6 +274,40 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     copy_block_to_lds<kFillOps, kTileBytes / 1024 / kWaves, kWaves>(
         kg + (int64_t)j * kBlock * D, vg + (int64_t)j * kBlock * D, rows * kRowBytes, fill_off,
         stage, w);
+  };
+
+  // CSR row bounds, clamped to the readable entries (the C ABI caps entries at
+  // int32 range).  The row's column indices are read 64 at a time into one
+  // register per lane and handed out with readlane; a reload drains the memory
+  // counter right away, so no other read of the window ever waits on memory.
+  int p = (int)min((int64_t)max(row_ptr[i], 0), nnz);
+  const int end = (int)max(min((int64_t)row_ptr[i + 1], nnz), (int64_t)p);
+  // The row's first block comes from a scalar load, so that its copy is queued
+  // before the per-lane window of column indices arrives.
+  int b_first = -1;
+  if (p < end) {
+    const int c = col_idx[p];
+    if (c >= 0 && c <= i) {
+      b_first = c;
+      ++p;
+    }
+  }
+  int win = p;
+  int cols = (p + l < end) ? col_idx[p + l] : -1;
+  if (b_first >= 0) fill(b_first, stages[0]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  auto next_block = [&](int last) -> int {
+    while (p < end) {
+      if (p - win >= 64) {
+        win = p;
+        cols = (p + l < end) ? col_idx[p + l] : -1;
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      }
+      const int c = __builtin_amdgcn_readlane(cols, p - win);
+      ++p;
+      if (c > last && c <= i) return c;
+    }
+    return -1;
   };
 
   f32x16 o[kTilesD];
@@ -387,11 +398,11 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   // wait until stage t's copy has landed (later copies may stay in flight),
   // barrier, queue the next block into the stage computed one step ago, compute.
   int blk[kStages];
-  blk[0] = next_block(-1);
+  blk[0] = b_first >= 0 ? b_first : next_block(-1);
 #pragma unroll
   for (int t = 1; t < kStages; ++t) blk[t] = -1;
   if (blk[0] >= 0) {
-    fill(blk[0], stages[0]);
+    if (b_first < 0) fill(blk[0], stages[0]);
 #pragma unroll
     for (int t = 1; t < kStages - 1; ++t) {
       blk[t] = blk[t - 1] >= 0 ? next_block(blk[t - 1]) : -1;
