@@ -138,16 +138,6 @@ struct Stages {
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int vmcnt_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
 
-// Wait until at most `later` stages' copies (kFillOps operations each) remain.
-template <int kStages, int kFillOps>
-__device__ __forceinline__ void wait_copies(int later) {
-  if (kStages >= 3 && later >= 1) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(kFillOps));
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-  }
-}
-
 // Transposing LDS read (ds_read_b64_tr_b16), issued through asm so that the
 // compiler does not order it behind the in-flight global->LDS copies of other
 // stages; the values may only be used after lds_wait_all().  Within each
@@ -282,20 +272,29 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   // counter right away, so no other read of the window ever waits on memory.
   int p = (int)min((int64_t)max(row_ptr[i], 0), nnz);
   const int end = (int)max(min((int64_t)row_ptr[i + 1], nnz), (int64_t)p);
-  // The row's first block comes from a scalar load, so that its copy is queued
-  // before the per-lane window of column indices arrives.
-  int b_first = -1;
+  // The row's first two blocks come from scalar loads, so that both ring
+  // stages' copies are queued before the per-lane window of column indices
+  // arrives (the compiler waits for the window only where it is first read).
+  static_assert(kStages == 2, "the prologue below fills exactly two stages");
+  int b_first = -1, b_second = -1;
   if (p < end) {
     const int c = col_idx[p];
     if (c >= 0 && c <= i) {
       b_first = c;
       ++p;
+      if (p < end) {
+        const int c2 = col_idx[p];
+        if (c2 > c && c2 <= i) {
+          b_second = c2;
+          ++p;
+        }
+      }
     }
   }
   int win = p;
   int cols = (p + l < end) ? col_idx[p + l] : -1;
   if (b_first >= 0) fill(b_first, stages[0]);
-  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  if (b_second >= 0) fill(b_second, stages[1]);
   auto next_block = [&](int last) -> int {
     while (p < end) {
       if (p - win >= 64) {
@@ -395,38 +394,37 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   };
 
   // Ring schedule.  blk[t] is the block held by stage t (-1: none).  At stage t:
-  // wait until stage t's copy has landed (later copies may stay in flight),
-  // barrier, queue the next block into the stage computed one step ago, compute.
+  // wait until stage t's copy has landed (the other stage's may stay in
+  // flight), barrier, queue the next block into the stage computed one step ago,
+  // compute.  When the prologue queued two blocks, the first step has nothing
+  // to refill.
   int blk[kStages];
   blk[0] = b_first >= 0 ? b_first : next_block(-1);
-#pragma unroll
-  for (int t = 1; t < kStages; ++t) blk[t] = -1;
+  blk[1] = b_first >= 0 ? b_second : -1;
   if (blk[0] >= 0) {
     if (b_first < 0) fill(blk[0], stages[0]);
-#pragma unroll
-    for (int t = 1; t < kStages - 1; ++t) {
-      blk[t] = blk[t - 1] >= 0 ? next_block(blk[t - 1]) : -1;
-      if (blk[t] >= 0) fill(blk[t], stages[t]);
-    }
-    int last = blk[kStages - 2];  // most recently queued block (-1: row exhausted)
+    bool pre = blk[1] >= 0;  // stage 1 already queued: first step waits for stage 0 only
+    int last = pre ? blk[1] : blk[0];
     bool done = false;
     while (!done) {
 #pragma unroll
       for (int t = 0; t < kStages; ++t) {
         if (!done) {
-          // copies queued after stage t's: blocks in stages t+1 .. t+kStages-2
-          int later = 0;
-#pragma unroll
-          for (int u = 1; u < kStages - 1; ++u) later += blk[(t + u) % kStages] >= 0 ? 1 : 0;
-          wait_copies<kStages, kFillOps>(later);
+          if (pre)
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(kFillOps));
+          else
+            __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
           ring_barrier();
-          const int refill = (t + kStages - 1) % kStages;
-          const int jn = last >= 0 ? next_block(last) : -1;
-          blk[refill] = jn;
-          last = jn;
-          if (jn >= 0) fill(jn, stages[refill]);
+          const int refill = (t + 1) % kStages;
+          if (!pre) {
+            const int jn = last >= 0 ? next_block(last) : -1;
+            blk[refill] = jn;
+            last = jn;
+            if (jn >= 0) fill(jn, stages[refill]);
+          }
+          pre = false;
           compute(blk[t], stages[t]);
-          done = blk[(t + 1) % kStages] < 0;
+          done = blk[refill] < 0;
         }
       }
     }
