@@ -13,16 +13,19 @@
 // parallel steps instead of the nb - 1 sequential steps of Prim or Kruskal.
 //
 // Kernels on the caller's stream:
-//   centroid_kernel   one workgroup per key block: fp64 mean of its keys, stored
-//                     dimension-major (dim d of centroid j at d * nbe + j, nbe =
-//                     nb rounded up to even).
-//   distance_kernel   the nb x nb distance matrix into the workspace, one entry
-//                     per thread over many CUs.
-//   nb <= 128, one workgroup (topology_small):
-//     the matrix into LDS; Boruvka rounds; MST edges ranked; the elder rule
-//     over them in rank order (one wavefront, per-block state in registers);
-//     blocks ranked by salience; CSR rows emitted.
+//   nb <= 128: one launch of schedule_small.  Each workgroup forms the
+//     centroids of one tile of block pairs from the keys and their distances;
+//     the workgroups then elect one (device-coherent flags and a claim word,
+//     no waiting) that finishes alone: the matrix into LDS; Boruvka rounds;
+//     MST edges ranked; the elder rule over them in rank order (one wavefront,
+//     per-block component keys in registers); blocks ranked by salience with
+//     an exact integer key; CSR rows emitted.
 //   nb > 128:
+//     centroid_kernel   one workgroup per key block: fp64 mean of its keys,
+//                       stored dimension-major (dim d of centroid j at
+//                       d * nbe + j, nbe = nb rounded up to even);
+//     distance_kernel   the nb x nb distance matrix, one entry per thread over
+//                       many CUs;
 //     boruvka_nearest   per block, the least edge to another component;
 //     boruvka_merge     one workgroup: per-component least edge, hooking,
 //                       pointer jumping, new labels, the new MST edges;
@@ -32,6 +35,10 @@
 //     finish_kernel     edge ranks, elder rule (union-find in LDS), top-k, CSR.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 
 #include "kernels.h"
 
@@ -67,6 +74,26 @@ __device__ __forceinline__ unsigned long long len_bits(double d) {
 __device__ __forceinline__ double bits_len(unsigned long long b) { return __builtin_bit_cast(double, b); }
 // NaN (from NaN keys) is treated as +inf so that the edge order stays total.
 __device__ __forceinline__ double finite_or_inf(double d) { return d == d ? d : __builtin_inf(); }
+
+// Device-coherent 64-bit store and load (agent scope, relaxed): they bypass
+// the non-coherent caches, so a value stored by one workgroup is seen by a
+// load in another once the store has completed.
+__device__ __forceinline__ void store_coherent(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(double* p, unsigned long long v) {
+  store_coherent(reinterpret_cast<unsigned long long*>(p), v);
+}
+__device__ __forceinline__ unsigned long long load_coherent(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this thread's vector memory operations have completed, and keeps
+// the compiler from moving memory accesses across the wait.
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));  // vmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // ------------------------------------------------------------------ wave helpers
 
@@ -324,88 +351,53 @@ struct SmallState {
   double sort_d[kLdsDistBlocks];              // MST edges, ascending
   uint32_t sort_t[kLdsDistBlocks];
   int rank[kLdsDistBlocks];
-  double sal[kLdsDistBlocks];
-  int topidx[kLdsDistBlocks];
   int nedges;
-  int changed;
 };
 static_assert(sizeof(SmallState) <= kStageBytes, "small-schedule state fits the staging area");
 
-// Elder rule over the MST edges in ascending order, one wavefront, nb <= 64 *
-// SLOTS.  Per block (lane v % 64, slot v / 64): its component's root and size,
-// and its salience.  The smaller component is absorbed (equal sizes: the
-// larger root index); the absorbed root's salience is the edge length; the
-// last survivor keeps 0.
+// Sets block x (uniform) of per-block register array `a` to `val` (uniform).
 template <int SLOTS>
-__device__ __forceinline__ void elder_registers(const double* sd, const uint32_t* st, int ne,
-                                                double (&sal)[SLOTS]) {
+__device__ __forceinline__ void set_block(int (&a)[SLOTS], int x, int val) {
   const int lane = threadIdx.x & 63;
-  int root[SLOTS], csz[SLOTS];
 #pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    root[s] = lane + 64 * s;
-    csz[s] = 1;
-    sal[s] = 0.0;
-  }
-  for (int base = 0; base < ne; base += 64) {
-    const int r = base + lane;
-    const int tw = r < ne ? (int)st[r] : 0;
-    const double dw = r < ne ? sd[r] : 0.0;
-    const int n = ne - base < 64 ? ne - base : 64;
-    for (int k = 0; k < n; ++k) {
-      const int t = read_lane(tw, k);
-      const int a = (int)((uint32_t)t >> 16), b = t & 0xffff;
-      const int ra = block_value<SLOTS>(root, a), rb = block_value<SLOTS>(root, b);
-      const int sa = block_value<SLOTS>(csz, a), sb = block_value<SLOTS>(csz, b);
-      const bool a_survives = sa > sb || (sa == sb && ra < rb);
-      const int surv = a_survives ? ra : rb, absorbed = a_survives ? rb : ra;
-      const int grown = sa + sb;
-      const double w = read_lane(dw, k);
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        const bool in = root[s] == ra || root[s] == rb;
-        root[s] = in ? surv : root[s];
-        csz[s] = in ? grown : csz[s];
-        sal[s] = (lane + 64 * s == absorbed) ? w : sal[s];
-      }
-    }
-  }
+  for (int s = 0; s < SLOTS; ++s) a[s] = (lane + 64 * s == x) ? val : a[s];
 }
 
-// The same rule for nb <= 64 with each block's component held as a 64-bit
-// mask: component sizes are popcounts, and a merge rewrites the lanes of the
-// merged mask.
-__device__ __forceinline__ void elder_masks(const double* sd, const uint32_t* st, int ne,
-                                            double (&sal)[1]) {
+// Elder rule over the MST edges in ascending order, one wavefront, nb <= 64 *
+// SLOTS <= 128.  Every component is named by key (size << 8) | (255 - root),
+// held by each of its blocks: of the two components an edge joins, the larger
+// key belongs to the larger one, or on equal sizes to the lower root index,
+// and its root survives.  The other root is absorbed at that edge.  Output per
+// block v (lane v % 64, slot v / 64): the rank of the edge at which v was
+// absorbed, or -1 for a root that never is.  The absorbed root's salience is
+// that edge's length.
+template <int SLOTS>
+__device__ __forceinline__ void elder_ranks(const uint32_t* st, int ne, int (&dead)[SLOTS]) {
   const int lane = threadIdx.x & 63;
-  uint32_t cm_lo = lane < 32 ? 1u << lane : 0u, cm_hi = lane < 32 ? 0u : 1u << (lane - 32);
-  int root = lane;
-  double s0 = 0.0;
+  int ckey[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    ckey[s] = (1 << 8) | (255 - (lane + 64 * s));
+    dead[s] = -1;
+  }
   for (int base = 0; base < ne; base += 64) {
     const int r = base + lane;
     const uint32_t tw = r < ne ? st[r] : 0u;
     const int aw = (int)(tw >> 16), bw = (int)(tw & 0xffffu);
-    const double dw = r < ne ? sd[r] : 0.0;
-    const int n = ne - base < 64 ? ne - base : 64;
+    const int n = __builtin_amdgcn_readfirstlane(ne - base < 64 ? ne - base : 64);
     for (int k = 0; k < n; ++k) {
       const int a = read_lane(aw, k), b = read_lane(bw, k);
-      const uint64_t ma = ((uint64_t)(uint32_t)read_lane((int)cm_hi, a) << 32) | (uint32_t)read_lane((int)cm_lo, a);
-      const uint64_t mb = ((uint64_t)(uint32_t)read_lane((int)cm_hi, b) << 32) | (uint32_t)read_lane((int)cm_lo, b);
-      const int ra = read_lane(root, a), rb = read_lane(root, b);
-      const int sa = __popcll(ma), sb = __popcll(mb);
-      const bool a_survives = sa > sb || (sa == sb && ra < rb);
-      const int surv = a_survives ? ra : rb, absorbed = a_survives ? rb : ra;
-      const uint64_t m = ma | mb;
-      const double w = read_lane(dw, k);
-      if ((m >> lane) & 1ull) {
-        cm_lo = (uint32_t)m;
-        cm_hi = (uint32_t)(m >> 32);
-        root = surv;
-      }
-      if (lane == absorbed) s0 = w;
+      const uint32_t ka = (uint32_t)block_value<SLOTS>(ckey, a);
+      const uint32_t kb = (uint32_t)block_value<SLOTS>(ckey, b);
+      const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
+      const int absorbed = 255 - (int)(lo & 255u);
+      const int grown = (int)(hi + (lo & ~255u));
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s)
+        ckey[s] = ((uint32_t)ckey[s] == ka || (uint32_t)ckey[s] == kb) ? grown : ckey[s];
+      set_block<SLOTS>(dead, absorbed, base + k);
     }
   }
-  sal[0] = s0;
 }
 
 // Inclusive prefix sum over the wavefront: shifts within each 16-lane row,
@@ -427,45 +419,65 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Top-k selection and CSR emission by one wavefront (nb <= 64 * SLOTS), rows
-// as in select_and_emit.  Row i = lane + 64 * slot writes its own entries.
-// LDS scratch: sal_lds[nb], topidx[nb].
+// Top-k selection and CSR emission by one wavefront (nb <= 64 * SLOTS <= 128),
+// rows as in select_and_emit.  Row i = lane + 64 * slot writes its own entries.
+// dead: per block, the rank of the edge (in sd, ascending lengths) at which it
+// was absorbed, or -1.  LDS scratch: grp[ne].
+//
+// Ranking is by (salience descending, index ascending).  Every salience is an
+// edge length or 0, and sd is sorted, so the salience order is the order of
+// grp = the first rank holding the same length (0 for a zero length); blocks
+// never absorbed have salience 0, which ties with zero-length edges and is
+// below every other length.  key = ((grp + 1) << 8) | (255 - v) is therefore
+// an exact integer form of the ranking, distinct per block, and the top-k set
+// is the blocks whose key is at least the k-th largest key.
 template <int SLOTS>
-__device__ __forceinline__ void select_and_emit_wave(const double (&sal)[SLOTS], int nb, int sink,
-                                                     int local_radius, int topk, double* sal_lds,
-                                                     int* topidx, int32_t* __restrict__ row_ptr,
+__device__ __forceinline__ void select_and_emit_wave(const int (&dead)[SLOTS], const double* sd,
+                                                     int ne, int nb, int sink, int local_radius,
+                                                     int topk, int* grp,
+                                                     int32_t* __restrict__ row_ptr,
                                                      int32_t* __restrict__ col_idx,
                                                      int64_t col_capacity,
                                                      double* __restrict__ salience) {
   const int lane = threadIdx.x & 63;
   const int kk = topk < nb ? topk : nb;
+  // grp per edge rank: the last rank <= j that starts a run of equal lengths.
+  int run = 0;
+  for (int base = 0; base < ne; base += 64) {
+    const int j = base + lane;
+    const bool starts = j < ne && (j == 0 || sd[j - 1] != sd[j]);
+    const uint64_t sm = (uint64_t)__ballot(starts);
+    const uint64_t upto = sm & (lane == 63 ? ~0ull : ((2ull << lane) - 1ull));
+    if (j < ne) grp[j] = upto != 0ull ? base + 63 - __clzll((long long)upto) : run;
+    if (sm != 0ull) run = base + 63 - __clzll((long long)sm);
+  }
+  wave_lds_sync();
+  const int zero_grp = ne > 0 && sd[0] == 0.0 ? 0 : -1;
+  int key[SLOTS];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     const int v = lane + 64 * s;
-    if (v < nb) {
-      sal_lds[v] = sal[s];
-      if (salience != nullptr) salience[v] = sal[s];
-    }
+    const int g = dead[s] >= 0 ? grp[dead[s]] : zero_grp;
+    key[s] = v < nb ? ((g + 1) << 8) | (255 - v) : 0;
+    if (salience != nullptr && v < nb) salience[v] = dead[s] >= 0 ? sd[dead[s]] : 0.0;
   }
-  wave_lds_sync();
-  // Top-k set as one bit mask per slot.
+  // Top-k set as one bit mask per slot: the k-th largest key, bit by bit.
   uint64_t topm[SLOTS];
   if (kk >= nb || kk == 0) {
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) topm[s] = kk == 0 ? 0ull : (uint64_t)__ballot(lane + 64 * s < nb);
   } else {
-    int brank[SLOTS];
+    int thr = 0;
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) brank[s] = 0;
-#pragma unroll 8
-    for (int u = 0; u < nb; ++u) {
-      const double su = sal_lds[u];
+    for (int bit = 15; bit >= 0; --bit) {
+      const int cand = thr | (1 << bit);
+      int cnt = 0;
 #pragma unroll
-      for (int s = 0; s < SLOTS; ++s)
-        brank[s] += (su > sal[s] || (su == sal[s] && u < lane + 64 * s)) ? 1 : 0;
+      for (int s = 0; s < SLOTS; ++s) cnt += __popcll((uint64_t)__ballot(key[s] >= cand));
+      thr = cnt >= kk ? cand : thr;
     }
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) topm[s] = __ballot(lane + 64 * s < nb && brank[s] < kk);
+    for (int s = 0; s < SLOTS; ++s) topm[s] = (uint64_t)__ballot(key[s] >= thr);
   }
   // Selected blocks below x, for a per-lane x in [0, nb].
   auto top_below = [&](int x) -> int {
@@ -480,16 +492,15 @@ __device__ __forceinline__ void select_and_emit_wave(const double (&sal)[SLOTS],
     }
     return c;
   };
-  // Selected blocks in ascending order.
-  int below = 0;
+  // Selected blocks at or above the sinks, one mask per slot (uniform).  Row
+  // i takes the first c_n of them in ascending order, so every row walks the
+  // same list with scalar bit scans and keeps the entries it needs.
+  uint64_t upper[SLOTS];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
-    const uint32_t lo = (uint32_t)topm[s], hi = (uint32_t)(topm[s] >> 32);
-    const int rank = below + (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-    if ((topm[s] >> lane) & 1ull) topidx[rank] = lane + 64 * s;
-    below += __popcll(topm[s]);
+    const int rel = sink - 64 * s;
+    upper[s] = rel <= 0 ? topm[s] : rel >= 64 ? 0ull : topm[s] & ~((1ull << rel) - 1ull);
   }
-  wave_lds_sync();
   // Row sizes, starts, entries.
   int carry = 0;
 #pragma unroll
@@ -499,22 +510,27 @@ __device__ __forceinline__ void select_and_emit_wave(const double (&sal)[SLOTS],
     const int loc_lo = (i - local_radius > sink) ? i - local_radius : sink;
     const int b_n = loc_lo <= i ? i - loc_lo + 1 : 0;
     const int t_hi = i - local_radius - 1;
-    const int c0 = t_hi >= sink ? top_below(sink) : 0;
-    const int c_n = t_hi >= sink ? top_below(t_hi + 1) - c0 : 0;
-    const int n = i < nb ? a_n + c_n + b_n : 0;
+    const int c_n = t_hi >= sink ? top_below(t_hi + 1) - top_below(sink) : 0;
+    const bool row = i < nb;
+    const int n = row ? a_n + c_n + b_n : 0;
     const int incl = wave_inclusive_scan(n);
     const int64_t start = carry + incl - n;
     carry += read_lane(incl, 63);
-    if (i < nb) {
-      row_ptr[i] = (int32_t)start;
-      int64_t pos = start;
-      for (int j = 0; j < a_n; ++j, ++pos)
-        if (pos < col_capacity) col_idx[pos] = j;
-      for (int k = 0; k < c_n; ++k, ++pos)
-        if (pos < col_capacity) col_idx[pos] = topidx[c0 + k];
-      for (int j = loc_lo; j <= i; ++j, ++pos)
-        if (pos < col_capacity) col_idx[pos] = j;
+    if (row) row_ptr[i] = (int32_t)start;
+    int64_t pos = start;
+    for (int j = 0; j < a_n; ++j, ++pos)
+      if (row && pos < col_capacity) col_idx[pos] = j;
+    int k = 0;
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u) {
+      for (uint64_t m = upper[u]; m != 0ull; m &= m - 1ull, ++k) {
+        const int64_t at = pos + k;
+        if (row && k < c_n && at < col_capacity) col_idx[at] = 64 * u + __builtin_ctzll(m);
+      }
     }
+    pos += c_n;
+    for (int j = loc_lo; j <= i; ++j, ++pos)
+      if (row && pos < col_capacity) col_idx[pos] = j;
   }
   if (lane == 0) row_ptr[nb] = carry;
 }
@@ -523,40 +539,37 @@ __device__ __forceinline__ void select_and_emit_wave(const double (&sal)[SLOTS],
 // an even count so that the staging area is 16-byte aligned.
 __host__ __device__ constexpr int small_stage_offset(int nb) { return (nb * nb + 1) & ~1; }
 
-// Everything after the distances for nb <= kLdsDistBlocks, in one workgroup of
-// 512 threads.  Dynamic LDS: small_stage_offset(nb) doubles (the distance
+// Everything after the distances for nb <= kLdsDistBlocks, by one workgroup of
+// 512 threads.  LDS at smem: small_stage_offset(nb) doubles (the distance
 // matrix) + kStageBytes (SmallState).
 template <int SLOTS>
-__global__ __launch_bounds__(kSmallThreads) void topology_small(
-    const double* __restrict__ dist_g, int nb, int sink, int local_radius, int topk,
+__device__ __forceinline__ void small_topology(
+    double* smem, const double* dist_g, int nb, int sink, int local_radius, int topk,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_capacity,
     double* __restrict__ salience) {
-  extern __shared__ __attribute__((aligned(16))) double smem[];
   double* dist = smem;
   SmallState& A = *reinterpret_cast<SmallState*>(smem + small_stage_offset(nb));  // 16-byte aligned
   const int tid = threadIdx.x;
   const double kInf = __builtin_inf();
 
-  // ---- Distance matrix (formed by distance_kernel) into LDS, 16 bytes a load.
+  // ---- Distance matrix (stored by the tile workgroups) into LDS, by
+  // device-coherent loads.
   {
-    typedef double f64x2 __attribute__((ext_vector_type(2)));
-    const int n16 = nb * nb / 2;
-    const f64x2* src = (const f64x2*)dist_g;
-    f64x2* dst = (f64x2*)dist;
-    for (int e0 = 0; e0 < n16; e0 += 4 * kSmallThreads) {
-      f64x2 r[4];  // unconditional (clamped) loads, so that all four are in flight
+    const unsigned long long* src = reinterpret_cast<const unsigned long long*>(dist_g);
+    const int n = nb * nb;
+    for (int e0 = 0; e0 < n; e0 += 8 * kSmallThreads) {
+      unsigned long long r[8];  // unconditional (clamped) loads, so that all eight are in flight
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int e = e0 + u * kSmallThreads + tid;
-        r[u] = src[e < n16 ? e : n16 - 1];
+        r[u] = load_coherent(src + (e < n ? e : n - 1));
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int e = e0 + u * kSmallThreads + tid;
-        if (e < n16) dst[e] = r[u];
+        if (e < n) dist[e] = bits_len(r[u]);
       }
     }
-    if ((nb & 1) && tid == 0) dist[nb * nb - 1] = dist_g[nb * nb - 1];  // odd element count
   }
   __syncthreads();
 
@@ -584,13 +597,22 @@ __global__ __launch_bounds__(kSmallThreads) void topology_small(
       if (v < nb) {
         const int cv = A.comp[v];
         const int j1 = (q + 1) * plen < nb ? (q + 1) * plen : nb;
-        for (int j = q * plen; j < j1; ++j) {
-          if (A.comp[j] == cv) continue;
-          const double d = dist[j * nb + v];
-          const uint32_t t = edge_tag(v, j);
-          if (edge_less(d, t, bd, bt)) {
-            bd = d;
-            bt = t;
+        // Eight candidates a pass: every load is issued before any is used.
+        for (int j0 = q * plen; j0 < j1; j0 += 8) {
+          int cj[8];
+          double dj[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u < nb ? j0 + u : nb - 1;
+            cj[u] = A.comp[j];
+            dj[u] = dist[j * nb + v];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const uint32_t t = edge_tag(v, j0 + u);
+            const bool take = j0 + u < j1 && cj[u] != cv && edge_less(dj[u], t, bd, bt);
+            bd = take ? dj[u] : bd;
+            bt = take ? t : bt;
           }
         }
       }
@@ -602,13 +624,18 @@ __global__ __launch_bounds__(kSmallThreads) void topology_small(
     uint32_t bt = kNoEdge;
     int cv = 0;
     if (tid < nb) {
-      for (int q = 0; q < parts; ++q) {
-        const double d = A.part_d[q * nbp + tid];
-        const uint32_t t = A.part_t[q * nbp + tid];
-        if (edge_less(d, t, bd, bt)) {
-          bd = d;
-          bt = t;
-        }
+      double pd[kSmallThreads / 64];
+      uint32_t pt[kSmallThreads / 64];
+#pragma unroll
+      for (int q = 0; q < kSmallThreads / 64; ++q) {
+        pd[q] = q < parts ? A.part_d[q * nbp + tid] : kInf;
+        pt[q] = q < parts ? A.part_t[q * nbp + tid] : kNoEdge;
+      }
+#pragma unroll
+      for (int q = 0; q < kSmallThreads / 64; ++q) {
+        const bool take = edge_less(pd[q], pt[q], bd, bt);
+        bd = take ? pd[q] : bd;
+        bt = take ? pt[q] : bt;
       }
       cv = A.comp[tid];
       if (bt != kNoEdge) atomicMin(&A.cmin_d[cv], len_bits(bd));
@@ -616,46 +643,38 @@ __global__ __launch_bounds__(kSmallThreads) void topology_small(
     __syncthreads();
     if (tid < nb && bt != kNoEdge && len_bits(bd) == A.cmin_d[cv]) atomicMin(&A.cmin_t[cv], bt);
     __syncthreads();
-    // Each component hooks onto the component across its least edge.
+    // Each component hooks onto the component across its least edge.  Edges are
+    // strictly ordered, so the only cycles are pairs that chose each other, and
+    // such a pair chose the same edge: the lower label stays a root and records
+    // it; every other component records its own edge.
     const bool is_root = tid < nb && A.comp[tid] == tid;
     if (is_root) {
       const uint32_t t = A.cmin_t[tid];  // always an edge while two components remain
       const int lo = (int)(t >> 16), hi = (int)(t & 0xffffu);
-      A.hook[tid] = t == kNoEdge ? tid : A.comp[A.comp[lo] == tid ? hi : lo];
-    }
-    __syncthreads();
-    // Two components that chose each other chose the same edge: the lower label
-    // stays a root and records it; every other component records its own edge.
-    if (is_root) {
-      const int c2 = A.hook[tid];
-      const bool mutual = A.hook[c2] == tid;  // includes c2 == tid (no edge): nothing recorded
-      if (!mutual || tid < c2) {
+      const int c2 = t == kNoEdge ? tid : A.comp[A.comp[lo] == tid ? hi : lo];
+      const bool mutual = c2 == tid || A.cmin_t[c2] == t;  // c2 == tid (no edge): nothing recorded
+      if (!mutual || (tid < c2)) {
         const int pos = atomicAdd(&A.nedges, 1);  // < nb - 1: each edge joins two components
         if (pos < kLdsDistBlocks) {
           A.edge_d[pos] = bits_len(A.cmin_d[tid]);
-          A.edge_t[pos] = A.cmin_t[tid];
+          A.edge_t[pos] = t;
         }
       }
-      A.par[tid] = (mutual && tid < c2) ? tid : c2;
+      A.par[tid] = (mutual && tid <= c2) ? tid : c2;
+    }
+    __syncthreads();
+    // New label of each component: the root of its hook tree, found by walking
+    // the (read-only) parent chain, which ends because the hooks hold no other
+    // cycle.
+    if (is_root) {
+      int x = A.par[tid];
+      for (int y = A.par[x]; y != x; y = A.par[x]) x = y;
+      A.hook[tid] = x;
       A.cmin_d[tid] = kNoLen;
       A.cmin_t[tid] = kNoEdge;
     }
-    // Pointer jumping over the hook forest (depth halves per pass).
-    for (int it = 0; it < 16; ++it) {
-      __syncthreads();
-      const int np = is_root ? A.par[A.par[tid]] : 0;
-      if (tid == 0) A.changed = 0;
-      __syncthreads();
-      if (is_root && np != A.par[tid]) {
-        A.par[tid] = np;
-        A.changed = 1;
-      }
-      __syncthreads();
-      if (!A.changed) break;
-    }
-    const int nc = tid < nb ? A.par[A.comp[tid]] : 0;
     __syncthreads();
-    if (tid < nb) A.comp[tid] = nc;
+    if (tid < nb) A.comp[tid] = A.hook[A.comp[tid]];
     __syncthreads();
   }
   const int ne = A.nedges < nb - 1 ? A.nedges : nb - 1;
@@ -675,13 +694,184 @@ __global__ __launch_bounds__(kSmallThreads) void topology_small(
   if (tid >= 64) return;  // one wavefront from here on
 
   // ---- Elder rule, top-k and CSR rows.
-  double sal[SLOTS];
-  if constexpr (SLOTS == 1)
-    elder_masks(A.sort_d, A.sort_t, ne, sal);
-  else
-    elder_registers<SLOTS>(A.sort_d, A.sort_t, ne, sal);
-  select_and_emit_wave<SLOTS>(sal, nb, sink, local_radius, topk, A.sal, A.topidx, row_ptr, col_idx,
-                              col_capacity, salience);
+  int dead[SLOTS];
+  elder_ranks<SLOTS>(A.sort_t, ne, dead);
+  select_and_emit_wave<SLOTS>(dead, A.sort_d, ne, nb, sink, local_radius, topk, A.rank, row_ptr,
+                              col_idx, col_capacity, salience);
+}
+
+// schedule_small splits the upper triangle of the distance matrix into tiles
+// of TILE x TILE blocks, one per workgroup; TILE is the smallest of 2, 4, 8
+// that keeps the tile count within one workgroup per CU, since a smaller tile
+// means fewer centroids formed per workgroup.
+constexpr int kTileDims = 64;  // centroid dims per pass
+constexpr int kMaxTiles = 256;
+__host__ __device__ constexpr int small_tile_count(int nb, int tile) {
+  return ((nb + tile - 1) / tile) * ((nb + tile - 1) / tile + 1) / 2;
+}
+__host__ __device__ constexpr int small_tile_edge(int nb) {
+  return small_tile_count(nb, 2) <= kMaxTiles ? 2 : small_tile_count(nb, 4) <= kMaxTiles ? 4 : 8;
+}
+// LDS of schedule_small: the topology's, or the tile pass's partial sums
+// [row group][slot][kTileDims] and centroids [kTileDims][16] if that is more.
+__host__ __device__ constexpr size_t small_lds_bytes(int nb) {
+  const size_t topo = (size_t)small_stage_offset(nb) * sizeof(double) + kStageBytes;
+  const size_t tile = (size_t)(kSmallThreads / 8 + 16) * kTileDims * sizeof(double);
+  return topo > tile ? topo : tile;
+}
+
+// The whole schedule for nb <= kLdsDistBlocks in one launch of
+// small_tile_count(nb, TILE) workgroups.  Workgroup w takes tile (ti, tj),
+// ti <= tj, of the block grid: it forms the centroids of its TILE row and TILE
+// column blocks from the keys (fp64 sums, then a division by the row count,
+// as centroid_kernel), and the distances between them: (c_i - c_j)^2 summed
+// with fma over each quarter of every 64 dims, the quarters then added in
+// order.  Each distance is formed once and stored at (i, j) and (j, i).
+//
+// Then the workgroups elect the one that continues with small_topology.  A
+// workgroup publishes `token` (unique to this call) in its flag once its
+// distances are stored; one that then finds every flag equal to the token
+// tries to swap the token into the claim word, and the one that finds the
+// claim not yet holding it wins.  A workgroup reads the flags only after its
+// own flag store has completed, so the one whose store completes last sees
+// every flag: at least one workgroup reaches the swap, and the swap admits
+// one.  No workgroup waits for another, and no flag needs clearing: stale
+// flags hold older tokens.  flags: small_tile_count + 1 words of workspace.
+template <int SLOTS, int TILE, bool BF16>
+__global__ __launch_bounds__(kSmallThreads) void schedule_small(
+    const uint16_t* __restrict__ keys, int64_t S, int64_t D, int nb,
+    double* dist_g, unsigned long long* flags, unsigned long long token, int sink,
+    int local_radius, int topk, int32_t* __restrict__ row_ptr,
+    int32_t* __restrict__ col_idx, int64_t col_capacity,
+    double* __restrict__ salience) {
+  static_assert(TILE == 2 || TILE == 4 || TILE == 8, "tile edge");
+  constexpr int kSlots = 2 * TILE;                           // TILE row + TILE column blocks
+  constexpr int kGroups = kSmallThreads / (8 * kSlots);      // row groups per block
+  constexpr int kRowsPer = kBlock / kGroups;                 // rows per group (= 2 * TILE)
+  extern __shared__ __attribute__((aligned(16))) double smem[];
+  __shared__ int elected;
+  const int tid = threadIdx.x;
+  const int T = (nb + TILE - 1) / TILE;
+  const int ntiles = T * (T + 1) / 2;
+  int ti = 0, w = (int)blockIdx.x;
+  while (w >= T - ti) {
+    w -= T - ti;
+    ++ti;
+  }
+  const int tj = ti + w;
+  const bool diag = ti == tj;
+  // Slot q (below TILE: row blocks, from TILE: column blocks) -> block index;
+  // a diagonal tile's columns are its rows.
+  auto slot_block = [&](int q) { return q < TILE ? ti * TILE + q : tj * TILE + (q - TILE); };
+  auto block_rows = [&](int blk) -> int {
+    const int64_t r0 = (int64_t)blk * kBlock;
+    return blk < nb ? (int)(r0 + kBlock < S ? kBlock : S - r0) : 0;
+  };
+  {
+    double* part = smem;                                     // [row group][slot][dim]
+    double* ct = smem + kGroups * kSlots * kTileDims;        // [dim][16]
+    const int c = tid & 7, g = (tid >> 3) % kGroups, q = tid / (8 * kGroups);  // 8 dims, group, slot
+    const int blk = slot_block(q);
+    const int rows = (diag && q >= TILE) ? 0 : block_rows(blk);
+    const int rlo = kRowsPer * g;
+    const uint16_t* kb = keys + (int64_t)blk * kBlock * D;
+    const bool vec = (D % 8) == 0 && ((uintptr_t)keys % 16) == 0;  // 16-byte aligned rows
+    double acc = 0.0;  // distance (ti*TILE + tid/TILE, tj*TILE + tid%TILE) for tid < TILE^2
+    for (int64_t d0 = 0; d0 < D; d0 += kTileDims) {
+      double sum8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const int64_t dc = d0 + 8 * c;
+      if (rows > rlo && vec && dc + 8 <= D) {
+        // All rows of the group in flight at once (rows past the block's end
+        // re-read its last row and are not added).
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 x[kRowsPer];
+#pragma unroll
+        for (int u = 0; u < kRowsPer; ++u) {
+          const int r = rlo + u < rows ? rlo + u : rows - 1;
+          x[u] = *(const u32x4*)(kb + (int64_t)r * D + dc);
+        }
+#pragma unroll
+        for (int u = 0; u < kRowsPer; ++u) {
+          if (rlo + u < rows) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sum8[2 * e] += key_to_double((uint16_t)(x[u][e] & 0xffffu), BF16);
+              sum8[2 * e + 1] += key_to_double((uint16_t)(x[u][e] >> 16), BF16);
+            }
+          }
+        }
+      } else if (rows > rlo) {
+        const int r1 = rows < rlo + kRowsPer ? rows : rlo + kRowsPer;
+        for (int r = rlo; r < r1; ++r) {
+          const uint16_t* row = kb + (int64_t)r * D;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (dc + e < D) sum8[e] += key_to_double(row[dc + e], BF16);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[(g * kSlots + q) * kTileDims + 8 * c + e] = sum8[e];
+      __syncthreads();
+      for (int e = tid; e < kSlots * kTileDims; e += kSmallThreads) {
+        const int qq = e / kTileDims, d = e % kTileDims;
+        const int src = (diag && qq >= TILE) ? qq - TILE : qq;
+        const int n = block_rows(slot_block(src));
+        double sm = part[src * kTileDims + d];
+#pragma unroll
+        for (int gg = 1; gg < kGroups; ++gg) sm += part[(gg * kSlots + src) * kTileDims + d];
+        ct[d * 16 + qq] = n > 0 ? sm / (double)n : 0.0;
+      }
+      __syncthreads();
+      // Four threads per entry, a quarter of the pass's dims each; the four
+      // partial sums are added to the running sum in dim order.
+      if (tid < 4 * TILE * TILE) {
+        const int ent = tid >> 2, qd = tid & 3;
+        const int i = ent / TILE, j = ent % TILE;
+        const int wd = (int)(D - d0 < kTileDims ? D - d0 : kTileDims);
+        const int da = qd * (kTileDims / 4), db = da + kTileDims / 4 < wd ? da + kTileDims / 4 : wd;
+        double p = 0.0;
+#pragma unroll 16
+        for (int d = da; d < db; ++d) {
+          const double df = ct[d * 16 + i] - ct[d * 16 + TILE + j];
+          p = __builtin_fma(df, df, p);
+        }
+        part[tid] = p;  // the partial sums are consumed above this pass
+      }
+      __syncthreads();
+      if (tid < TILE * TILE) acc += ((part[4 * tid] + part[4 * tid + 1]) + part[4 * tid + 2]) + part[4 * tid + 3];
+      __syncthreads();  // part and ct are rewritten by the next pass
+    }
+    if (tid < TILE * TILE) {
+      const int gi = ti * TILE + tid / TILE, gj = tj * TILE + tid % TILE;
+      if (gi < nb && gj < nb) {
+        const unsigned long long v = len_bits(finite_or_inf(__builtin_sqrt(acc)));
+        store_coherent(dist_g + (int64_t)gi * nb + gj, v);
+        store_coherent(dist_g + (int64_t)gj * nb + gi, v);
+      }
+    }
+  }
+  // ---- Election of the workgroup that builds the schedule.  Every value
+  // that crosses workgroups (distances, flags, the claim) moves by a device-
+  // coherent access that bypasses the non-coherent caches, so ordering needs
+  // only waits for completion, not cache write-back or invalidation.
+  wait_vmem();  // this thread's distance stores have completed
+  __syncthreads();
+  if (tid < 64) {
+    if (tid == 0) store_coherent(&flags[blockIdx.x], token);
+    wait_vmem();  // the flag store completes before any flag is read
+    bool mine = true;
+    for (int t = tid; t < ntiles; t += 64)
+      if (t != (int)blockIdx.x) mine = mine && load_coherent(&flags[t]) == token;
+    const bool all = __ballot(!mine) == 0ull;
+    if (tid == 0)
+      elected = all && __hip_atomic_exchange(&flags[ntiles], token, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) != token;
+    wait_vmem();
+  }
+  __syncthreads();
+  if (!elected) return;
+  small_topology<SLOTS>(smem, dist_g, nb, sink, local_radius, topk, row_ptr, col_idx, col_capacity,
+                        salience);
 }
 
 // ------------------------------------------------------------------ larger schedules
@@ -953,7 +1143,7 @@ __global__ void dense_schedule_kernel(int64_t nb, int32_t* __restrict__ row_ptr,
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t cent, dist, comp, state, best_d, best_t, edge_d, edge_t, total;
+  size_t cent, dist, comp, state, best_d, best_t, edge_d, edge_t, flags, total;
 };
 
 WorkspaceLayout workspace_layout(int64_t nb, int64_t D) {
@@ -973,8 +1163,25 @@ WorkspaceLayout workspace_layout(int64_t nb, int64_t D) {
   L.best_t = take(n * sizeof(uint32_t));
   L.edge_d = take(n * sizeof(double));
   L.edge_t = take(n * sizeof(uint32_t));
+  L.flags = take(nb <= kLdsDistBlocks
+                     ? (size_t)(small_tile_count((int)nb, small_tile_edge((int)nb)) + 1) * sizeof(unsigned long long)
+                     : 0);
   L.total = off;
   return L;
+}
+
+// A value unique to each schedule_small launch of this process: a nonzero
+// 64-bit start drawn from the clock and the process id, then consecutive.
+unsigned long long next_call_token() {
+  static std::atomic<unsigned long long> next{[] {
+    unsigned long long x = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    x ^= (unsigned long long)getpid() << 40;
+    x *= 0x9E3779B97F4A7C15ull;  // spread the bits (Fibonacci hashing constant)
+    return (x ^ (x >> 29)) | 1ull;
+  }()};
+  unsigned long long t = next.fetch_add(1, std::memory_order_relaxed);
+  if (t == 0) t = next.fetch_add(1, std::memory_order_relaxed);
+  return t;
 }
 
 template <typename K>
@@ -997,35 +1204,42 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
   const int nb = (int)nb64;
   const WorkspaceLayout L = workspace_layout(nb, D);
   char* ws = (char*)workspace;
+  double* dist = (double*)(ws + L.dist);
+  hipError_t err;
+  if (nb <= kLdsDistBlocks) {
+    unsigned long long* flags = (unsigned long long*)(ws + L.flags);
+    const unsigned long long token = next_call_token();
+    const size_t lds = small_lds_bytes(nb);
+    const int tile = small_tile_edge(nb);
+    const dim3 grid((unsigned)small_tile_count(nb, tile));
+    auto launch = [&](auto kernel) -> hipError_t {
+      hipError_t e = allow_lds(kernel, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kernel, grid, dim3(kSmallThreads), lds, stream, (const uint16_t*)keys, S,
+                         D, nb, dist, flags, token, sink, local_radius, topk, row_ptr, col_idx,
+                         col_capacity, salience);
+      return hipGetLastError();
+    };
+    if (bf16) {
+      if (nb <= 64)
+        return tile == 2 ? launch(schedule_small<1, 2, true>) : launch(schedule_small<1, 4, true>);
+      return tile == 4 ? launch(schedule_small<2, 4, true>) : launch(schedule_small<2, 8, true>);
+    }
+    if (nb <= 64)
+      return tile == 2 ? launch(schedule_small<1, 2, false>) : launch(schedule_small<1, 4, false>);
+    return tile == 4 ? launch(schedule_small<2, 4, false>) : launch(schedule_small<2, 8, false>);
+  }
+
   double* cent_t = (double*)(ws + L.cent);
-  const bool small = nb <= kLdsDistBlocks;
   int* comp = (int*)(ws + L.comp);
   int* state = (int*)(ws + L.state);
   hipLaunchKernelGGL(centroid_kernel, dim3((unsigned)nb), dim3(256), 0, stream,
-                     (const uint16_t*)keys, bf16, S, D, nb, cent_t, small ? nullptr : comp,
-                     small ? nullptr : state);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  double* dist = (double*)(ws + L.dist);
+                     (const uint16_t*)keys, bf16, S, D, nb, cent_t, comp, state);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const unsigned tiles = (unsigned)((nb + kDistTile - 1) / kDistTile);
   hipLaunchKernelGGL(distance_kernel, dim3(tiles, tiles), dim3(256), 0, stream, cent_t, nb, D,
                      dist);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-
-  if (small) {
-    const size_t lds = (size_t)small_stage_offset(nb) * sizeof(double) + kStageBytes;
-    if (nb <= 64) {
-      if ((err = allow_lds(topology_small<1>, lds)) != hipSuccess) return err;
-      hipLaunchKernelGGL(topology_small<1>, dim3(1), dim3(kSmallThreads), lds, stream, dist, nb,
-                         sink, local_radius, topk, row_ptr, col_idx, col_capacity, salience);
-    } else {
-      if ((err = allow_lds(topology_small<2>, lds)) != hipSuccess) return err;
-      hipLaunchKernelGGL(topology_small<2>, dim3(1), dim3(kSmallThreads), lds, stream, dist, nb,
-                         sink, local_radius, topk, row_ptr, col_idx, col_capacity, salience);
-    }
-    return hipGetLastError();
-  }
 
   double* best_d = (double*)(ws + L.best_d);
   uint32_t* best_t = (uint32_t*)(ws + L.best_t);

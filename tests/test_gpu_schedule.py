@@ -172,3 +172,25 @@ def test_exact_ties_repeated_points(tsa, nb):
     rng = np.random.default_rng(10 + nb)
     pts = rng.integers(-2, 3, size=(nb, 3)).astype(np.float64)  # many exact duplicates
     _compare_tied(tsa, _keys_at(pts, D=8), 2, 1, 7, f"repeats nb {nb}")
+
+
+@pytest.mark.parametrize("nb,D", [(3, 20), (17, 200), (64, 64), (100, 72), (128, 128)])
+def test_reused_and_prefilled_workspace(tsa, nb, D):
+    """One set of buffers serves several builds with different keys, and the
+    workspace is filled with zeros, ones or a byte pattern before some builds:
+    every schedule still matches the oracle, so the builder needs no cleared
+    workspace and leaves nothing behind that misleads the next call."""
+    S = 64 * nb - 7
+    bufs = tsa.ScheduleBuffers(S, D, 1, 2, 5, "cuda:0", salience=True)
+    for it, fill in enumerate([None, 0x00, 0xFF, None, 0x5A, None]):
+        keys = workloads.random_normal((S, D), "bf16", 4000 + 10 * nb + it)
+        if fill is not None:
+            bufs._ws.fill_(fill)
+        tsa.build_schedule_into(keys.to("cuda:0"), bufs)
+        rp_o, ci_o, sal_o = oracle.build_schedule(keys, 64, 1, 2, 5)
+        rp = bufs.row_ptr.cpu().numpy()
+        nnz = int(rp[-1])
+        label = f"nb {nb} D {D} build {it} fill {fill}"
+        assert np.array_equal(rp, rp_o), label
+        assert np.array_equal(bufs.col_idx[:nnz].cpu().numpy(), ci_o), label
+        assert np.allclose(bufs.salience.cpu().numpy(), sal_o, rtol=1e-12, atol=0), label
