@@ -179,13 +179,16 @@ def main() -> int:
     step_ms = start.elapsed_time(end) / args.steps
     print(f"# timed {args.steps} steps in {wall:.3f} s wall", file=sys.stderr, flush=True)
 
-    # Kernel pass: the same K steps again, with events on the attention kernel's
-    # stream around each of its launches; their mean is the kernel's launch
-    # duration behind the roofline figures.
+    # Kernel pass: the same K steps again, with events on the kernels' stream
+    # before the schedule build, between it and the attention kernel, and after
+    # that kernel.  Their means give the build time and the attention kernel's
+    # launch duration behind the roofline figures.
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
+        ev_s[i].record(stream)
         step()
         ev_a[i].record(stream)
         attention()
@@ -193,6 +196,7 @@ def main() -> int:
     torch.cuda.synchronize()
     attn_ms_each = sorted(a.elapsed_time(b) for a, b in zip(ev_a, ev_b))
     attn_ms = sum(attn_ms_each) / len(attn_ms_each)
+    build_ms = sum(s.elapsed_time(a) for s, a in zip(ev_s, ev_a)) / args.steps
 
     # Same kernel over the dense causal CSR at the same shape (like-for-like baseline).
     drp, dci = tsa.dense_causal_schedule(w.nb, dev)
@@ -253,7 +257,7 @@ def main() -> int:
         "frac_of_peak": round(value / peak, 4),
         "attention_ms": round(attn_ms, 5),
         "attention_ms_min": round(attn_ms_each[0], 5),
-        "builder_ms": round(step_ms - attn_ms, 5),
+        "builder_ms": round(build_ms, 5),
         "attention_tflops": round(attn_tflops, 3),
         "attention_frac_of_peak": round(attn_tflops / peak, 4),
         "attention_tflops_causal_exact": round(flops_exact / (attn_ms * 1e-3) / 1e12, 3),
