@@ -106,7 +106,10 @@ size_t tsa_build_schedule_workspace_bytes(int64_t S, int64_t D, int32_t block);
  *               local_radius, topk), so the build can never overflow it.
  *   salience    device double [nb] or NULL; written when not NULL.
  *   workspace   device, >= tsa_build_schedule_workspace_bytes(S, D, 64) bytes,
- *               256-byte aligned; contents on return are unspecified.
+ *               256-byte aligned.  Its contents on entry may be anything (it needs
+ *               no clearing) and are unspecified on return.  Two builds that may
+ *               run at the same time (on different streams) must not share one
+ *               workspace.
  *   nnz_host    host int64 or NULL.  When not NULL the call waits for the
  *               stream and stores row_ptr[nb] (the number of entries) there.
  *   S == 0 builds an empty schedule (row_ptr = {0}).
