@@ -11,7 +11,8 @@ What it computes (all in float64, numpy only):
   sparse attention kernel" (triton-lang/kernels pull request 22): sink blocks,
   a local window and the top-k key blocks ranked by elder-rule 0-dimensional
   persistence (H0) salience of the key-block centroids, built by brute force
-  over ALL centroid pairs (no MST shortcut); plus the dense causal CSR.
+  over ALL centroid pairs (no MST shortcut); plus the dense causal CSR and the
+  fixed-segment (block-diagonal causal) CSR.
 * ``attention`` -- dense masked attention: every query row takes a full-width
   softmax over the keys its CSR row allows, with the causal constraint
   (key position <= query position).
@@ -28,6 +29,7 @@ from .schedule import (
     schedule_from_salience,
     build_schedule,
     dense_causal_schedule,
+    fixed_segment_schedule,
     csr_to_block_sets,
 )
 from .attention import allowed_key_mask, masked_attention, masked_attention_rows
@@ -40,6 +42,7 @@ __all__ = [
     "schedule_from_salience",
     "build_schedule",
     "dense_causal_schedule",
+    "fixed_segment_schedule",
     "csr_to_block_sets",
     "allowed_key_mask",
     "masked_attention",
