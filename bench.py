@@ -220,6 +220,22 @@ def main() -> int:
     d1.record(stream)
     torch.cuda.synchronize()
     sparse_ms = d0.elapsed_time(d1) / reps
+    # The fixed-segment CSR (512-token segments) at the same shape, timed the same way.
+    seg = None
+    if w.S % 512 == 0:
+        srp, sci = tsa.segment_schedule(w.nb, 512 // 64, dev)
+        seg_nnz = int(sci.shape[0])
+        for _ in range(3):
+            tsa.scheduled_attention(q, k, v, srp, sci, out=out)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for _ in range(reps):
+            tsa.scheduled_attention(q, k, v, srp, sci, out=out)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        seg_ms = d0.elapsed_time(d1) / reps
+        seg = {"segment_tokens": 512, "nnz_blocks": seg_nnz, "ms": round(seg_ms, 5),
+               "tflops": round(lanes * seg_nnz * 4 * 64 * 64 * w.D / (seg_ms * 1e-3) / 1e12, 3)}
     if not bool(torch.isfinite(out).all()):
         print("non-finite output", file=sys.stderr)
         return 1
@@ -266,6 +282,7 @@ def main() -> int:
         "sparse_vs_dense_csr_speedup": round(dense_ms / sparse_ms, 3),
         "ideal_speedup": round(nnz_dense / nnz, 3),
         "dense_csr_tflops": round(lanes * nnz_dense * 4 * 64 * 64 * w.D / (dense_ms * 1e-3) / 1e12, 3),
+        "segment_csr": seg,
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tflops, 3),

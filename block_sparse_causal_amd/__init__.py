@@ -12,6 +12,7 @@ triton-lang/kernels PR 22, Summary):
 
 * ``build_schedule``       sink + local window + top-k salient key blocks -> CSR
 * ``dense_causal_schedule`` the lower-triangular CSR
+* ``segment_schedule``      the fixed-segment (block-diagonal causal) CSR
 * ``scheduled_attention``  forward causal attention over a CSR block schedule
 """
 from __future__ import annotations
@@ -30,6 +31,7 @@ __all__ = [
     "ScheduleBuffers",
     "build_schedule_into",
     "dense_causal_schedule",
+    "segment_schedule",
     "scheduled_attention",
 ]
 
@@ -75,6 +77,10 @@ def _load():
     ]
     lib.tsa_dense_causal_schedule.restype = ctypes.c_int
     lib.tsa_dense_causal_schedule.argtypes = [i64, vp, vp, i64, vp]
+    lib.tsa_segment_schedule_nnz.restype = i64
+    lib.tsa_segment_schedule_nnz.argtypes = [i64, i32]
+    lib.tsa_segment_schedule.restype = ctypes.c_int
+    lib.tsa_segment_schedule.argtypes = [i64, i32, vp, vp, i64, vp]
     lib.tsa_scheduled_attention_fwd.restype = ctypes.c_int
     lib.tsa_scheduled_attention_fwd.argtypes = [
         vp, vp, vp, vp, i32, i64, i64, i64, i64, vp, vp, i64, i32, ctypes.c_float, vp
@@ -219,6 +225,22 @@ def dense_causal_schedule(nb: int, device) -> tuple[torch.Tensor, torch.Tensor]:
         col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
         status = _lib.tsa_dense_causal_schedule(nb, _ptr(row_ptr), _ptr(col_idx), nnz, _stream(dev))
     _check(status, "dense_causal_schedule")
+    return row_ptr, col_idx[:nnz]
+
+
+def segment_schedule(nb: int, segment_blocks: int, device) -> tuple[torch.Tensor, torch.Tensor]:
+    """Fixed-segment (block-diagonal causal) CSR for nb blocks on ``device``: row i
+    lists blocks L*(i//L) .. i for L = segment_blocks (int32 row_ptr, col_idx)."""
+    dev = torch.device(device)
+    nnz = int(_lib.tsa_segment_schedule_nnz(nb, segment_blocks))
+    if nnz < 0:
+        raise ValueError(f"segment_schedule: invalid nb={nb} or segment_blocks={segment_blocks}")
+    with torch.cuda.device(dev):
+        row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+        col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        status = _lib.tsa_segment_schedule(nb, segment_blocks, _ptr(row_ptr), _ptr(col_idx), nnz,
+                                           _stream(dev))
+    _check(status, "segment_schedule")
     return row_ptr, col_idx[:nnz]
 
 

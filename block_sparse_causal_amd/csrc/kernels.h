@@ -27,5 +27,7 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
 
 hipError_t launch_dense_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,
                                  hipStream_t stream);
+hipError_t launch_segment_schedule(int64_t nb, int64_t segment_blocks, int32_t* row_ptr,
+                                   int32_t* col_idx, hipStream_t stream);
 
 }  // namespace tsa

@@ -585,6 +585,7 @@ __device__ __forceinline__ void small_topology(
   const int nbp = (nb + 63) & ~63;           // 64 or 128: divides kSmallThreads
   const int parts = kSmallThreads / nbp;
   const int plen = (nb + parts - 1) / parts;
+  int nedges = 0;                             // MST edges so far (wavefront 0)
   for (int round = 0; round < 16; ++round) {  // ceil(log2 128) = 7 rounds suffice
     if (A.nedges >= nb - 1) break;
     // Least edge from each block to another component, over one part of the
@@ -620,61 +621,95 @@ __device__ __forceinline__ void small_topology(
       A.part_t[tid] = bt;
     }
     __syncthreads();
-    double bd = kInf;
-    uint32_t bt = kNoEdge;
-    int cv = 0;
-    if (tid < nb) {
-      double pd[kSmallThreads / 64];
-      uint32_t pt[kSmallThreads / 64];
+    // The rest of the round on one wavefront: block v = lane + 64 * slot.
+    if (tid < 64) {
+      const int lane = tid;
+      double bd[SLOTS];
+      uint32_t bt[SLOTS];
+      int cv[SLOTS];
 #pragma unroll
-      for (int q = 0; q < kSmallThreads / 64; ++q) {
-        pd[q] = q < parts ? A.part_d[q * nbp + tid] : kInf;
-        pt[q] = q < parts ? A.part_t[q * nbp + tid] : kNoEdge;
-      }
+      for (int sl = 0; sl < SLOTS; ++sl) {
+        const int v = lane + 64 * sl;
+        bd[sl] = kInf;
+        bt[sl] = kNoEdge;
+        cv[sl] = v;
+        if (v < nb) {
+          double pd[kSmallThreads / 64];
+          uint32_t pt[kSmallThreads / 64];
 #pragma unroll
-      for (int q = 0; q < kSmallThreads / 64; ++q) {
-        const bool take = edge_less(pd[q], pt[q], bd, bt);
-        bd = take ? pd[q] : bd;
-        bt = take ? pt[q] : bt;
-      }
-      cv = A.comp[tid];
-      if (bt != kNoEdge) atomicMin(&A.cmin_d[cv], len_bits(bd));
-    }
-    __syncthreads();
-    if (tid < nb && bt != kNoEdge && len_bits(bd) == A.cmin_d[cv]) atomicMin(&A.cmin_t[cv], bt);
-    __syncthreads();
-    // Each component hooks onto the component across its least edge.  Edges are
-    // strictly ordered, so the only cycles are pairs that chose each other, and
-    // such a pair chose the same edge: the lower label stays a root and records
-    // it; every other component records its own edge.
-    const bool is_root = tid < nb && A.comp[tid] == tid;
-    if (is_root) {
-      const uint32_t t = A.cmin_t[tid];  // always an edge while two components remain
-      const int lo = (int)(t >> 16), hi = (int)(t & 0xffffu);
-      const int c2 = t == kNoEdge ? tid : A.comp[A.comp[lo] == tid ? hi : lo];
-      const bool mutual = c2 == tid || A.cmin_t[c2] == t;  // c2 == tid (no edge): nothing recorded
-      if (!mutual || (tid < c2)) {
-        const int pos = atomicAdd(&A.nedges, 1);  // < nb - 1: each edge joins two components
-        if (pos < kLdsDistBlocks) {
-          A.edge_d[pos] = bits_len(A.cmin_d[tid]);
-          A.edge_t[pos] = t;
+          for (int q = 0; q < kSmallThreads / 64; ++q) {
+            pd[q] = q < parts ? A.part_d[q * nbp + v] : kInf;
+            pt[q] = q < parts ? A.part_t[q * nbp + v] : kNoEdge;
+          }
+#pragma unroll
+          for (int q = 0; q < kSmallThreads / 64; ++q) {
+            const bool take = edge_less(pd[q], pt[q], bd[sl], bt[sl]);
+            bd[sl] = take ? pd[q] : bd[sl];
+            bt[sl] = take ? pt[q] : bt[sl];
+          }
+          cv[sl] = A.comp[v];
+          if (bt[sl] != kNoEdge) atomicMin(&A.cmin_d[cv[sl]], len_bits(bd[sl]));
         }
       }
-      A.par[tid] = (mutual && tid <= c2) ? tid : c2;
+      wave_lds_sync();
+#pragma unroll
+      for (int sl = 0; sl < SLOTS; ++sl)
+        if (lane + 64 * sl < nb && bt[sl] != kNoEdge && len_bits(bd[sl]) == A.cmin_d[cv[sl]])
+          atomicMin(&A.cmin_t[cv[sl]], bt[sl]);
+      wave_lds_sync();
+      // Each component hooks onto the component across its least edge.  Edges
+      // are strictly ordered, so the only cycles are pairs that chose each
+      // other, and such a pair chose the same edge: the lower label stays a
+      // root and records it; every other component records its own edge.
+      bool root[SLOTS];
+#pragma unroll
+      for (int sl = 0; sl < SLOTS; ++sl) {
+        const int v = lane + 64 * sl;
+        root[sl] = v < nb && cv[sl] == v;
+        bool rec = false;
+        uint32_t t = kNoEdge;
+        if (root[sl]) {
+          t = A.cmin_t[v];  // always an edge while two components remain
+          const int lo = (int)(t >> 16), hi = (int)(t & 0xffffu);
+          const int c2 = t == kNoEdge ? v : A.comp[A.comp[lo] == v ? hi : lo];
+          const bool mutual = c2 == v || A.cmin_t[c2] == t;  // c2 == v (no edge): nothing recorded
+          rec = !mutual || v < c2;
+          A.par[v] = (mutual && v <= c2) ? v : c2;
+        }
+        const uint64_t m = (uint64_t)__ballot(rec);
+        const int pos = nedges + (int)__builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (rec) {  // pos < nb - 1: each edge joins two components
+          A.edge_d[pos] = bits_len(A.cmin_d[v]);
+          A.edge_t[pos] = t;
+        }
+        nedges += __popcll(m);
+      }
+      wave_lds_sync();
+      // New label of each component: the root of its hook tree, found by
+      // walking the parent chain, which ends because the hooks hold no other
+      // cycle.
+#pragma unroll
+      for (int sl = 0; sl < SLOTS; ++sl) {
+        const int v = lane + 64 * sl;
+        if (root[sl]) {
+          int x = A.par[v];
+          for (int y = A.par[x]; y != x; y = A.par[x]) x = y;
+          A.hook[v] = x;
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int sl = 0; sl < SLOTS; ++sl) {
+        const int v = lane + 64 * sl;
+        if (v < nb) A.comp[v] = A.hook[cv[sl]];
+        if (root[sl]) {
+          A.cmin_d[v] = kNoLen;
+          A.cmin_t[v] = kNoEdge;
+        }
+      }
+      if (lane == 0) A.nedges = nedges;
     }
-    __syncthreads();
-    // New label of each component: the root of its hook tree, found by walking
-    // the (read-only) parent chain, which ends because the hooks hold no other
-    // cycle.
-    if (is_root) {
-      int x = A.par[tid];
-      for (int y = A.par[x]; y != x; y = A.par[x]) x = y;
-      A.hook[tid] = x;
-      A.cmin_d[tid] = kNoLen;
-      A.cmin_t[tid] = kNoEdge;
-    }
-    __syncthreads();
-    if (tid < nb) A.comp[tid] = A.hook[A.comp[tid]];
     __syncthreads();
   }
   const int ne = A.nedges < nb - 1 ? A.nedges : nb - 1;
@@ -1140,6 +1175,21 @@ __global__ void dense_schedule_kernel(int64_t nb, int32_t* __restrict__ row_ptr,
     for (int64_t j = 0; j <= i; ++j) col_idx[base + j] = (int32_t)j;
 }
 
+// Fixed segments of L blocks: row i lists blocks L*(i/L) .. i.  Row i starts
+// after i/L full segments of L(L+1)/2 entries and the first i%L rows of its
+// own segment, so every row and its entries have a closed form; one thread
+// per row, the last thread writes row_ptr[nb].
+__global__ void segment_schedule_kernel(int64_t nb, int64_t L, int32_t* __restrict__ row_ptr,
+                                        int32_t* __restrict__ col_idx) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i > nb) return;
+  const int64_t q = i / L, r = i % L;
+  const int64_t base = q * (L * (L + 1) / 2) + r * (r + 1) / 2;
+  row_ptr[i] = (int32_t)base;
+  if (i < nb)
+    for (int64_t j = 0; j <= r; ++j) col_idx[base + j] = (int32_t)(q * L + j);
+}
+
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
@@ -1262,6 +1312,15 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
   hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kLargeThreads), finish_lds, stream, nb, state,
                      edge_d, edge_t, sink, local_radius, topk, row_ptr, col_idx, col_capacity,
                      salience);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_schedule(int64_t nb, int64_t segment_blocks, int32_t* row_ptr,
+                                   int32_t* col_idx, hipStream_t stream) {
+  const int64_t rows = nb + 1;
+  const unsigned grid = (unsigned)((rows + 255) / 256);
+  hipLaunchKernelGGL(segment_schedule_kernel, dim3(grid), dim3(256), 0, stream, nb, segment_blocks,
+                     row_ptr, col_idx);
   return hipGetLastError();
 }
 

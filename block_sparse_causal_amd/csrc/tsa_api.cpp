@@ -167,6 +167,37 @@ int tsa_dense_causal_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,
   return ok();
 }
 
+int64_t tsa_segment_schedule_nnz(int64_t nb, int32_t segment_blocks) {
+  if (nb < 0 || segment_blocks < 1) return -1;
+  const int64_t L = segment_blocks < nb ? segment_blocks : (nb > 0 ? nb : 1);
+  const int64_t q = nb / L, r = nb % L;
+  return q * (L * (L + 1) / 2) + r * (r + 1) / 2;
+}
+
+int tsa_segment_schedule(int64_t nb, int32_t segment_blocks, int32_t* row_ptr, int32_t* col_idx,
+                         int64_t col_capacity, void* stream) {
+  if (nb < 0) return fail(TSA_ERR_INVALID_ARG, "tsa_segment_schedule: nb must be >= 0");
+  if (segment_blocks < 1)
+    return fail(TSA_ERR_INVALID_ARG, "tsa_segment_schedule: segment_blocks must be >= 1, got %d",
+                segment_blocks);
+  const int64_t need = tsa_segment_schedule_nnz(nb, segment_blocks);
+  if (need > INT32_MAX)
+    return fail(TSA_ERR_SHAPE, "tsa_segment_schedule: %lld entries exceed int32 offsets",
+                (long long)need);
+  if (col_capacity < need)
+    return fail(TSA_ERR_SCHEDULE, "tsa_segment_schedule: col_capacity %lld < %lld",
+                (long long)col_capacity, (long long)need);
+  if (row_ptr == nullptr || (nb > 0 && col_idx == nullptr))
+    return fail(TSA_ERR_INVALID_ARG, "tsa_segment_schedule: NULL output");
+  int rc;
+  if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
+  if (nb > 0 && (rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
+  const int64_t L = segment_blocks < nb ? segment_blocks : (nb > 0 ? nb : 1);
+  hipError_t e = tsa::launch_segment_schedule(nb, L, row_ptr, col_idx, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "segment schedule kernel");
+  return ok();
+}
+
 int tsa_scheduled_attention_fwd(const void* q, const void* k, const void* v, void* out,
                                 int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D,
                                 const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,

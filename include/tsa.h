@@ -133,6 +133,28 @@ int tsa_dense_causal_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,
                               int64_t col_capacity, void* stream);
 
 /*
+ * Entries of the fixed-segment CSR for nb blocks and segments of segment_blocks
+ * blocks (below).  Host-only; returns -1 if nb < 0 or segment_blocks < 1.
+ */
+int64_t tsa_segment_schedule_nnz(int64_t nb, int32_t segment_blocks);
+
+/*
+ * The fixed-segment (block-diagonal causal) CSR: with L = segment_blocks, row i
+ * lists blocks L*floor(i/L) .. i, so attention never crosses a segment
+ * boundary.  (Mirror page, commit note on learned segment boundaries: a merged
+ * causal CSR kernel consumes segment boundaries exactly; fixed 512- and 256-token
+ * segments at S 4096 visit 288 and 160 blocks.)
+ *   row_ptr   device int32 [nb + 1], written.
+ *   col_idx   device int32 [col_capacity], entries [0, nnz) written;
+ *             col_capacity >= tsa_segment_schedule_nnz(nb, segment_blocks).
+ * Errors: nb < 0 or segment_blocks < 1 (TSA_ERR_INVALID_ARG), more entries than
+ * int32 offsets hold (TSA_ERR_SHAPE), a short col_idx (TSA_ERR_SCHEDULE), NULL
+ * or non-device pointers.  Nothing is written on error.
+ */
+int tsa_segment_schedule(int64_t nb, int32_t segment_blocks, int32_t* row_ptr, int32_t* col_idx,
+                         int64_t col_capacity, void* stream);
+
+/*
  * Forward scheduled attention.  (PR page, Summary, first, third and fourth
  * bullets; mirror page, Rust-port commit note: running row max and denominator
  * rescaled by exp(m_prev - m_new), one score tile live at a time.)

@@ -29,8 +29,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for required in ("tsa_build_schedule", "tsa_scheduled_attention_fwd", "tsa_dense_causal_schedule",
-                     "tsa_schedule_max_nnz", "tsa_build_schedule_workspace_bytes", "tsa_last_error",
-                     "tsa_version"):
+                     "tsa_segment_schedule", "tsa_segment_schedule_nnz", "tsa_schedule_max_nnz",
+                     "tsa_build_schedule_workspace_bytes", "tsa_last_error", "tsa_version"):
         assert required in names
 
 
@@ -61,6 +61,24 @@ def test_max_nnz_bound_holds_for_oracle_schedules(lib):
         s, r, k = (int(x) for x in rng.integers(0, 6, 3))
         rp, _, _ = oracle.build_schedule(rng.standard_normal((64 * nb, 4)), 64, s, r, k)
         assert rp[-1] <= lib.tsa_schedule_max_nnz(nb, s, r, k)
+
+
+@pytest.mark.parametrize("nb,seg", [(64, 8), (64, 4), (64, 64), (64, 100), (0, 3), (1, 1), (13, 5),
+                                    (100, 7)])
+def test_segment_nnz_matches_oracle(lib, nb, seg):
+    import oracle
+
+    rp, _ = oracle.fixed_segment_schedule(nb, seg)
+    assert lib.tsa_segment_schedule_nnz(nb, seg) == int(rp[-1])
+
+
+def test_segment_schedule_checks_before_gpu(lib):
+    vp = ctypes.c_void_p
+    assert lib.tsa_segment_schedule_nnz(4, 0) == -1 and lib.tsa_segment_schedule_nnz(-1, 2) == -1
+    assert lib.tsa_segment_schedule(4, 0, vp(None), vp(None), 10, vp(None)) == -1
+    assert b"segment_blocks" in lib.tsa_last_error()
+    assert lib.tsa_segment_schedule(64, 8, vp(None), vp(None), 287, vp(None)) == -4  # short col_idx
+    assert lib.tsa_segment_schedule(64, 8, vp(None), vp(None), 288, vp(None)) == -1  # NULL outputs
 
 
 def test_max_nnz_rejects_negative(lib):
