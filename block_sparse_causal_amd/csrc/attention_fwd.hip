@@ -14,7 +14,9 @@
 //   running max, denominator and O, and the two key halves of a query half are
 //   merged once at the end.  Workgroup ids are remapped so that each of the 8
 //   XCDs receives a contiguous range of lanes (its L2 then holds those lanes'
-//   K/V); within a lane, query blocks run longest-row first.
+//   K/V).  Within that range the query blocks run by position, longest rows
+//   first: the last query block of every lane of the range, then the one
+//   before it, and so on, so that the short rows form the tail of the launch.
 //
 // Contractions (v_mfma_f32_32x32x16_{f16,bf16}, fp32 accumulation)
 //   S^T = K . Q^T : A = K rows (keys) from LDS, B = Q^T held in registers.  The
@@ -225,11 +227,22 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   const int g = l >> 4;     // 16-lane group
   const int gi = l & 15;
 
+  // Workgroup b runs on XCD b % 8; XCD x takes lane group x (lanes / 8 lanes)
+  // and position u / lx = nb - 1 - i of its lanes in turn.
   const uint32_t G = gridDim.x;
   const uint32_t bid = blockIdx.x;
-  const uint32_t logical = (G % 8u == 0u) ? (bid % 8u) * (G / 8u) + bid / 8u : bid;
-  const int64_t lane = lane_base + logical / (uint32_t)nb;
-  const int i = nb - 1 - (int)(logical % (uint32_t)nb);
+  const int lanes = (int)(G / (uint32_t)nb);
+  int64_t lane;
+  int i;
+  if (G % 8u == 0u && lanes % 8 == 0) {
+    const uint32_t lx = (uint32_t)lanes / 8u;
+    const uint32_t u = bid / 8u;
+    lane = lane_base + (int64_t)((bid % 8u) * lx + u % lx);
+    i = nb - 1 - (int)(u / lx);
+  } else {
+    lane = lane_base + (int64_t)(bid % (uint32_t)lanes);
+    i = nb - 1 - (int)(bid / (uint32_t)lanes);
+  }
 
   const int64_t lane_off = lane * (int64_t)S * D;
   const uint16_t* kg = k + lane_off;
