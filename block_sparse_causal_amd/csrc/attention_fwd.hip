@@ -151,10 +151,26 @@ __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOffset));
   return r;
 }
+// 16-byte global load issued through asm, so that the compiler does not wait
+// for it (and with it for every later copy) at each use.  The value may only be
+// used after an s_waitcnt that covers it.
+template <int kOffset>
+__device__ __forceinline__ u32x4 global_load_b128(const uint16_t* p) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(r) : "v"(p), "i"(kOffset) : "memory");
+  return r;
+}
+// 16-byte LDS read, issued through asm for the same reason.
+template <int kOffset>
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOffset));
+  return r;
+}
 // Wait for every outstanding LDS read of this wave; the values pass through the
 // asm statement so that no use of them can be scheduled above the wait.
-template <int N>
-__device__ __forceinline__ void lds_wait_all(u32x2 (&x)[N]) {
+template <typename T, int N>
+__device__ __forceinline__ void lds_wait_all(T (&x)[N]) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
   for (int e = 0; e < N; ++e) asm volatile("" : "+v"(x[e]));
@@ -251,10 +267,23 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   // Q^T operands: lane holds query row qrow, dims 16c + 8h .. +7 for step c.
   const int qrow = i * kBlock + 32 * qh + n;
   const int qrow_c = qrow < S ? qrow : S - 1;
+  // Issued before any copy: the first ring step's wait (at most the second
+  // stage's copies outstanding) covers them.
   u32x4 qop[kStepsD];
-#pragma unroll
-  for (int c = 0; c < kStepsD; ++c)
-    qop[c] = *(const u32x4*)(q + lane_off + (int64_t)qrow_c * D + 16 * c + 8 * h);
+  {
+    const uint16_t* qp = q + lane_off + (int64_t)qrow_c * D + 8 * h;
+    static_assert(kStepsD == 4 || kStepsD == 8, "head dim");
+    qop[0] = global_load_b128<0>(qp);
+    qop[1] = global_load_b128<32>(qp);
+    qop[2] = global_load_b128<64>(qp);
+    qop[3] = global_load_b128<96>(qp);
+    if constexpr (kStepsD == 8) {
+      qop[4] = global_load_b128<128>(qp);
+      qop[5] = global_load_b128<160>(qp);
+      qop[6] = global_load_b128<192>(qp);
+      qop[7] = global_load_b128<224>(qp);
+    }
+  }
 
   // Per-lane byte offset, inside a block's rows, of the 16 bytes each fill op
   // moves.  Op o of wave w fills the 1 KB piece (o * kWaves + w) of [K | V].
@@ -328,16 +357,36 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   float m_use = -__builtin_inff();  // exponent offset in use (log2 units)
   float l_run = 0.0f;               // this lane's share of the denominator
 
-  auto compute = [&](int j, const uint8_t* stage) {
+  // LDS byte addresses (stage 0) of this lane's K and V operand reads; stage t
+  // adds t * 2 * kTileBytes through the instructions' offset field.
+  const uint32_t ring_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)&stages[0][0];
+  uint32_t k_addr[kStepsD];
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c)
+    k_addr[c] = ring_base + (uint32_t)k_chunk_offset<D>(32 * kh + n, 2 * c + h);
+  uint32_t v_addr[kTilesD];
+  {
+    const int r0 = 32 * kh + 8 * (g >> 1) + (gi >> 2);  // key row for chunk 2kh, first read
+    const uint32_t lane_addr = ring_base + (uint32_t)(kTileBytes + r0 * kRowBytes + 8 * (gi & 1));
+    const int sw = v_swizzle<D>(r0);  // rows r0 + 4t + 16gg share r0's swizzle (same r & 3)
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt) {
+      const int dchunk = 4 * dt + 2 * (g & 1) + ((gi & 3) >> 1);
+      v_addr[dt] = lane_addr + 16u * (uint32_t)(dchunk ^ sw);
+    }
+  }
+
+  auto compute = [&](int j, auto T_c) {
+    constexpr int kStageOff = decltype(T_c)::value * 2 * kTileBytes;
     // On the diagonal block the key half above the query half is fully masked.
     if (j == i && kh > qh) return;
-    const uint8_t* ks = stage;
-    const uint8_t* vs = stage + kTileBytes;
     // S^T (32 keys of this half x 32 queries) = K . Q^T.
+    // K operands through asm reads: a plain LDS load here would make the
+    // compiler wait for the next block's in-flight copy into the other stage.
     u32x4 ka[kStepsD];
 #pragma unroll
-    for (int c = 0; c < kStepsD; ++c)
-      ka[c] = *(const u32x4*)(ks + k_chunk_offset<D>(32 * kh + n, 2 * c + h));
+    for (int c = 0; c < kStepsD; ++c) ka[c] = lds_read_b128<kStageOff>(k_addr[c]);
+    lds_wait_all(ka);
     f32x16 s = f32x16{};
 #pragma unroll
     for (int c = 0; c < kStepsD; ++c) s = E::mfma(ka[c], qop[c], s);
@@ -366,21 +415,12 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     // keys kb .. kb+3 of head dim 32dt + 16(g&1) + gi.  They are issued now and
     // land while the softmax runs.
     u32x2 va[kTilesD * 4];
-    {
-      const uint32_t vbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)vs;
-      // byte offset of (key row r, head dim d0) for this lane, with the row swizzle
-      const int r0 = 32 * kh + 8 * (g >> 1) + (gi >> 2);  // key row for chunk 2kh, first read
-      const uint32_t lane_addr = vbase + (uint32_t)(r0 * kRowBytes + 8 * (gi & 1));
-      const int sw = v_swizzle<D>(r0);  // rows r0 + 4t + 16gg share r0's swizzle (same r & 3)
 #pragma unroll
-      for (int dt = 0; dt < kTilesD; ++dt) {
-        const int dchunk = 4 * dt + 2 * (g & 1) + ((gi & 3) >> 1);
-        const uint32_t a = lane_addr + 16u * (uint32_t)(dchunk ^ sw);
-        va[dt * 4 + 0] = lds_read_tr16<0>(a);
-        va[dt * 4 + 1] = lds_read_tr16<4 * kRowBytes>(a);
-        va[dt * 4 + 2] = lds_read_tr16<16 * kRowBytes>(a);
-        va[dt * 4 + 3] = lds_read_tr16<20 * kRowBytes>(a);
-      }
+    for (int dt = 0; dt < kTilesD; ++dt) {
+      va[dt * 4 + 0] = lds_read_tr16<kStageOff>(v_addr[dt]);
+      va[dt * 4 + 1] = lds_read_tr16<kStageOff + 4 * kRowBytes>(v_addr[dt]);
+      va[dt * 4 + 2] = lds_read_tr16<kStageOff + 16 * kRowBytes>(v_addr[dt]);
+      va[dt * 4 + 3] = lds_read_tr16<kStageOff + 20 * kRowBytes>(v_addr[dt]);
     }
     u32x4 pb[2];
 #pragma unroll
@@ -419,27 +459,29 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     bool pre = blk[1] >= 0;  // stage 1 already queued: first step waits for stage 0 only
     int last = pre ? blk[1] : blk[0];
     bool done = false;
-    while (!done) {
+    auto step = [&](auto T_c) {
+      constexpr int t = decltype(T_c)::value;
+      constexpr int refill = (t + 1) % kStages;
+      if (pre)
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(kFillOps));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      ring_barrier();
 #pragma unroll
-      for (int t = 0; t < kStages; ++t) {
-        if (!done) {
-          if (pre)
-            __builtin_amdgcn_s_waitcnt(vmcnt_wait(kFillOps));
-          else
-            __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-          ring_barrier();
-          const int refill = (t + 1) % kStages;
-          if (!pre) {
-            const int jn = last >= 0 ? next_block(last) : -1;
-            blk[refill] = jn;
-            last = jn;
-            if (jn >= 0) fill(jn, stages[refill]);
-          }
-          pre = false;
-          compute(blk[t], stages[t]);
-          done = blk[refill] < 0;
-        }
+      for (int c = 0; c < kStepsD; ++c) asm volatile("" : "+v"(qop[c]));  // loaded (waited above)
+      if (!pre) {
+        const int jn = last >= 0 ? next_block(last) : -1;
+        blk[refill] = jn;
+        last = jn;
+        if (jn >= 0) fill(jn, stages[refill]);
       }
+      pre = false;
+      compute(blk[t], T_c);
+      done = blk[refill] < 0;
+    };
+    while (!done) {
+      step(std::integral_constant<int, 0>{});
+      if (!done) step(std::integral_constant<int, 1>{});
     }
     __syncthreads();  // every wave is done with the stages before they hold the merge
   }
@@ -450,6 +492,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   // hands the other half, unscaled, to its partner together with its (m, l);
   // after one barrier each wave combines and stores its half.  The stage
   // buffers are free here (every wave has passed the last barrier).
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no load of this wave outlives it (empty rows)
   const float l_half = sum_with_other_half(l_run);
   constexpr int kHalfTiles = kTilesD / 2;
   constexpr int kSendStride = kHalfTiles * 16 + 4;  // floats per lane (16-byte aligned, padded)
