@@ -146,18 +146,24 @@ def _csr_from_rows(rows: list[list[int]]) -> tuple[np.ndarray, np.ndarray]:
 
 
 def schedule_from_salience(
-    salience: np.ndarray, sink: int, local_radius: int, topk: int
+    salience: np.ndarray, sink: int, local_radius: int, topk: int, per_row: bool = False
 ) -> tuple[np.ndarray, np.ndarray]:
     """CSR rows: sink blocks, local window and top-k blocks, each clipped causally.
 
     PR page, Summary, first and second bullets.  Row i lists, in ascending order,
     every key block j <= i with j < sink, or i - local_radius <= j, or j in the
-    global top-k set.
+    top-k set.  With per_row=False the top-k set is global: the first topk
+    blocks of the whole ranking.  With per_row=True each row takes its own
+    top-k among its causal blocks j <= i under the same ranking, and may
+    overlap the sink and local blocks.  The pages do not settle which of the
+    two readings the kernel used.
     """
     nb = len(salience)
     top = set(top_k_blocks(salience, topk))
     rows = []
     for i in range(nb):
+        if per_row:
+            top = set(j for j in top_k_blocks(np.asarray(salience)[: i + 1], topk))
         rows.append(
             [j for j in range(i + 1) if j < sink or j >= i - local_radius or j in top]
         )
@@ -165,19 +171,21 @@ def schedule_from_salience(
 
 
 def build_schedule(
-    keys, block: int = 64, sink: int = 1, local_radius: int = 1, topk: int = 2
+    keys, block: int = 64, sink: int = 1, local_radius: int = 1, topk: int = 2,
+    per_row: bool = False,
 ) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Topology-derived CSR schedule from one lane of keys [S, D].
 
     Returns (row_ptr int32 [nb+1], col_idx int32 [nnz], salience fp64 [nb]).
-    PR page, Summary, second bullet; salience as in ``elder_rule_salience``.
+    PR page, Summary, second bullet; salience as in ``elder_rule_salience``;
+    per_row as in ``schedule_from_salience``.
     """
     if block <= 0:
         raise ValueError("block must be positive")
     if min(sink, local_radius, topk) < 0:
         raise ValueError("sink, local_radius and topk must be >= 0")
     sal = elder_rule_salience(block_centroids(keys, block))
-    row_ptr, col_idx = schedule_from_salience(sal, sink, local_radius, topk)
+    row_ptr, col_idx = schedule_from_salience(sal, sink, local_radius, topk, per_row)
     return row_ptr, col_idx, sal
 
 
