@@ -75,6 +75,10 @@ def _load():
     lib.tsa_build_schedule.argtypes = [
         vp, i32, i64, i64, i32, i32, i32, i32, vp, vp, i64, vp, vp, sz, ctypes.POINTER(i64), vp
     ]
+    lib.tsa_build_schedule_ex.restype = ctypes.c_int
+    lib.tsa_build_schedule_ex.argtypes = [
+        vp, i32, i64, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, sz, ctypes.POINTER(i64), vp
+    ]
     lib.tsa_dense_causal_schedule.restype = ctypes.c_int
     lib.tsa_dense_causal_schedule.argtypes = [i64, vp, vp, i64, vp]
     lib.tsa_segment_schedule_nnz.restype = i64
@@ -129,12 +133,14 @@ def schedule_max_nnz(nb: int, sink: int, local_radius: int, topk: int) -> int:
 
 
 def build_schedule(keys: torch.Tensor, block: int = BLOCK, sink: int = 1, local_radius: int = 1,
-                   topk: int = 2, return_salience: bool = False):
+                   topk: int = 2, return_salience: bool = False, per_row: bool = False):
     """Topology-derived CSR schedule from the keys of lane (0, 0).
 
     keys: [S, D] or [B, H, S, D] float16/bfloat16 on a GPU.  Returns int32
     (row_ptr [nb+1], col_idx [nnz]) on the keys' device, plus the fp64 salience
     [nb] when ``return_salience``.  Waits for the stream to read back nnz.
+    per_row: each row takes its own top-k among its blocks j <= i instead of
+    one global top-k set (TSA_TOPK_PER_ROW).
     """
     if not isinstance(keys, torch.Tensor):
         raise TypeError("keys must be a torch.Tensor")
@@ -160,9 +166,9 @@ def build_schedule(keys: torch.Tensor, block: int = BLOCK, sink: int = 1, local_
         base = ws.data_ptr()
         aligned = (base + 255) // 256 * 256
         nnz = ctypes.c_int64(0)
-        status = _lib.tsa_build_schedule(
-            _ptr(keys), code, S, D, block, sink, local_radius, topk, _ptr(row_ptr),
-            _ptr(col_idx), cap, _ptr(sal), ctypes.c_void_p(aligned), int(ws_bytes),
+        status = _lib.tsa_build_schedule_ex(
+            _ptr(keys), code, S, D, block, sink, local_radius, topk, 1 if per_row else 0,
+            _ptr(row_ptr), _ptr(col_idx), cap, _ptr(sal), ctypes.c_void_p(aligned), int(ws_bytes),
             ctypes.byref(nnz), _stream(dev),
         )
     _check(status, "build_schedule")
@@ -181,9 +187,10 @@ class ScheduleBuffers:
     """
 
     def __init__(self, S: int, D: int, sink: int, local_radius: int, topk: int, device,
-                 salience: bool = False):
+                 salience: bool = False, per_row: bool = False):
         dev = torch.device(device)
         self.S, self.D, self.sink, self.local_radius, self.topk = S, D, sink, local_radius, topk
+        self.per_row = per_row
         self.nb = -(-S // BLOCK)
         self.capacity = schedule_max_nnz(self.nb, sink, local_radius, topk)
         self.ws_bytes = int(_lib.tsa_build_schedule_workspace_bytes(S, D, BLOCK))
@@ -208,10 +215,11 @@ def build_schedule_into(keys: torch.Tensor, bufs: ScheduleBuffers) -> None:
         raise ValueError("keys must be a contiguous GPU tensor of the buffers' [S, D]")
     code = _dtype_code(keys, "keys")
     with torch.cuda.device(keys.device):
-        status = _lib.tsa_build_schedule(
+        status = _lib.tsa_build_schedule_ex(
             _ptr(keys), code, bufs.S, bufs.D, BLOCK, bufs.sink, bufs.local_radius, bufs.topk,
-            _ptr(bufs.row_ptr), _ptr(bufs.col_idx), bufs.capacity, _ptr(bufs.salience),
-            ctypes.c_void_p(bufs.ws_ptr), bufs.ws_bytes, None, _stream(keys.device),
+            1 if bufs.per_row else 0, _ptr(bufs.row_ptr), _ptr(bufs.col_idx), bufs.capacity,
+            _ptr(bufs.salience), ctypes.c_void_p(bufs.ws_ptr), bufs.ws_bytes, None,
+            _stream(keys.device),
         )
     _check(status, "build_schedule_into")
 

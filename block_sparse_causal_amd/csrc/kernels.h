@@ -21,8 +21,9 @@ struct ScheduleWorkspace {
 constexpr int kLdsDistBlocks = 128;  // distance matrix kept in LDS up to this many blocks
 size_t schedule_workspace_bytes(int64_t nb, int64_t D);
 hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t D, int sink,
-                                 int local_radius, int topk, int32_t* row_ptr, int32_t* col_idx,
-                                 int64_t col_capacity, double* salience, void* workspace,
+                                 int local_radius, int topk, bool per_row, int32_t* row_ptr,
+                                 int32_t* col_idx, int64_t col_capacity, double* salience,
+                                 void* workspace,
                                  hipStream_t stream);
 
 hipError_t launch_dense_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,

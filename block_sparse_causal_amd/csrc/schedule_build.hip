@@ -208,6 +208,70 @@ __device__ __forceinline__ void count_ranks(int n, int* rank, Before before) {
   }
 }
 
+// Per-row top-k rows for the workgroup (brank: rank of each block under
+// (-salience, index), valid when 0 < topk < nb).  Block j enters the top-k set
+// of every row i with j <= i < e_j, where e_j is the topk-th smallest index
+// among the blocks ranked above j (nb when fewer are, 0 when topk is 0): row i
+// has exactly topk blocks ranked above j among its blocks 0..i from row e_j on.
+// Row i lists, ascending: sink blocks [0, min(sink, i+1)), blocks j in
+// [sink, i - r - 1] with i < e_j, local blocks [max(sink, i - r), i].
+// Scratch (LDS): e[nb + 1], cnt[nb + 1], tmp.
+template <int kThreads>
+__device__ void emit_rows_per_row(int nb, int sink, int local_radius, int topk, const int* brank,
+                                  int* e, int* cnt, int* tmp, int32_t* __restrict__ row_ptr,
+                                  int32_t* __restrict__ col_idx, int64_t col_capacity) {
+  const int tid = threadIdx.x;
+  for (int v = tid; v < nb; v += kThreads) {
+    int ev = topk == 0 ? 0 : nb;
+    if (topk > 0 && topk < nb) {
+      const int rv = brank[v];
+      int c = 0;
+      for (int u = 0; u < nb; ++u)
+        if (brank[u] < rv && ++c == topk) {
+          ev = u;
+          break;
+        }
+    }
+    e[v] = ev;
+  }
+  __syncthreads();
+  for (int i = tid; i <= nb; i += kThreads) {
+    int c = 0;
+    if (i < nb) {
+      const int a_n = sink < i + 1 ? sink : i + 1;
+      const int loc_lo = (i - local_radius > sink) ? i - local_radius : sink;
+      const int b_n = loc_lo <= i ? i - loc_lo + 1 : 0;
+      for (int j = sink; j <= i - local_radius - 1; ++j) c += e[j] > i ? 1 : 0;
+      c += a_n + b_n;
+    }
+    cnt[i] = c;
+  }
+  __syncthreads();
+  block_exclusive_scan<kThreads>(cnt, nb + 1, tmp);  // also leaves cnt[nb] = nnz
+  for (int i = tid; i <= nb; i += kThreads) row_ptr[i] = cnt[i];
+  // Entries: one wavefront per row; the middle part is compacted with a ballot.
+  const int lane = tid & 63;
+  for (int i = tid >> 6; i < nb; i += kThreads / 64) {
+    const int a_n = sink < i + 1 ? sink : i + 1;
+    const int loc_lo = (i - local_radius > sink) ? i - local_radius : sink;
+    const int t_hi = i - local_radius - 1;
+    int64_t pos = cnt[i];
+    for (int k = lane; k < a_n; k += 64)
+      if (pos + k < col_capacity) col_idx[pos + k] = k;
+    pos += a_n;
+    for (int j0 = sink; j0 <= t_hi; j0 += 64) {
+      const int j = j0 + lane;
+      const bool take = j <= t_hi && e[j] > i;
+      const uint64_t m = (uint64_t)__ballot(take);
+      const int at = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (take && pos + at < col_capacity) col_idx[pos + at] = j;
+      pos += __popcll(m);
+    }
+    for (int k = lane; loc_lo + k <= i; k += 64)
+      if (pos + k < col_capacity) col_idx[pos + k] = loc_lo + k;
+  }
+}
+
 // Top-k selection and CSR emission from the per-block salience (LDS).
 //   Blocks are ranked by (-salience, index); the first min(topk, nb) form the
 //   global top-k set.  Row i lists, ascending: sink blocks [0, min(sink, i+1)),
@@ -215,9 +279,10 @@ __device__ __forceinline__ void count_ranks(int n, int* rank, Before before) {
 // Scratch (LDS): brank[nb], top[nb + 1], topidx[nb], cnt[nb + 1], tmp.
 template <int kThreads>
 __device__ void select_and_emit(const double* sal, int nb, int sink, int local_radius, int topk,
-                                int* brank, int* top, int* topidx, int* cnt, int* tmp,
-                                int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
-                                int64_t col_capacity, double* __restrict__ salience) {
+                                bool per_row, int* brank, int* top, int* topidx, int* cnt,
+                                int* tmp, int32_t* __restrict__ row_ptr,
+                                int32_t* __restrict__ col_idx, int64_t col_capacity,
+                                double* __restrict__ salience) {
   const int tid = threadIdx.x;
   const int kk = topk < nb ? topk : nb;
   for (int v = tid; v < nb; v += kThreads) brank[v] = 0;
@@ -228,9 +293,14 @@ __device__ void select_and_emit(const double* sal, int nb, int sink, int local_r
       return su > sv || (su == sv && u < v);
     });
   __syncthreads();
-  for (int v = tid; v <= nb; v += kThreads) top[v] = (v < nb && brank[v] < kk) ? 1 : 0;
   if (salience != nullptr)
     for (int v = tid; v < nb; v += kThreads) salience[v] = sal[v];
+  if (per_row) {
+    emit_rows_per_row<kThreads>(nb, sink, local_radius, topk, brank, top, cnt, tmp, row_ptr,
+                                col_idx, col_capacity);
+    return;
+  }
+  for (int v = tid; v <= nb; v += kThreads) top[v] = (v < nb && brank[v] < kk) ? 1 : 0;
   __syncthreads();
   block_exclusive_scan<kThreads>(top, nb + 1, tmp);  // top[x] = selected blocks below x
   for (int v = tid; v < nb; v += kThreads)
@@ -419,6 +489,84 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Per-row top-k rows by one wavefront (nb <= 64 * SLOTS <= 128), from the exact
+// ranking keys of select_and_emit_wave (larger key = ranked higher).  Block j
+// enters the top-k set of every row i with j <= i < e_j, where e_j is the
+// topk-th smallest index among the blocks ranked above j (nb when fewer are, 0
+// when topk is 0).  Row i lists, ascending: sink blocks [0, min(sink, i+1)),
+// blocks j in [sink, i - r - 1] with i < e_j, local blocks [max(sink, i - r), i].
+template <int SLOTS>
+__device__ __forceinline__ void emit_rows_per_row_wave(const int (&key)[SLOTS], int nb, int sink,
+                                                       int local_radius, int topk,
+                                                       int32_t* __restrict__ row_ptr,
+                                                       int32_t* __restrict__ col_idx,
+                                                       int64_t col_capacity) {
+  const int lane = threadIdx.x & 63;
+  int e[SLOTS], seen[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    e[s] = topk == 0 ? 0 : nb;
+    seen[s] = 0;
+  }
+  if (topk > 0 && topk < nb) {
+    for (int u = 0; u < nb; ++u) {
+      const int ku = block_value<SLOTS>(key, u);
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const bool above = ku > key[s];
+        seen[s] += above ? 1 : 0;
+        e[s] = (above && seen[s] == topk) ? u : e[s];
+      }
+    }
+  }
+  // Middle-part sizes: blocks j in [sink, i - r - 1] with i < e_j.
+  int mid[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) mid[s] = 0;
+  for (int j = sink; j < nb; ++j) {
+    const int ej = block_value<SLOTS>(e, j);
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const int i = lane + 64 * s;
+      mid[s] += (j <= i - local_radius - 1 && i < ej) ? 1 : 0;
+    }
+  }
+  int carry = 0;
+  int64_t start[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int i = lane + 64 * s;
+    const int a_n = sink < i + 1 ? sink : i + 1;
+    const int loc_lo = (i - local_radius > sink) ? i - local_radius : sink;
+    const int b_n = loc_lo <= i ? i - loc_lo + 1 : 0;
+    const int n = i < nb ? a_n + mid[s] + b_n : 0;
+    const int incl = wave_inclusive_scan(n);
+    start[s] = carry + incl - n;
+    carry += read_lane(incl, 63);
+    if (i < nb) {
+      row_ptr[i] = (int32_t)start[s];
+      for (int j = 0; j < a_n; ++j)
+        if (start[s] + j < col_capacity) col_idx[start[s] + j] = j;
+      int64_t pos = start[s] + a_n + mid[s];
+      for (int j = loc_lo; j <= i; ++j, ++pos)
+        if (pos < col_capacity) col_idx[pos] = j;
+      start[s] += a_n;  // next free entry of the middle part
+    }
+  }
+  for (int j = sink; j < nb; ++j) {
+    const int ej = block_value<SLOTS>(e, j);
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const int i = lane + 64 * s;
+      if (i < nb && j <= i - local_radius - 1 && i < ej) {
+        if (start[s] < col_capacity) col_idx[start[s]] = j;
+        ++start[s];
+      }
+    }
+  }
+  if (lane == 0) row_ptr[nb] = carry;
+}
+
 // Top-k selection and CSR emission by one wavefront (nb <= 64 * SLOTS <= 128),
 // rows as in select_and_emit.  Row i = lane + 64 * slot writes its own entries.
 // dead: per block, the rank of the edge (in sd, ascending lengths) at which it
@@ -434,7 +582,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int SLOTS>
 __device__ __forceinline__ void select_and_emit_wave(const int (&dead)[SLOTS], const double* sd,
                                                      int ne, int nb, int sink, int local_radius,
-                                                     int topk, int* grp,
+                                                     int topk, bool per_row, int* grp,
                                                      int32_t* __restrict__ row_ptr,
                                                      int32_t* __restrict__ col_idx,
                                                      int64_t col_capacity,
@@ -460,6 +608,11 @@ __device__ __forceinline__ void select_and_emit_wave(const int (&dead)[SLOTS], c
     const int g = dead[s] >= 0 ? grp[dead[s]] : zero_grp;
     key[s] = v < nb ? ((g + 1) << 8) | (255 - v) : 0;
     if (salience != nullptr && v < nb) salience[v] = dead[s] >= 0 ? sd[dead[s]] : 0.0;
+  }
+  if (per_row) {
+    emit_rows_per_row_wave<SLOTS>(key, nb, sink, local_radius, topk, row_ptr, col_idx,
+                                  col_capacity);
+    return;
   }
   // Top-k set as one bit mask per slot: the k-th largest key, bit by bit.
   uint64_t topm[SLOTS];
@@ -544,7 +697,7 @@ __host__ __device__ constexpr int small_stage_offset(int nb) { return (nb * nb +
 // matrix) + kStageBytes (SmallState).
 template <int SLOTS>
 __device__ __forceinline__ void small_topology(
-    double* smem, const double* dist_g, int nb, int sink, int local_radius, int topk,
+    double* smem, const double* dist_g, int nb, int sink, int local_radius, int topk, bool per_row,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_capacity,
     double* __restrict__ salience) {
   double* dist = smem;
@@ -731,7 +884,8 @@ __device__ __forceinline__ void small_topology(
   // ---- Elder rule, top-k and CSR rows.
   int dead[SLOTS];
   elder_ranks<SLOTS>(A.sort_t, ne, dead);
-  select_and_emit_wave<SLOTS>(dead, A.sort_d, ne, nb, sink, local_radius, topk, A.rank, row_ptr,
+  select_and_emit_wave<SLOTS>(dead, A.sort_d, ne, nb, sink, local_radius, topk, per_row, A.rank,
+                              row_ptr,
                               col_idx, col_capacity, salience);
 }
 
@@ -776,7 +930,7 @@ template <int SLOTS, int TILE, bool BF16>
 __global__ __launch_bounds__(kSmallThreads) void schedule_small(
     const uint16_t* __restrict__ keys, int64_t S, int64_t D, int nb,
     double* dist_g, unsigned long long* flags, unsigned long long token, int sink,
-    int local_radius, int topk, int32_t* __restrict__ row_ptr,
+    int local_radius, int topk, int per_row, int32_t* __restrict__ row_ptr,
     int32_t* __restrict__ col_idx, int64_t col_capacity,
     double* __restrict__ salience) {
   static_assert(TILE == 2 || TILE == 4 || TILE == 8, "tile edge");
@@ -905,8 +1059,8 @@ __global__ __launch_bounds__(kSmallThreads) void schedule_small(
   }
   __syncthreads();
   if (!elected) return;
-  small_topology<SLOTS>(smem, dist_g, nb, sink, local_radius, topk, row_ptr, col_idx, col_capacity,
-                        salience);
+  small_topology<SLOTS>(smem, dist_g, nb, sink, local_radius, topk, per_row != 0, row_ptr, col_idx,
+                        col_capacity, salience);
 }
 
 // ------------------------------------------------------------------ larger schedules
@@ -1078,7 +1232,7 @@ __global__ __launch_bounds__(kLargeThreads) void boruvka_merge(int nb, int* __re
 //   R4 int[nb+1]   edge ranks     -> component sizes -> block ranks
 __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
     int nb, const int* __restrict__ state, const double* __restrict__ edge_d_g,
-    const uint32_t* __restrict__ edge_t_g, int sink, int local_radius, int topk,
+    const uint32_t* __restrict__ edge_t_g, int sink, int local_radius, int topk, int per_row,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_capacity,
     double* __restrict__ salience) {
   extern __shared__ __attribute__((aligned(16))) double lds_f64[];
@@ -1161,7 +1315,8 @@ __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
   }
   __syncthreads();
 
-  select_and_emit<kLargeThreads>(sal, nb, sink, local_radius, topk, R4, R1, R3, (int*)R2, tmp,
+  select_and_emit<kLargeThreads>(sal, nb, sink, local_radius, topk, per_row != 0, R4, R1, R3,
+                                 (int*)R2, tmp,
                                  row_ptr, col_idx, col_capacity, salience);
 }
 
@@ -1246,8 +1401,9 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 size_t schedule_workspace_bytes(int64_t nb, int64_t D) { return workspace_layout(nb, D).total; }
 
 hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t D, int sink,
-                                 int local_radius, int topk, int32_t* row_ptr, int32_t* col_idx,
-                                 int64_t col_capacity, double* salience, void* workspace,
+                                 int local_radius, int topk, bool per_row, int32_t* row_ptr,
+                                 int32_t* col_idx, int64_t col_capacity, double* salience,
+                                 void* workspace,
                                  hipStream_t stream) {
   const int64_t nb64 = (S + kBlock - 1) / kBlock;
   if (nb64 == 0) return launch_dense_schedule(0, row_ptr, col_idx, stream);
@@ -1266,8 +1422,8 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
       hipError_t e = allow_lds(kernel, lds);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kernel, grid, dim3(kSmallThreads), lds, stream, (const uint16_t*)keys, S,
-                         D, nb, dist, flags, token, sink, local_radius, topk, row_ptr, col_idx,
-                         col_capacity, salience);
+                         D, nb, dist, flags, token, sink, local_radius, topk, (int)per_row,
+                         row_ptr, col_idx, col_capacity, salience);
       return hipGetLastError();
     };
     if (bf16) {
@@ -1310,8 +1466,8 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
   const size_t finish_lds = 2 * (size_t)nb * sizeof(double) + 3 * n1 * sizeof(int);
   if ((err = allow_lds(finish_kernel, finish_lds)) != hipSuccess) return err;
   hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kLargeThreads), finish_lds, stream, nb, state,
-                     edge_d, edge_t, sink, local_radius, topk, row_ptr, col_idx, col_capacity,
-                     salience);
+                     edge_d, edge_t, sink, local_radius, topk, (int)per_row, row_ptr, col_idx,
+                     col_capacity, salience);
   return hipGetLastError();
 }
 

@@ -88,6 +88,20 @@ int tsa_build_schedule(const void* keys, int32_t dtype, int64_t S, int64_t D, in
                        int32_t sink, int32_t local_radius, int32_t topk, int32_t* row_ptr,
                        int32_t* col_idx, int64_t col_capacity, double* salience, void* workspace,
                        size_t workspace_bytes, int64_t* nnz_host, void* stream) {
+  return tsa_build_schedule_ex(keys, dtype, S, D, block, sink, local_radius, topk, TSA_TOPK_GLOBAL,
+                               row_ptr, col_idx, col_capacity, salience, workspace, workspace_bytes,
+                               nnz_host, stream);
+}
+
+int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
+                          int32_t sink, int32_t local_radius, int32_t topk, int32_t topk_scope,
+                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                          double* salience, void* workspace, size_t workspace_bytes,
+                          int64_t* nnz_host, void* stream) {
+  if (topk_scope != TSA_TOPK_GLOBAL && topk_scope != TSA_TOPK_PER_ROW)
+    return fail(TSA_ERR_INVALID_ARG,
+                "tsa_build_schedule: topk_scope must be TSA_TOPK_GLOBAL or TSA_TOPK_PER_ROW, got %d",
+                topk_scope);
   if (dtype != TSA_F16 && dtype != TSA_BF16)
     return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: dtype must be TSA_F16 or TSA_BF16");
   if (S < 0 || D <= 0)
@@ -135,6 +149,7 @@ int tsa_build_schedule(const void* keys, int32_t dtype, int64_t S, int64_t D, in
   }
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = tsa::launch_build_schedule(keys, dtype == TSA_BF16, S, D, sink, local_radius, topk,
+                                            topk_scope == TSA_TOPK_PER_ROW,
                                             row_ptr, col_idx, col_capacity, salience, workspace, st);
   if (e != hipSuccess) return hip_fail(e, "schedule kernels");
   if (nnz_host) {

@@ -123,6 +123,29 @@ int tsa_build_schedule(const void* keys, int32_t dtype, int64_t S, int64_t D, in
                        int32_t* col_idx, int64_t col_capacity, double* salience, void* workspace,
                        size_t workspace_bytes, int64_t* nnz_host, void* stream);
 
+/* Scope of the top-k term of a schedule row. */
+#define TSA_TOPK_GLOBAL 0  /* one set: the topk blocks of highest salience */
+#define TSA_TOPK_PER_ROW 1 /* each row: the topk highest among its blocks j <= i */
+
+/*
+ * tsa_build_schedule with a choice of top-k scope.  (PR page, Summary, second
+ * bullet: a top-k selection of salient key blocks; the pages do not settle
+ * whether the selection is one set for all rows or one per row.)
+ *   topk_scope  TSA_TOPK_GLOBAL: exactly tsa_build_schedule.
+ *               TSA_TOPK_PER_ROW: row i takes the min(topk, i+1) blocks of
+ *               highest salience among blocks 0..i (same ranking: salience
+ *               descending, lower index first on ties), besides its sink and
+ *               local blocks; the sets may overlap.  The same capacity bound,
+ *               tsa_schedule_max_nnz, holds.
+ * Every other argument, the workspace contract and the errors are those of
+ * tsa_build_schedule; an unknown topk_scope is TSA_ERR_INVALID_ARG.
+ */
+int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
+                          int32_t sink, int32_t local_radius, int32_t topk, int32_t topk_scope,
+                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                          double* salience, void* workspace, size_t workspace_bytes,
+                          int64_t* nnz_host, void* stream);
+
 /*
  * The dense causal (lower-triangular) CSR for nb blocks: row i lists 0..i.
  * (PR page, Summary: "dense causal CSR layout"; Local benchmark: the dense CSR

@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for required in ("tsa_build_schedule", "tsa_scheduled_attention_fwd", "tsa_dense_causal_schedule",
                      "tsa_segment_schedule", "tsa_segment_schedule_nnz", "tsa_schedule_max_nnz",
+                     "tsa_build_schedule_ex",
                      "tsa_build_schedule_workspace_bytes", "tsa_last_error", "tsa_version"):
         assert required in names
 
@@ -79,6 +80,27 @@ def test_segment_schedule_checks_before_gpu(lib):
     assert b"segment_blocks" in lib.tsa_last_error()
     assert lib.tsa_segment_schedule(64, 8, vp(None), vp(None), 287, vp(None)) == -4  # short col_idx
     assert lib.tsa_segment_schedule(64, 8, vp(None), vp(None), 288, vp(None)) == -1  # NULL outputs
+
+
+def test_build_schedule_ex_rejects_unknown_scope(lib):
+    vp = ctypes.c_void_p
+    f = lib.tsa_build_schedule_ex
+    f.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, ctypes.c_int64, vp, vp,
+                  ctypes.c_size_t, ctypes.POINTER(ctypes.c_int64), vp]
+    assert f(None, 1, 128, 64, 64, 1, 1, 2, 2, None, None, 10, None, None, 0, None, None) == -1
+    assert b"topk_scope" in lib.tsa_last_error()
+
+
+def test_max_nnz_bound_holds_for_per_row_oracle_schedules(lib):
+    import oracle
+
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        nb = int(rng.integers(1, 40))
+        s, r, k = (int(x) for x in rng.integers(0, 6, 3))
+        rp, _, _ = oracle.build_schedule(rng.standard_normal((64 * nb, 4)), 64, s, r, k, per_row=True)
+        assert rp[-1] <= lib.tsa_schedule_max_nnz(nb, s, r, k)
 
 
 def test_max_nnz_rejects_negative(lib):
