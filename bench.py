@@ -220,6 +220,32 @@ def main() -> int:
     d1.record(stream)
     torch.cuda.synchronize()
     sparse_ms = d0.elapsed_time(d1) / reps
+    # The per-row top-k scope of the builder: its build time, and the kernel over
+    # its schedule, timed the same way.
+    per_row = None
+    if not w.dense:
+        pbufs = tsa.ScheduleBuffers(w.S, w.D, w.sink, w.local_radius, w.topk, dev, per_row=True)
+        for _ in range(3):
+            tsa.build_schedule_into(keys, pbufs)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for _ in range(reps):
+            tsa.build_schedule_into(keys, pbufs)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        pr_build_ms = d0.elapsed_time(d1) / reps
+        pr_nnz = int(pbufs.row_ptr[-1].item())
+        for _ in range(3):
+            tsa.scheduled_attention(q, k, v, pbufs.row_ptr, pbufs.col_idx, out=out)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for _ in range(reps):
+            tsa.scheduled_attention(q, k, v, pbufs.row_ptr, pbufs.col_idx, out=out)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        pr_ms = d0.elapsed_time(d1) / reps
+        per_row = {"nnz_blocks": pr_nnz, "builder_ms": round(pr_build_ms, 5), "attention_ms": round(pr_ms, 5),
+                   "attention_tflops": round(lanes * pr_nnz * 4 * 64 * 64 * w.D / (pr_ms * 1e-3) / 1e12, 3)}
     # The fixed-segment CSR (512-token segments) at the same shape, timed the same way.
     seg = None
     if w.S % 512 == 0:
@@ -283,6 +309,7 @@ def main() -> int:
         "ideal_speedup": round(nnz_dense / nnz, 3),
         "dense_csr_tflops": round(lanes * nnz_dense * 4 * 64 * 64 * w.D / (dense_ms * 1e-3) / 1e12, 3),
         "segment_csr": seg,
+        "per_row_topk": per_row,
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tflops, 3),
