@@ -16,6 +16,10 @@ What it computes (all in float64, numpy only):
 * ``attention`` -- dense masked attention: every query row takes a full-width
   softmax over the keys its CSR row allows, with the causal constraint
   (key position <= query position).
+* ``attention_grad`` -- the gradients (dQ, dK, dV) of that attention and its
+  per-row log-sum-exp, by the closed form of the row-softmax chain rule; and
+  ``schedule.transpose_schedule``, the column view of a CSR schedule that the
+  key/value gradients gather over.
 
 Each function names the passage of the pages it follows.  Readings of points the
 pages leave open are listed, with the reason for each, in the repository's
@@ -31,8 +35,10 @@ from .schedule import (
     dense_causal_schedule,
     fixed_segment_schedule,
     csr_to_block_sets,
+    transpose_schedule,
 )
 from .attention import allowed_key_mask, masked_attention, masked_attention_rows
+from .attention_grad import masked_lse, attention_backward, attention_backward_rows
 
 __all__ = [
     "block_centroids",
@@ -44,7 +50,11 @@ __all__ = [
     "dense_causal_schedule",
     "fixed_segment_schedule",
     "csr_to_block_sets",
+    "transpose_schedule",
     "allowed_key_mask",
     "masked_attention",
     "masked_attention_rows",
+    "masked_lse",
+    "attention_backward",
+    "attention_backward_rows",
 ]

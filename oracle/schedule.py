@@ -220,3 +220,18 @@ def csr_to_block_sets(row_ptr, col_idx) -> list[set[int]]:
     rp = np.asarray(row_ptr).astype(np.int64)
     ci = np.asarray(col_idx).astype(np.int64)
     return [set(int(x) for x in ci[rp[i] : rp[i + 1]]) for i in range(len(rp) - 1)]
+
+
+def transpose_schedule(row_ptr, col_idx) -> tuple[np.ndarray, np.ndarray]:
+    """Column view (CSC) of a causal CSR schedule: column j lists, ascending,
+    the query blocks i whose row lists key block j, j <= i.
+
+    The gradients of keys and values (dK, dV) of key block j gather over exactly
+    these query blocks (the backward of the forward on the PR page, Summary,
+    first bullet).  Listed blocks outside 0..i select no keys and do not appear.
+    Returns int32 (col_ptr [nb+1], row_idx [nnz']).
+    """
+    sets = csr_to_block_sets(row_ptr, col_idx)
+    nb = len(sets)
+    cols = [[i for i in range(nb) if j in sets[i] and j <= i] for j in range(nb)]
+    return _csr_from_rows(cols)
