@@ -14,6 +14,13 @@ triton-lang/kernels PR 22, Summary):
 * ``dense_causal_schedule`` the lower-triangular CSR
 * ``segment_schedule``      the fixed-segment (block-diagonal causal) CSR
 * ``scheduled_attention``  forward causal attention over a CSR block schedule
+  (optionally with each row's log-sum-exp)
+
+and, beyond the pages (whose kernel is forward-only), the backward pass:
+
+* ``schedule_transpose``            column view (CSC) of a CSR schedule
+* ``scheduled_attention_backward``  dq, dk, dv over the same schedule
+* ``attention``                     forward with torch autograd support
 """
 from __future__ import annotations
 
@@ -33,6 +40,9 @@ __all__ = [
     "dense_causal_schedule",
     "segment_schedule",
     "scheduled_attention",
+    "schedule_transpose",
+    "scheduled_attention_backward",
+    "attention",
 ]
 
 BLOCK = 64
@@ -88,6 +98,21 @@ def _load():
     lib.tsa_scheduled_attention_fwd.restype = ctypes.c_int
     lib.tsa_scheduled_attention_fwd.argtypes = [
         vp, vp, vp, vp, i32, i64, i64, i64, i64, vp, vp, i64, i32, ctypes.c_float, vp
+    ]
+    lib.tsa_scheduled_attention_fwd_lse.restype = ctypes.c_int
+    lib.tsa_scheduled_attention_fwd_lse.argtypes = [
+        vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, vp, vp, i64, i32, ctypes.c_float, vp
+    ]
+    lib.tsa_schedule_transpose_workspace_bytes.restype = sz
+    lib.tsa_schedule_transpose_workspace_bytes.argtypes = [i64]
+    lib.tsa_schedule_transpose.restype = ctypes.c_int
+    lib.tsa_schedule_transpose.argtypes = [i64, vp, vp, i64, vp, vp, i64, vp, sz, ctypes.POINTER(i64), vp]
+    lib.tsa_scheduled_attention_bwd_workspace_bytes.restype = sz
+    lib.tsa_scheduled_attention_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.tsa_scheduled_attention_bwd.restype = ctypes.c_int
+    lib.tsa_scheduled_attention_bwd.argtypes = [
+        vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, vp, vp, i64, vp, vp, i64, i32, ctypes.c_float,
+        vp, vp, vp, vp, sz, vp,
     ]
     return lib
 
@@ -252,15 +277,7 @@ def segment_schedule(nb: int, segment_blocks: int, device) -> tuple[torch.Tensor
     return row_ptr, col_idx[:nnz]
 
 
-def scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
-                        col_idx: torch.Tensor, block: int = BLOCK, sm_scale: float | None = None,
-                        out: torch.Tensor | None = None) -> torch.Tensor:
-    """Forward scheduled attention; returns a tensor of q's shape and dtype.
-
-    q, k, v: [S, D] or [B, H, S, D], one float16/bfloat16 dtype, contiguous, on
-    one GPU.  row_ptr/col_idx: int32 CSR on the same device, shared by every
-    (b, h) lane.  sm_scale defaults to 1/sqrt(D).
-    """
+def _attention_shape(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
@@ -280,17 +297,43 @@ def scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_p
             raise ValueError(f"{name} must be on a GPU device")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError(f"{name} must be a torch.Tensor")
-        if t.dtype != torch.int32:
-            raise TypeError(f"{name} must be int32, got {t.dtype}")
-        if t.dim() != 1 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous 1-D tensor")
-        if t.device != q.device:
-            raise ValueError(f"{name} is on {t.device}, q is on {q.device}")
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k, v must be on one device")
+    return code, B, H, S, D
+
+
+def _check_index(name, t, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    if t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 1-D tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _scale_arg(sm_scale):
+    scale = 0.0 if sm_scale is None else float(sm_scale)
+    if sm_scale is not None and scale <= 0:
+        raise ValueError("sm_scale must be positive")
+    return scale
+
+
+def scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                        col_idx: torch.Tensor, block: int = BLOCK, sm_scale: float | None = None,
+                        out: torch.Tensor | None = None, return_lse: bool = False):
+    """Forward scheduled attention; returns a tensor of q's shape and dtype, or
+    (out, lse) with ``return_lse`` (lse float32 [..., S], natural log of each
+    row's softmax denominator, -inf for rows with no allowed key).
+
+    q, k, v: [S, D] or [B, H, S, D], one float16/bfloat16 dtype, contiguous, on
+    one GPU.  row_ptr/col_idx: int32 CSR on the same device, shared by every
+    (b, h) lane.  sm_scale defaults to 1/sqrt(D).
+    """
+    code, B, H, S, D = _attention_shape(q, k, v)
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        _check_index(name, t, q.device)
     nb = -(-S // BLOCK)
     if row_ptr.numel() != nb + 1:
         raise ValueError(f"row_ptr must have nb+1 = {nb + 1} entries for S={S}, got {row_ptr.numel()}")
@@ -298,13 +341,109 @@ def scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_p
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
-    scale = 0.0 if sm_scale is None else float(sm_scale)
-    if sm_scale is not None and scale <= 0:
-        raise ValueError("sm_scale must be positive")
+    scale = _scale_arg(sm_scale)
     with torch.cuda.device(q.device):
-        status = _lib.tsa_scheduled_attention_fwd(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(out), code, B, H, S, D, _ptr(row_ptr), _ptr(col_idx),
-            col_idx.numel(), block, scale, _stream(q.device),
-        )
+        if return_lse:
+            lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+            status = _lib.tsa_scheduled_attention_fwd_lse(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), code, B, H, S, D, _ptr(row_ptr),
+                _ptr(col_idx), col_idx.numel(), block, scale, _stream(q.device),
+            )
+        else:
+            status = _lib.tsa_scheduled_attention_fwd(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(out), code, B, H, S, D, _ptr(row_ptr), _ptr(col_idx),
+                col_idx.numel(), block, scale, _stream(q.device),
+            )
     _check(status, "scheduled_attention")
-    return out
+    return (out, lse) if return_lse else out
+
+
+def schedule_transpose(row_ptr: torch.Tensor, col_idx: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """Column view (CSC) of a causal CSR schedule, built on the GPU: column j
+    lists, ascending, the query blocks whose rows list key block j.  Returns
+    int32 (col_ptr [nb+1], row_idx [nnz']); waits for the stream to read nnz'."""
+    dev = row_ptr.device
+    _check_index("row_ptr", row_ptr, dev)
+    _check_index("col_idx", col_idx, dev)
+    if not row_ptr.is_cuda:
+        raise ValueError("row_ptr must be on a GPU device")
+    nb = row_ptr.numel() - 1
+    if nb < 0:
+        raise ValueError("row_ptr must have at least one entry")
+    nnz = col_idx.numel()
+    cap = min(nnz, nb * (nb + 1) // 2)
+    ws_bytes = int(_lib.tsa_schedule_transpose_workspace_bytes(nb))
+    with torch.cuda.device(dev):
+        col_ptr = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+        row_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+        aligned = (ws.data_ptr() + 255) // 256 * 256
+        total = ctypes.c_int64(0)
+        status = _lib.tsa_schedule_transpose(
+            nb, _ptr(row_ptr), _ptr(col_idx), nnz, _ptr(col_ptr), _ptr(row_idx), cap,
+            ctypes.c_void_p(aligned if ws_bytes else None), ws_bytes, ctypes.byref(total), _stream(dev),
+        )
+    _check(status, "schedule_transpose")
+    return col_ptr, row_idx[: total.value]
+
+
+def scheduled_attention_backward(q, k, v, out, dout, lse, row_ptr, col_idx, col_ptr, row_idx,
+                                 block: int = BLOCK, sm_scale: float | None = None):
+    """Gradients (dq, dk, dv) of ``scheduled_attention`` for the upstream gradient
+    ``dout``; ``out`` and ``lse`` are the forward's (``return_lse=True``) and
+    (col_ptr, row_idx) is ``schedule_transpose(row_ptr, col_idx)``.  Returns
+    tensors of q's shape and dtype."""
+    code, B, H, S, D = _attention_shape(q, k, v)
+    for name, t in (("out", out), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a tensor of q's shape and dtype")
+        if t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on q's device")
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or lse.shape != q.shape[:-1]:
+        raise ValueError("lse must be a float32 tensor of q's shape without the head dim")
+    if lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous on q's device")
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx), ("col_ptr", col_ptr), ("row_idx", row_idx)):
+        _check_index(name, t, q.device)
+    nb = -(-S // BLOCK)
+    if row_ptr.numel() != nb + 1 or col_ptr.numel() != nb + 1:
+        raise ValueError(f"row_ptr and col_ptr must have nb+1 = {nb + 1} entries for S={S}")
+    scale = _scale_arg(sm_scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws_bytes = int(_lib.tsa_scheduled_attention_bwd_workspace_bytes(B, H, S))
+    with torch.cuda.device(q.device):
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        status = _lib.tsa_scheduled_attention_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), code, B, H, S, D,
+            _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _ptr(col_ptr), _ptr(row_idx),
+            row_idx.numel(), block, scale, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws_bytes,
+            _stream(q.device),
+        )
+    _check(status, "scheduled_attention_backward")
+    return dq, dk, dv
+
+
+class _ScheduledAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, row_ptr, col_idx, col_ptr, row_idx, sm_scale):
+        out, lse = scheduled_attention(q, k, v, row_ptr, col_idx, sm_scale=sm_scale, return_lse=True)
+        ctx.save_for_backward(q, k, v, out, lse, row_ptr, col_idx, col_ptr, row_idx)
+        ctx.sm_scale = sm_scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse, row_ptr, col_idx, col_ptr, row_idx = ctx.saved_tensors
+        dq, dk, dv = scheduled_attention_backward(q, k, v, out, dout.contiguous(), lse, row_ptr, col_idx,
+                                                  col_ptr, row_idx, sm_scale=ctx.sm_scale)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def attention(q, k, v, row_ptr, col_idx, col_ptr=None, row_idx=None, sm_scale: float | None = None):
+    """Scheduled attention that torch autograd can differentiate: the forward
+    keeps lse, the backward runs ``scheduled_attention_backward``.  Pass the
+    schedule's column view (``schedule_transpose``) to reuse it across calls;
+    otherwise it is built here."""
+    if col_ptr is None or row_idx is None:
+        col_ptr, row_idx = schedule_transpose(row_ptr, col_idx)
+    return _ScheduledAttention.apply(q, k, v, row_ptr, col_idx, col_ptr, row_idx, sm_scale)

@@ -1,0 +1,640 @@
+// Scheduled block-sparse causal attention backward for gfx950 (CDNA4).
+//
+// The pages' kernel is forward-only ("Add topology-derived sparse attention
+// kernel", triton-lang/kernels PR 22, Summary, first bullet; the mirror page's
+// note on learned segment boundaries records that without a backward, training
+// would run dense).  These kernels differentiate that forward over the same CSR
+// schedule.  With P_tu = exp(z_tu - lse_t) on the allowed keys of query row t:
+//   dV = P^T dO,  dP = dO V^T,  Delta_t = dO_t . O_t,  dS = P * (dP - Delta),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// Two kernels, no atomics, every output element written once:
+//   dq kernel   - one workgroup per (lane, query block i), walking CSR row i:
+//                 recomputes S^T and P^T, forms dP^T = V . dO^T and dS^T, and
+//                 accumulates dQ^T += K^T . dS^T.  It also writes the per-row
+//                 statistics (lse in log2 units, Delta) the second kernel reads.
+//   dkdv kernel - one workgroup per (lane, key block j), walking column j of the
+//                 transposed schedule (the query blocks whose rows list j):
+//                 recomputes S = Q . K^T and P, dP = dO . V^T and dS, and
+//                 accumulates dV^T += dO^T . P and dK^T += Q^T . dS.
+//
+// Both kernels mirror the forward's layout (4 waves = 2 row halves x 2 column
+// halves, v_mfma_f32_32x32x16, a two-stage ring of direct global->LDS copies).
+// The streamed operand is always read twice from LDS: row-wise as the A operand
+// of the score-shaped product (its rows permuted by swapping bits 2 and 3, so
+// that the result registers are already the B operand of the next product) and
+// with transposing reads (ds_read_b64_tr_b16) as the A operand of the gradient
+// product.  The stationary operand (Q and dO rows in the dq kernel, K and V
+// rows in the dkdv kernel) stays in registers as B operands.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "kernels.h"
+#include "mfma_tile.h"
+
+namespace tsa {
+namespace {
+
+using namespace tile;
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kWaves = kThreads / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct Geo {
+  static constexpr int kStepsD = D / 16;          // 16-deep steps over the head dims
+  static constexpr int kTilesD = D / 32;          // 32-row tiles of a [D x 32] accumulator
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kBlock * kRowBytes;
+  static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kTileOps = 2 * kTileBytes / 1024 / kWaves;  // 1 KB copy ops per wave, two tiles
+};
+
+// LDS row r of every tile holds block row (r & 32) | swap_bits23(r & 31) and the
+// 16-byte chunk c of that row sits at chunk c ^ (r & 7).  fill_offsets gives,
+// for each 1 KB copy op of wave w, the byte offset in the block's rows of the
+// 16 bytes lane l moves (op o fills LDS piece o * kWaves + w of [tile A | tile B]).
+template <int D>
+__device__ __forceinline__ void fill_offsets(uint32_t (&off)[Geo<D>::kTileOps], int w, int l) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int op = 0; op < G::kTileOps; ++op) {
+    const int chunk = (op * kWaves + w) * 64 + l;
+    const int cc = chunk % (kBlock * G::kChunksPerRow);
+    const int r = cc / G::kChunksPerRow, pc = cc % G::kChunksPerRow;
+    const int row = (r & 32) | swap_bits23(r & 31);
+    off[op] = (uint32_t)(row * G::kRowBytes + 16 * (pc ^ (r & 7)));
+  }
+}
+
+// LDS address (tile base + offsets) of this lane's row-wise A-operand read for
+// step c: MFMA row n of half `half` (block row half*32 + pi(n)), dims 16c+8h..+7.
+template <int D>
+__device__ __forceinline__ uint32_t row_read_addr(uint32_t base, int half, int n, int h, int c) {
+  return base + (uint32_t)k_chunk_offset<D>(32 * half + n, 2 * c + h);
+}
+
+// LDS address of this lane's transposing read for head-dim tile dt: within each
+// 16-lane group, lane gi supplies the 8-byte piece (dims 4 (gi & 3) .. +3 of the
+// group's 16 dims) of row r0 = 32 half + 4 h + gi / 4, which holds block row
+// 32 half + 8 h + gi / 4; adding 8 rows gives block rows +4, adding 16 gives +16.
+template <int D>
+__device__ __forceinline__ uint32_t tr_read_addr(uint32_t base, int half, int g, int gi, int dt) {
+  const int r0 = 32 * half + 4 * (g >> 1) + (gi >> 2);
+  const int dchunk = 4 * dt + 2 * (g & 1) + ((gi & 3) >> 1);
+  return base + (uint32_t)(r0 * Geo<D>::kRowBytes + 16 * (dchunk ^ (r0 & 7)) + 8 * (gi & 1));
+}
+
+// Issue the four transposing reads of one head-dim tile: block rows 16 gg + 8 h +
+// 4 e + 0..3 of the lane's half for (gg, e) = (0,0), (0,1), (1,0), (1,1).
+template <int kOff, int kRowBytes>
+__device__ __forceinline__ void tr_reads(u32x2* dst, uint32_t addr) {
+  dst[0] = lds_read_tr16<kOff>(addr);
+  dst[1] = lds_read_tr16<kOff + 8 * kRowBytes>(addr);
+  dst[2] = lds_read_tr16<kOff + 16 * kRowBytes>(addr);
+  dst[3] = lds_read_tr16<kOff + 24 * kRowBytes>(addr);
+}
+// A operand of k-step gg from the reads of one tile.
+__device__ __forceinline__ u32x4 tr_operand(const u32x2* t, int gg) {
+  const u32x2 lo = t[2 * gg], hi = t[2 * gg + 1];
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Maps workgroup b to (lane, position): workgroup b runs on XCD b % 8, which takes
+// a contiguous group of lanes (its L2 then holds their operands) and runs their
+// positions 0, 1, ... in turn.
+__device__ __forceinline__ void grid_position(int nb, int64_t lane_base, int64_t& lane, int& pos) {
+  const uint32_t G = gridDim.x, bid = blockIdx.x;
+  const int lanes = (int)(G / (uint32_t)nb);
+  if (G % 8u == 0u && lanes % 8 == 0) {
+    const uint32_t lx = (uint32_t)lanes / 8u, u = bid / 8u;
+    lane = lane_base + (int64_t)((bid % 8u) * lx + u % lx);
+    pos = (int)(u / lx);
+  } else {
+    lane = lane_base + (int64_t)(bid % (uint32_t)lanes);
+    pos = (int)(bid / (uint32_t)lanes);
+  }
+}
+
+// Walker over one CSR row (or CSC column) whose accepted entries are strictly
+// ascending and within [lo, hi]: entries are read 64 at a time into one register
+// per lane and handed out with readlane; a reload waits for the memory counter
+// right away so no other read ever waits on it.
+struct ListWalker {
+  int p, end, win, cols, lo, hi;
+  __device__ __forceinline__ void init(const int32_t* ptr, const int32_t* idx, int64_t nnz, int r,
+                                       int lo_, int hi_, int l) {
+    p = (int)min((int64_t)max(ptr[r], 0), nnz);
+    end = (int)max(min((int64_t)ptr[r + 1], nnz), (int64_t)p);
+    lo = lo_;
+    hi = hi_;
+    win = p;
+    cols = (p + l < end) ? idx[p + l] : -1;
+    idx_ = idx;
+    l_ = l;
+  }
+  __device__ __forceinline__ int next(int last) {
+    while (p < end) {
+      if (p - win >= 64) {
+        win = p;
+        cols = (p + l_ < end) ? idx_[p + l_] : -1;
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      }
+      const int c = __builtin_amdgcn_readlane(cols, p - win);
+      ++p;
+      if (c > last && c >= lo && c <= hi) return c;
+    }
+    return -1;
+  }
+  const int32_t* idx_;
+  int l_;
+};
+
+// ----------------------------------------------------------------------------
+// dq kernel
+// ----------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t nnz, int S,
+    int nb, int64_t lane_base, float scale_log2, float scale, float2* __restrict__ stats,
+    uint16_t* __restrict__ dq) {
+  using E = Elem<BF16>;
+  using G = Geo<D>;
+  constexpr int kStepsD = G::kStepsD, kTilesD = G::kTilesD, kTileBytes = G::kTileBytes;
+  constexpr int kStageBytes = 2 * kTileBytes;  // [K tile | V tile]
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qh = w & 1;   // query half
+  const int kh = w >> 1;  // key half of every visited block
+  const int l = tid & 63, h = l >> 5, n = l & 31, g = l >> 4, gi = l & 15;
+
+  int64_t lane;
+  int pos;
+  grid_position(nb, lane_base, lane, pos);
+  const int i = nb - 1 - pos;  // longest rows first
+  const int64_t lane_off = lane * (int64_t)S * D;
+  const uint16_t* kg = k + lane_off;
+  const uint16_t* vg = v + lane_off;
+
+  // Stationary operands of query row qrow: Q^T and dO^T as B operands (dims
+  // 16c + 8h .. +7), the row's lse (log2 units) and Delta = dO . O, whose two
+  // halves of the dims live in the two half-waves.
+  const int qrow = i * kBlock + 32 * qh + n;
+  const int qrow_c = qrow < S ? qrow : S - 1;
+  const int64_t row_off = lane_off + (int64_t)qrow_c * D + 8 * h;
+  u32x4 qop[kStepsD], dop[kStepsD];
+  float delta = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) {
+    qop[c] = *(const u32x4*)(q + row_off + 16 * c);
+    dop[c] = *(const u32x4*)(dout + row_off + 16 * c);
+    const u32x4 oc = *(const u32x4*)(o + row_off + 16 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) delta = E::dot_pair(dop[c][e], oc[e], delta);
+  }
+  delta = sum_with_other_half(delta);
+  float lse2 = lse[lane * (int64_t)S + qrow_c] * kLog2e;
+  if (kh == 0 && qrow < S) stats[lane * (int64_t)S + qrow] = float2{lse2, delta};
+  // Every load above has landed before any copy is queued, so the ring's waits
+  // below count copies only.
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) {
+    asm volatile("" : "+v"(qop[c]));
+    asm volatile("" : "+v"(dop[c]));
+  }
+  asm volatile("" : "+v"(lse2), "+v"(delta));
+
+  uint32_t fill_off[G::kTileOps];
+  fill_offsets<D>(fill_off, w, l);
+  auto fill = [&](int j, uint8_t* stage) {
+    const int rows = S - j * kBlock < kBlock ? S - j * kBlock : kBlock;
+    copy_block_to_lds<G::kTileOps, G::kTileOps / 2, kWaves>(kg + (int64_t)j * kBlock * D,
+                                                           vg + (int64_t)j * kBlock * D,
+                                                           rows * G::kRowBytes, fill_off, stage, w);
+  };
+
+  ListWalker walk;
+  walk.init(row_ptr, col_idx, nnz, i, 0, i, l);
+
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)&ring[0];
+  uint32_t a_addr[kStepsD];
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) a_addr[c] = row_read_addr<D>(base, kh, n, h, c);
+  uint32_t t_addr[kTilesD];
+#pragma unroll
+  for (int dt = 0; dt < kTilesD; ++dt) t_addr[dt] = tr_read_addr<D>(base, kh, g, gi, dt);
+
+  f32x16 acc[kTilesD];
+#pragma unroll
+  for (int dt = 0; dt < kTilesD; ++dt) acc[dt] = f32x16{};
+
+  auto compute = [&](int j, auto T_c) {
+    constexpr int kOff = decltype(T_c)::value * kStageBytes;
+    if (j == i && kh > qh) return;  // keys of this half all after the queries
+    u32x4 ka[kStepsD], va[kStepsD];
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) {
+      ka[c] = lds_read_b128<kOff>(a_addr[c]);
+      va[c] = lds_read_b128<kOff + kTileBytes>(a_addr[c]);
+    }
+    lds_wait_all(ka);
+    lds_wait_all(va);
+    // S^T = K . Q^T and dP^T = V . dO^T: MFMA row m holds key 32kh + pi(m).
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) s = E::mfma(ka[c], qop[c], s);
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) dp = E::mfma(va[c], dop[c], dp);
+    // K^T operands of dQ^T += K^T . dS^T, landing while dS is formed.
+    u32x2 kt[kTilesD * 4];
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt) tr_reads<kOff, G::kRowBytes>(&kt[dt * 4], t_addr[dt]);
+    if (j == i && kh == qh) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kpos = 16 * (r >> 3) + 8 * h + (r & 7);
+        if (kpos > n) s[r] = -__builtin_inff();
+      }
+    }
+    u32x4 pb[2];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 8 * gg + 2 * x;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -lse2));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, -lse2));
+        pb[gg][x] = E::pack(p0 * (dp[r] - delta), p1 * (dp[r + 1] - delta));
+      }
+    lds_wait_all(kt);
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt)
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) acc[dt] = E::mfma(tr_operand(&kt[dt * 4], gg), pb[gg], acc[dt]);
+  };
+
+  // Ring over the row's blocks, as in the forward: wait for the stage's copy,
+  // barrier, queue the next block into the stage computed one step ago, compute.
+  int blk[2];
+  blk[0] = walk.next(-1);
+  blk[1] = blk[0] >= 0 ? walk.next(blk[0]) : -1;
+  if (blk[0] >= 0) {
+    fill(blk[0], ring);
+    if (blk[1] >= 0) fill(blk[1], ring + kStageBytes);
+    bool pre = blk[1] >= 0;
+    int last = pre ? blk[1] : blk[0];
+    bool done = false;
+    auto step = [&](auto T_c) {
+      constexpr int t = decltype(T_c)::value;
+      constexpr int refill = t ^ 1;
+      if (pre)
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(G::kTileOps));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      ring_barrier();
+      if (!pre) {
+        const int jn = last >= 0 ? walk.next(last) : -1;
+        blk[refill] = jn;
+        last = jn;
+        if (jn >= 0) fill(jn, ring + refill * kStageBytes);
+      }
+      pre = false;
+      compute(blk[t], T_c);
+      done = blk[refill] < 0;
+    };
+    while (!done) {
+      step(std::integral_constant<int, 0>{});
+      if (!done) step(std::integral_constant<int, 1>{});
+    }
+    __syncthreads();
+  }
+
+  // Sum the two key halves: wave kh keeps tiles [kh, kh + 1) * kTilesD / 2 and
+  // hands the others to its partner through LDS, then stores scale * sum.
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  constexpr int kHalfTiles = kTilesD / 2;
+  constexpr int kSendStride = kHalfTiles * 16 + 4;
+  static_assert(4 * 64 * kSendStride * 4 <= 2 * kStageBytes, "merge area exceeds the ring");
+  float* const xbase = (float*)&ring[0];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  auto merge = [&](auto KHc) {
+    constexpr int KH = decltype(KHc)::value;
+    float* send = xbase + ((qh * 2 + KH) * 64 + l) * kSendStride;
+#pragma unroll
+    for (int t = 0; t < kHalfTiles; ++t) {
+      constexpr int kSendBase = (1 - KH) * kHalfTiles;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(f32x4*)(send + t * 16 + 4 * g4) = f32x4{acc[kSendBase + t][4 * g4], acc[kSendBase + t][4 * g4 + 1],
+                                                  acc[kSendBase + t][4 * g4 + 2], acc[kSendBase + t][4 * g4 + 3]};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    ring_barrier();
+    const float* recv = xbase + ((qh * 2 + (1 - KH)) * 64 + l) * kSendStride;
+    if (qrow < S) {
+      uint16_t* drow = dq + lane_off + (int64_t)qrow * D;
+#pragma unroll
+      for (int t = 0; t < kHalfTiles; ++t) {
+        constexpr int kKeepBase = KH * kHalfTiles;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const f32x4 y = *(const f32x4*)(recv + t * 16 + 4 * gg);
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (acc[kKeepBase + t][4 * gg + e] + y[e]) * scale;
+          u32x2 val;
+          val[0] = E::pack(x[0], x[1]);
+          val[1] = E::pack(x[2], x[3]);
+          *(u32x2*)(drow + 32 * (kKeepBase + t) + 8 * gg + 4 * h) = val;
+        }
+      }
+    }
+  };
+  if (kh == 0)
+    merge(std::integral_constant<int, 0>{});
+  else
+    merge(std::integral_constant<int, 1>{});
+}
+
+// ----------------------------------------------------------------------------
+// dkdv kernel
+// ----------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float2* __restrict__ stats,
+    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx, int64_t nnz_t, int S,
+    int nb, int64_t lane_base, float scale_log2, float scale, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv) {
+  using E = Elem<BF16>;
+  using G = Geo<D>;
+  constexpr int kStepsD = G::kStepsD, kTilesD = G::kTilesD, kTileBytes = G::kTileBytes;
+  constexpr int kStatBytes = 1024;  // 4 slots of 256 B; slots 0, 1 hold the block's 64 (lse2, Delta)
+  constexpr int kStageBytes = 2 * kTileBytes + kStatBytes;  // [Q tile | dO tile | stats]
+  constexpr int kFillOps = G::kTileOps + 1;
+  // The ring, reused after the loop for the merge of the two query halves.
+  constexpr int kMergeBytes = 4 * 64 * (G::kTilesD * 16 + 4) * 4;
+  constexpr int kRingBytes = 2 * kStageBytes > kMergeBytes ? 2 * kStageBytes : kMergeBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = w & 1;   // key half owned
+  const int qh = w >> 1;  // query half of every visited block
+  const int l = tid & 63, h = l >> 5, n = l & 31, g = l >> 4, gi = l & 15;
+
+  int64_t lane;
+  int j;
+  grid_position(nb, lane_base, lane, j);  // lowest key blocks (longest columns) first
+  const int64_t lane_off = lane * (int64_t)S * D;
+  const uint16_t* qg = q + lane_off;
+  const uint16_t* dog = dout + lane_off;
+  [[maybe_unused]] const float2* sg = stats + lane * (int64_t)S;
+
+  // Stationary operands of key row krow: K^T and V^T as B operands.
+  const int krow = j * kBlock + 32 * kh + n;
+  const int krow_c = krow < S ? krow : S - 1;
+  const int64_t row_off = lane_off + (int64_t)krow_c * D + 8 * h;
+  u32x4 kop[kStepsD], vop[kStepsD];
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) {
+    kop[c] = *(const u32x4*)(k + row_off + 16 * c);
+    vop[c] = *(const u32x4*)(v + row_off + 16 * c);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) {
+    asm volatile("" : "+v"(kop[c]));
+    asm volatile("" : "+v"(vop[c]));
+  }
+
+  uint32_t fill_off[G::kTileOps];
+  fill_offsets<D>(fill_off, w, l);
+  // Queue query block i: Q and dO tiles, and its rows' statistics (wave w copies
+  // the 256 bytes (w & 1) into slot w; rows past S read as zero).
+  auto fill = [&](int i, uint8_t* stage) {
+    const int rows = S - i * kBlock < kBlock ? S - i * kBlock : kBlock;
+    copy_block_to_lds<G::kTileOps, G::kTileOps / 2, kWaves>(qg + (int64_t)i * kBlock * D,
+                                                           dog + (int64_t)i * kBlock * D,
+                                                           rows * G::kRowBytes, fill_off, stage, w);
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(sg + (int64_t)i * kBlock), 0, rows * 8, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(stage + 2 * kTileBytes + 256 * w), 4,
+        (uint32_t)(256 * (w & 1) + 4 * l), 0, 0, 0);
+#endif
+  };
+
+  ListWalker walk;
+  walk.init(col_ptr, row_idx, nnz_t, j, j, nb - 1, l);
+
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)&ring[0];
+  uint32_t a_addr[kStepsD];
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) a_addr[c] = row_read_addr<D>(base, qh, n, h, c);
+  uint32_t t_addr[kTilesD];
+#pragma unroll
+  for (int dt = 0; dt < kTilesD; ++dt) t_addr[dt] = tr_read_addr<D>(base, qh, g, gi, dt);
+  // Statistics of the query rows of this lane's result registers: register r
+  // holds query row 32qh + 16 (r >> 3) + 8h + (r & 7).
+  const uint32_t st_addr = base + 2 * kTileBytes + 8 * (32 * qh + 8 * h);
+
+  f32x16 adk[kTilesD], adv[kTilesD];
+#pragma unroll
+  for (int dt = 0; dt < kTilesD; ++dt) {
+    adk[dt] = f32x16{};
+    adv[dt] = f32x16{};
+  }
+
+  auto compute = [&](int i, auto T_c) {
+    constexpr int kOff = decltype(T_c)::value * kStageBytes;
+    if (i == j && qh < kh) return;  // queries of this half all before the keys
+    u32x4 qa[kStepsD], da[kStepsD], st[8];
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) {
+      qa[c] = lds_read_b128<kOff>(a_addr[c]);
+      da[c] = lds_read_b128<kOff + kTileBytes>(a_addr[c]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      st[e] = lds_read_b128<kOff>(st_addr + 16 * e);
+      st[4 + e] = lds_read_b128<kOff + 128>(st_addr + 16 * e);
+    }
+    lds_wait_all(qa);
+    lds_wait_all(da);
+    lds_wait_all(st);
+    // S = Q . K^T and dP = dO . V^T: MFMA row m holds query 32qh + pi(m), column n key 32kh + n.
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) s = E::mfma(qa[c], kop[c], s);
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) dp = E::mfma(da[c], vop[c], dp);
+    u32x2 qt[kTilesD * 4], dt_[kTilesD * 4];
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt) {
+      tr_reads<kOff, G::kRowBytes>(&qt[dt * 4], t_addr[dt]);
+      tr_reads<kOff + kTileBytes, G::kRowBytes>(&dt_[dt * 4], t_addr[dt]);
+    }
+    if (i == j && qh == kh) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qpos = 16 * (r >> 3) + 8 * h + (r & 7);
+        if (qpos < n) s[r] = -__builtin_inff();
+      }
+    }
+    u32x4 pp[2], pd[2];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 8 * gg + 2 * x;
+        const u32x4 sv = st[4 * gg + x];  // rows r, r + 1: (lse2, Delta) pairs
+        const float l0 = __uint_as_float(sv[0]), d0 = __uint_as_float(sv[1]);
+        const float l1 = __uint_as_float(sv[2]), d1 = __uint_as_float(sv[3]);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -l0));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, -l1));
+        pp[gg][x] = E::pack(p0, p1);
+        pd[gg][x] = E::pack(p0 * (dp[r] - d0), p1 * (dp[r + 1] - d1));
+      }
+    lds_wait_all(qt);
+    lds_wait_all(dt_);
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt)
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        adv[dt] = E::mfma(tr_operand(&dt_[dt * 4], gg), pp[gg], adv[dt]);
+        adk[dt] = E::mfma(tr_operand(&qt[dt * 4], gg), pd[gg], adk[dt]);
+      }
+  };
+
+  int blk[2];
+  blk[0] = walk.next(-1);
+  blk[1] = blk[0] >= 0 ? walk.next(blk[0]) : -1;
+  if (blk[0] >= 0) {
+    fill(blk[0], ring);
+    if (blk[1] >= 0) fill(blk[1], ring + kStageBytes);
+    bool pre = blk[1] >= 0;
+    int last = pre ? blk[1] : blk[0];
+    bool done = false;
+    auto step = [&](auto T_c) {
+      constexpr int t = decltype(T_c)::value;
+      constexpr int refill = t ^ 1;
+      if (pre)
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(kFillOps));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      ring_barrier();
+      if (!pre) {
+        const int in = last >= 0 ? walk.next(last) : -1;
+        blk[refill] = in;
+        last = in;
+        if (in >= 0) fill(in, ring + refill * kStageBytes);
+      }
+      pre = false;
+      compute(blk[t], T_c);
+      done = blk[refill] < 0;
+    };
+    while (!done) {
+      step(std::integral_constant<int, 0>{});
+      if (!done) step(std::integral_constant<int, 1>{});
+    }
+    __syncthreads();
+  }
+
+  // Sum the two query halves: wave qh keeps head-dim tiles [qh, qh + 1) *
+  // kTilesD / 2 of dK and dV and hands the others to its partner.
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+  constexpr int kHalfTiles = kTilesD / 2;
+  constexpr int kSendStride = 2 * kHalfTiles * 16 + 4;
+  static_assert(4 * 64 * kSendStride * 4 <= kRingBytes, "merge area exceeds the ring");
+  float* const xbase = (float*)&ring[0];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  auto merge = [&](auto QHc) {
+    constexpr int QH = decltype(QHc)::value;
+    constexpr int kSendBase = (1 - QH) * kHalfTiles;
+    constexpr int kKeepBase = QH * kHalfTiles;
+    float* send = xbase + ((kh * 2 + QH) * 64 + l) * kSendStride;
+#pragma unroll
+    for (int t = 0; t < kHalfTiles; ++t)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        *(f32x4*)(send + t * 16 + 4 * g4) =
+            f32x4{adk[kSendBase + t][4 * g4], adk[kSendBase + t][4 * g4 + 1],
+                  adk[kSendBase + t][4 * g4 + 2], adk[kSendBase + t][4 * g4 + 3]};
+        *(f32x4*)(send + (kHalfTiles + t) * 16 + 4 * g4) =
+            f32x4{adv[kSendBase + t][4 * g4], adv[kSendBase + t][4 * g4 + 1],
+                  adv[kSendBase + t][4 * g4 + 2], adv[kSendBase + t][4 * g4 + 3]};
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    ring_barrier();
+    const float* recv = xbase + ((kh * 2 + (1 - QH)) * 64 + l) * kSendStride;
+    if (krow < S) {
+      uint16_t* krow_dk = dk + lane_off + (int64_t)krow * D;
+      uint16_t* krow_dv = dv + lane_off + (int64_t)krow * D;
+#pragma unroll
+      for (int t = 0; t < kHalfTiles; ++t)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const f32x4 yk = *(const f32x4*)(recv + t * 16 + 4 * gg);
+          const f32x4 yv = *(const f32x4*)(recv + (kHalfTiles + t) * 16 + 4 * gg);
+          float xk[4], xv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xk[e] = (adk[kKeepBase + t][4 * gg + e] + yk[e]) * scale;
+            xv[e] = adv[kKeepBase + t][4 * gg + e] + yv[e];
+          }
+          const int col = 32 * (kKeepBase + t) + 8 * gg + 4 * h;
+          *(u32x2*)(krow_dk + col) = u32x2{E::pack(xk[0], xk[1]), E::pack(xk[2], xk[3])};
+          *(u32x2*)(krow_dv + col) = u32x2{E::pack(xv[0], xv[1]), E::pack(xv[2], xv[3])};
+        }
+    }
+  };
+  if (qh == 0)
+    merge(std::integral_constant<int, 0>{});
+  else
+    merge(std::integral_constant<int, 1>{});
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
+  const int64_t nb = (a.S + kBlock - 1) / kBlock;
+  const int64_t max_wg = (int64_t(1) << 31) / kThreads;
+  const int64_t lanes_per_launch = max_wg / nb > 0 ? max_wg / nb : 1;
+  for (int64_t l0 = 0; l0 < a.lanes; l0 += lanes_per_launch) {
+    const int64_t nl = a.lanes - l0 < lanes_per_launch ? a.lanes - l0 : lanes_per_launch;
+    hipLaunchKernelGGL((attention_bwd_dq_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
+                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, a.row_ptr, a.col_idx,
+                       a.nnz, (int)a.S, (int)nb, l0, a.scale_log2, a.scale, (float2*)a.stats,
+                       (uint16_t*)a.dq);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  for (int64_t l0 = 0; l0 < a.lanes; l0 += lanes_per_launch) {
+    const int64_t nl = a.lanes - l0 < lanes_per_launch ? a.lanes - l0 : lanes_per_launch;
+    hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
+                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, (const float2*)a.stats, a.col_ptr, a.row_idx, a.nnz_t,
+                       (int)a.S, (int)nb, l0, a.scale_log2, a.scale, (uint16_t*)a.dk, (uint16_t*)a.dv);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t stream) {
+  if (a.D == 64) return a.bf16 ? launch_bwd_typed<64, true>(a, stream) : launch_bwd_typed<64, false>(a, stream);
+  return a.bf16 ? launch_bwd_typed<128, true>(a, stream) : launch_bwd_typed<128, false>(a, stream);
+}
+
+}  // namespace tsa

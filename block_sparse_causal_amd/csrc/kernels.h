@@ -7,11 +7,36 @@
 
 namespace tsa {
 
-// Scheduled attention forward over `lanes` lanes of [S, D] (D = 64 or 128).
-hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* out,
+// Scheduled attention forward over `lanes` lanes of [S, D] (D = 64 or 128);
+// lse [lanes, S] (natural log of each row's denominator) is written when not null.
+hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                                 bool bf16, int64_t lanes, int64_t S, int D,
                                 const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                                 float scale_log2, hipStream_t stream);
+
+// Scheduled attention backward: the dq kernel (CSR rows, also writes the per-row
+// statistics) and then the dkdv kernel (columns of the transposed schedule).
+struct BwdArgs {
+  const void *q, *k, *v, *out, *dout;
+  const float* lse;               // [lanes, S], natural log
+  const int32_t *row_ptr, *col_idx;
+  int64_t nnz;
+  const int32_t *col_ptr, *row_idx;
+  int64_t nnz_t;
+  void *dq, *dk, *dv;
+  void* stats;                    // [lanes, S] float2 workspace
+  bool bf16;
+  int64_t lanes, S;
+  int D;
+  float scale, scale_log2;
+};
+hipError_t launch_attention_bwd(const BwdArgs& args, hipStream_t stream);
+
+// Column view of a CSR schedule (see schedule_transpose.hip).
+size_t transpose_workspace_bytes(int64_t nb);
+hipError_t launch_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* col_idx,
+                                     int64_t nnz, int32_t* col_ptr, int32_t* row_idx,
+                                     void* workspace, hipStream_t stream);
 
 // Schedule builder: centroids -> distances -> MST -> elder rule -> top-k -> CSR.
 struct ScheduleWorkspace {

@@ -58,6 +58,71 @@ int64_t row_cap(int32_t sink, int32_t local_radius, int32_t topk) {
   return (int64_t)sink + (int64_t)local_radius + 1 + (int64_t)topk;
 }
 
+
+// Checks shared by the attention entry points (no GPU call); sets *lanes.
+int check_attention_args(const char* fn, int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                         int64_t nnz, int32_t block, float sm_scale, int64_t* lanes) {
+  if (dtype != TSA_F16 && dtype != TSA_BF16)
+    return fail(TSA_ERR_INVALID_ARG, "%s: dtype must be TSA_F16 or TSA_BF16", fn);
+  if (B < 0 || H < 0 || S < 0 || nnz < 0)
+    return fail(TSA_ERR_INVALID_ARG, "%s: B, H, S and nnz must be >= 0", fn);
+  if (block != TSA_BLOCK)
+    return fail(TSA_ERR_UNSUPPORTED, "%s: block must be %d, got %d", fn, TSA_BLOCK, block);
+  if (D != 64 && D != 128)
+    return fail(TSA_ERR_UNSUPPORTED, "%s: head dim must be 64 or 128, got %lld", fn, (long long)D);
+  if (std::isnan(sm_scale) || std::isinf(sm_scale))
+    return fail(TSA_ERR_INVALID_ARG, "%s: sm_scale must be finite", fn);
+  if (S > INT32_MAX - TSA_BLOCK) return fail(TSA_ERR_SHAPE, "%s: S=%lld too large", fn, (long long)S);
+  if (B > 0 && H > INT64_MAX / B) return fail(TSA_ERR_SHAPE, "%s: B*H overflows", fn);
+  *lanes = B * H;
+  if (*lanes > 0 && S > 0 && *lanes > INT64_MAX / (S * D))
+    return fail(TSA_ERR_SHAPE, "%s: B*H*S*D overflows", fn);
+  return TSA_OK;
+}
+
+// lse_required: the entry point returns lse (a NULL lse is then an error).
+int attention_fwd(const char* fn, const void* q, const void* k, const void* v, void* out, float* lse,
+                  bool lse_required, int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D, const int32_t* row_ptr,
+                  const int32_t* col_idx, int64_t nnz, int32_t block, float sm_scale, void* stream) {
+  int64_t lanes = 0;
+  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, &lanes);
+  if (rc != TSA_OK) return rc;
+  if (lanes == 0 || S == 0) return ok();  // empty problem: nothing to read or write
+  if (!q || !k || !v || !out || !row_ptr || (nnz > 0 && !col_idx) || (lse_required && !lse))
+    return fail(TSA_ERR_INVALID_ARG, "%s: NULL pointer argument", fn);
+  for (const void* p : {q, k, v, (const void*)out})
+    if (((uintptr_t)p) % 16 != 0)
+      return fail(TSA_ERR_INVALID_ARG, "%s: q, k, v and out must be 16-byte aligned", fn);
+  if (lse && ((uintptr_t)lse) % 4 != 0)
+    return fail(TSA_ERR_INVALID_ARG, "%s: lse must be 4-byte aligned", fn);
+  const size_t bytes = (size_t)(lanes * S * D) * 2;
+  const size_t lse_bytes = (size_t)(lanes * S) * 4;
+  const char* o0 = (const char*)out;
+  const char* l0 = (const char*)lse;
+  const char* ins[3] = {(const char*)q, (const char*)k, (const char*)v};
+  for (const char* p : ins) {
+    if (o0 < p + bytes && p < o0 + bytes)
+      return fail(TSA_ERR_INVALID_ARG, "%s: out overlaps an input", fn);
+    if (lse && l0 < p + bytes && p < l0 + lse_bytes)
+      return fail(TSA_ERR_INVALID_ARG, "%s: lse overlaps an input", fn);
+  }
+  if (lse && l0 < o0 + bytes && o0 < l0 + lse_bytes)
+    return fail(TSA_ERR_INVALID_ARG, "%s: lse overlaps out", fn);
+  if ((rc = check_device_ptr(q, "q")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(k, "k")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(v, "v")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(out, "out")) != TSA_OK) return rc;
+  if (lse && (rc = check_device_ptr(lse, "lse")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
+  if (nnz > 0 && (rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
+  const double scale = sm_scale > 0.0f ? (double)sm_scale : 1.0 / std::sqrt((double)D);
+  const float scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
+  hipError_t e = tsa::launch_attention_fwd(q, k, v, out, lse, dtype == TSA_BF16, lanes, S, (int)D,
+                                           row_ptr, col_idx, nnz, scale_log2, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,51 +282,139 @@ int tsa_scheduled_attention_fwd(const void* q, const void* k, const void* v, voi
                                 int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D,
                                 const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                                 int32_t block, float sm_scale, void* stream) {
-  if (dtype != TSA_F16 && dtype != TSA_BF16)
-    return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: dtype must be TSA_F16 or TSA_BF16");
-  if (B < 0 || H < 0 || S < 0 || nnz < 0)
-    return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: B, H, S and nnz must be >= 0");
-  if (block != TSA_BLOCK)
-    return fail(TSA_ERR_UNSUPPORTED, "tsa_scheduled_attention_fwd: block must be %d, got %d",
-                TSA_BLOCK, block);
-  if (D != 64 && D != 128)
-    return fail(TSA_ERR_UNSUPPORTED, "tsa_scheduled_attention_fwd: head dim must be 64 or 128, got %lld",
-                (long long)D);
-  if (std::isnan(sm_scale) || std::isinf(sm_scale))
-    return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: sm_scale must be finite");
-  if (S > INT32_MAX - TSA_BLOCK)
-    return fail(TSA_ERR_SHAPE, "tsa_scheduled_attention_fwd: S=%lld too large", (long long)S);
-  if (B > 0 && H > INT64_MAX / B)
-    return fail(TSA_ERR_SHAPE, "tsa_scheduled_attention_fwd: B*H overflows");
-  const int64_t lanes = B * H;
-  if (lanes > 0 && S > 0 && lanes > INT64_MAX / (S * D))
-    return fail(TSA_ERR_SHAPE, "tsa_scheduled_attention_fwd: B*H*S*D overflows");
-  const int64_t nb = (S + TSA_BLOCK - 1) / TSA_BLOCK;
-  if (lanes == 0 || S == 0) return ok();  // empty problem: nothing to read or write
-  if (!q || !k || !v || !out || !row_ptr || (nnz > 0 && !col_idx))
-    return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: NULL pointer argument");
-  for (const void* p : {q, k, v, (const void*)out})
-    if (((uintptr_t)p) % 16 != 0)
-      return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: q, k, v and out must be 16-byte aligned");
-  const size_t bytes = (size_t)(lanes * S * D) * 2;
-  const char* o0 = (const char*)out;
-  const char* ins[3] = {(const char*)q, (const char*)k, (const char*)v};
-  for (const char* p : ins)
-    if (o0 < p + bytes && p < o0 + bytes)
-      return fail(TSA_ERR_INVALID_ARG, "tsa_scheduled_attention_fwd: out overlaps an input");
+  return attention_fwd("tsa_scheduled_attention_fwd", q, k, v, out, nullptr, false, dtype, B, H, S, D,
+                       row_ptr, col_idx, nnz, block, sm_scale, stream);
+}
+
+int tsa_scheduled_attention_fwd_lse(const void* q, const void* k, const void* v, void* out,
+                                    float* lse, int32_t dtype, int64_t B, int64_t H, int64_t S,
+                                    int64_t D, const int32_t* row_ptr, const int32_t* col_idx,
+                                    int64_t nnz, int32_t block, float sm_scale, void* stream) {
+  return attention_fwd("tsa_scheduled_attention_fwd_lse", q, k, v, out, lse, true, dtype, B, H, S, D,
+                       row_ptr, col_idx, nnz, block, sm_scale, stream);
+}
+
+size_t tsa_schedule_transpose_workspace_bytes(int64_t nb) {
+  if (nb <= 0 || nb > TSA_MAX_SCHEDULE_BLOCKS) return 0;
+  return tsa::transpose_workspace_bytes(nb);
+}
+
+int tsa_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                           int32_t* col_ptr, int32_t* row_idx, int64_t row_capacity,
+                           void* workspace, size_t workspace_bytes, int64_t* nnz_host,
+                           void* stream) {
+  const char* fn = "tsa_schedule_transpose";
+  if (nb < 0 || nnz < 0 || row_capacity < 0)
+    return fail(TSA_ERR_INVALID_ARG, "%s: nb, nnz and row_capacity must be >= 0", fn);
+  if (nb > TSA_MAX_SCHEDULE_BLOCKS)
+    return fail(TSA_ERR_UNSUPPORTED, "%s: %lld blocks exceed the limit of %d", fn, (long long)nb,
+                TSA_MAX_SCHEDULE_BLOCKS);
+  const int64_t tri = nb * (nb + 1) / 2;
+  const int64_t need = nnz < tri ? nnz : tri;
+  if (row_capacity < need)
+    return fail(TSA_ERR_SCHEDULE, "%s: row_capacity %lld < min(nnz, nb*(nb+1)/2) = %lld", fn,
+                (long long)row_capacity, (long long)need);
+  if (row_ptr == nullptr || col_ptr == nullptr || (nnz > 0 && col_idx == nullptr) ||
+      (need > 0 && row_idx == nullptr))
+    return fail(TSA_ERR_INVALID_ARG, "%s: NULL pointer argument", fn);
+  if (nb > 0) {
+    const size_t ws = tsa::transpose_workspace_bytes(nb);
+    if (workspace == nullptr || workspace_bytes < ws)
+      return fail(TSA_ERR_INVALID_ARG, "%s: workspace of %zu bytes < required %zu", fn,
+                  workspace_bytes, ws);
+    if (((uintptr_t)workspace) % 256 != 0)
+      return fail(TSA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  }
   int rc;
-  if ((rc = check_device_ptr(q, "q")) != TSA_OK) return rc;
-  if ((rc = check_device_ptr(k, "k")) != TSA_OK) return rc;
-  if ((rc = check_device_ptr(v, "v")) != TSA_OK) return rc;
-  if ((rc = check_device_ptr(out, "out")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(col_ptr, "col_ptr")) != TSA_OK) return rc;
+  if (nnz > 0 && (rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
+  if (need > 0 && (rc = check_device_ptr(row_idx, "row_idx")) != TSA_OK) return rc;
+  if (nb > 0 && (rc = check_device_ptr(workspace, "workspace")) != TSA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = tsa::launch_schedule_transpose(nb, row_ptr, col_idx, nnz, col_ptr, row_idx,
+                                                workspace, st);
+  if (e != hipSuccess) return hip_fail(e, "transpose kernels");
+  if (nnz_host) {
+    int32_t n = 0;
+    e = hipMemcpyAsync(&n, col_ptr + nb, sizeof n, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "reading nnz");
+    *nnz_host = n;
+  }
+  return ok();
+}
+
+size_t tsa_scheduled_attention_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S) {
+  if (B < 0 || H < 0 || S < 0) return 0;
+  if (B > 0 && H > INT64_MAX / B) return 0;
+  const int64_t lanes = B * H;
+  if (lanes > 0 && S > INT64_MAX / 8 / lanes) return 0;
+  return (size_t)(lanes * S * 8);
+}
+
+int tsa_scheduled_attention_bwd(const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, int32_t dtype, int64_t B,
+                                int64_t H, int64_t S, int64_t D, const int32_t* row_ptr,
+                                const int32_t* col_idx, int64_t nnz, const int32_t* col_ptr,
+                                const int32_t* row_idx, int64_t nnz_t, int32_t block,
+                                float sm_scale, void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  const char* fn = "tsa_scheduled_attention_bwd";
+  int64_t lanes = 0;
+  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, &lanes);
+  if (rc != TSA_OK) return rc;
+  if (nnz_t < 0) return fail(TSA_ERR_INVALID_ARG, "%s: nnz_t must be >= 0", fn);
+  if (lanes == 0 || S == 0) return ok();
+  if (!q || !k || !v || !out || !dout || !lse || !row_ptr || (nnz > 0 && !col_idx) || !col_ptr ||
+      (nnz_t > 0 && !row_idx) || !dq || !dk || !dv || !workspace)
+    return fail(TSA_ERR_INVALID_ARG, "%s: NULL pointer argument", fn);
+  for (const void* p : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (((uintptr_t)p) % 16 != 0)
+      return fail(TSA_ERR_INVALID_ARG, "%s: q, k, v, out, dout, dq, dk and dv must be 16-byte aligned", fn);
+  if (((uintptr_t)lse) % 4 != 0 || ((uintptr_t)workspace) % 16 != 0)
+    return fail(TSA_ERR_INVALID_ARG, "%s: lse must be 4-byte and workspace 16-byte aligned", fn);
+  const size_t ws = (size_t)(lanes * S * 8);
+  if (workspace_bytes < ws)
+    return fail(TSA_ERR_INVALID_ARG, "%s: workspace of %zu bytes < required %zu", fn,
+                workspace_bytes, ws);
+  const size_t bytes = (size_t)(lanes * S * D) * 2;
+  const char* ins[6] = {(const char*)q, (const char*)k, (const char*)v, (const char*)out,
+                        (const char*)dout, (const char*)lse};
+  const size_t in_bytes[6] = {bytes, bytes, bytes, bytes, bytes, (size_t)(lanes * S * 4)};
+  const char* outs[4] = {(const char*)dq, (const char*)dk, (const char*)dv, (const char*)workspace};
+  const size_t out_bytes[4] = {bytes, bytes, bytes, ws};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (outs[a] < ins[b] + in_bytes[b] && ins[b] < outs[a] + out_bytes[a])
+        return fail(TSA_ERR_INVALID_ARG, "%s: an output or the workspace overlaps an input", fn);
+    for (int b = a + 1; b < 4; ++b)
+      if (outs[a] < outs[b] + out_bytes[b] && outs[b] < outs[a] + out_bytes[a])
+        return fail(TSA_ERR_INVALID_ARG, "%s: dq, dk, dv and the workspace must not overlap", fn);
+  }
+  const char* names[] = {"q", "k", "v", "out", "dout", "lse"};
+  for (int b = 0; b < 6; ++b)
+    if ((rc = check_device_ptr(ins[b], names[b])) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(dq, "dq")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(dk, "dk")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(dv, "dv")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(workspace, "workspace")) != TSA_OK) return rc;
   if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
   if (nnz > 0 && (rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(col_ptr, "col_ptr")) != TSA_OK) return rc;
+  if (nnz_t > 0 && (rc = check_device_ptr(row_idx, "row_idx")) != TSA_OK) return rc;
+  tsa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+  a.row_ptr = row_ptr; a.col_idx = col_idx; a.nnz = nnz;
+  a.col_ptr = col_ptr; a.row_idx = row_idx; a.nnz_t = nnz_t;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.stats = workspace;
+  a.bf16 = dtype == TSA_BF16;
+  a.lanes = lanes; a.S = S; a.D = (int)D;
   const double scale = sm_scale > 0.0f ? (double)sm_scale : 1.0 / std::sqrt((double)D);
-  const float scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
-  (void)nb;
-  hipError_t e = tsa::launch_attention_fwd(q, k, v, out, dtype == TSA_BF16, lanes, S, (int)D,
-                                           row_ptr, col_idx, nnz, scale_log2, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  a.scale = (float)scale;
+  a.scale_log2 = (float)(scale * 1.4426950408889634);
+  hipError_t e = tsa::launch_attention_bwd(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention backward kernels");
   return ok();
 }
 

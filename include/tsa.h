@@ -3,7 +3,8 @@
  * for AMD Instinct MI355X (gfx950).
  *
  * The operations are those of the pages "Add topology-derived sparse attention
- * kernel" (triton-lang/kernels pull request 22) and its mirror page:
+ * kernel" (triton-lang/kernels pull request 22) and its mirror page, plus the
+ * backward pass of the attention, which the pages do not have:
  *   - a forward-only causal attention that consumes a CSR block schedule
  *     (Summary, first bullet), for [S, D] and [B, H, S, D] inputs with one
  *     schedule shared by every batch/head lane (third bullet), whose output has
@@ -13,7 +14,9 @@
  *     centroids (second bullet), elder-rule salience as described in the
  *     mirror page's Rust-port commit note, computed from MST edges as in its
  *     schedule.py commit note;
- *   - the dense causal CSR used as the like-for-like baseline (Local benchmark).
+ *   - the dense causal CSR used as the like-for-like baseline (Local benchmark);
+ *   - the gradients of the attention with respect to q, k and v over the same
+ *     schedule, and the column view of a schedule they gather over.
  *
  * Conventions shared by every entry point
  *   - All functions are callable from C; none throws.  Status: 0 = TSA_OK,
@@ -205,6 +208,100 @@ int tsa_scheduled_attention_fwd(const void* q, const void* k, const void* v, voi
                                 int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D,
                                 const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                                 int32_t block, float sm_scale, void* stream);
+
+/*
+ * Forward scheduled attention that also returns each row's log-sum-exp, the
+ * statistic the backward pass reads.  (Same passages as
+ * tsa_scheduled_attention_fwd; the mirror page's Rust-port commit note: the
+ * running maximum and denominator of each row.)
+ *   lse   device float [B, H, S], written: lse[t] = log of the row's softmax
+ *         denominator in natural units, log sum_{u in A(t)} exp(scale q_t.k_u),
+ *         from the same fp32 running max and denominator the output is
+ *         normalised by; -inf for a row with no allowed key.  4-byte aligned,
+ *         must not overlap q, k, v or out.
+ * Every other argument, the output and the errors are those of
+ * tsa_scheduled_attention_fwd; a NULL lse is TSA_ERR_INVALID_ARG.
+ */
+int tsa_scheduled_attention_fwd_lse(const void* q, const void* k, const void* v, void* out,
+                                    float* lse, int32_t dtype, int64_t B, int64_t H, int64_t S,
+                                    int64_t D, const int32_t* row_ptr, const int32_t* col_idx,
+                                    int64_t nnz, int32_t block, float sm_scale, void* stream);
+
+/*
+ * Device workspace, in bytes, of tsa_schedule_transpose for nb blocks (256-byte
+ * aligned start required).  Host-only.  0 when nb <= 0 (none is needed for nb = 0)
+ * or nb > TSA_MAX_SCHEDULE_BLOCKS.
+ */
+size_t tsa_schedule_transpose_workspace_bytes(int64_t nb);
+
+/*
+ * Column view (CSC) of a causal CSR schedule: column j lists, ascending, the
+ * query blocks i whose row lists key block j.  The key and value gradients of
+ * block j gather over exactly these rows (backward of the forward of PR page,
+ * Summary, first bullet; the pages' kernel has none, see
+ * tsa_scheduled_attention_bwd).  Build it once per schedule.
+ *   row_ptr, col_idx  device int32 CSR, nb rows, `nnz` readable entries.  An
+ *               entry of row i counts exactly when the attention kernels accept
+ *               it: it lies in 0..i and exceeds every earlier entry of the row
+ *               that lies in 0..i (all entries, for a row that is strictly
+ *               ascending within 0..i as the schedule contract asks).
+ *   col_ptr     device int32 [nb + 1], written.
+ *   row_idx     device int32 [row_capacity], entries [0, col_ptr[nb]) written;
+ *               row_capacity >= min(nnz, nb*(nb+1)/2), so it can never overflow.
+ *   workspace   device, >= tsa_schedule_transpose_workspace_bytes(nb) bytes,
+ *               256-byte aligned, any contents on entry (NULL allowed when nb = 0).
+ *   nnz_host    host int64 or NULL: when not NULL the call waits for the stream
+ *               and stores col_ptr[nb] there.
+ * Errors: negative sizes (TSA_ERR_INVALID_ARG), nb > TSA_MAX_SCHEDULE_BLOCKS
+ * (TSA_ERR_UNSUPPORTED), a short row_idx (TSA_ERR_SCHEDULE), a short or misaligned
+ * workspace, NULL or non-device pointers.  Nothing is written on error.
+ */
+int tsa_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* col_idx,
+                           int64_t nnz, int32_t* col_ptr, int32_t* row_idx, int64_t row_capacity,
+                           void* workspace, size_t workspace_bytes, int64_t* nnz_host,
+                           void* stream);
+
+/*
+ * Device workspace, in bytes, of tsa_scheduled_attention_bwd: 8 bytes per query
+ * row of every lane (B * H * S * 8).  Host-only; 0 for negative or overflowing sizes.
+ */
+size_t tsa_scheduled_attention_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S);
+
+/*
+ * Backward of tsa_scheduled_attention_fwd: the gradients of q, k and v for an
+ * upstream gradient dout of the output.  The pages' kernel is forward-only (PR
+ * page, Summary, first bullet; the mirror page's note on learned segment
+ * boundaries says training would otherwise run dense).  With P_tu = exp(scale
+ * q_t.k_u - lse_t) on the allowed keys A(t) of row t (0 elsewhere):
+ *   dV = P^T dout,  dS = P * (dout V^T - Delta),  Delta_t = dout_t . out_t,
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, k, v, out, dout   device, [B, H, S, D] of `dtype` ([S, D]: B = H = 1);
+ *               out is the forward's output for these q, k, v and schedule.
+ *   lse         device float [B, H, S] from tsa_scheduled_attention_fwd_lse.
+ *   row_ptr, col_idx, nnz   the CSR the forward used (same contract).
+ *   col_ptr, row_idx, nnz_t its column view from tsa_schedule_transpose
+ *               (nnz_t readable row_idx entries).  The kernels skip entries of a
+ *               column that are outside j..nb-1 or not above the previous accepted
+ *               one; a column view that is not the CSR's transpose gives
+ *               unspecified gradients (never an out-of-bounds access).
+ *   block       must be 64;  D 64 or 128;  sm_scale as in the forward.
+ *   dq, dk, dv  device, q's shape and dtype, written (rounded to nearest even).
+ *   workspace   device, >= tsa_scheduled_attention_bwd_workspace_bytes(B, H, S)
+ *               bytes, 16-byte aligned, any contents on entry; it holds each
+ *               row's (lse, Delta) between the two kernels.
+ * All 16-bit tensors 16-byte aligned; dq, dk, dv and the workspace must not
+ * overlap each other or any input.  Scores, statistics and accumulators are
+ * fp32; P and dS are rounded to the input dtype as MFMA operands.  B, H or S
+ * equal to 0 is a valid empty call.  Errors as tsa_scheduled_attention_fwd, plus
+ * a short or misaligned workspace (TSA_ERR_INVALID_ARG).
+ */
+int tsa_scheduled_attention_bwd(const void* q, const void* k, const void* v, const void* out,
+                                const void* dout, const float* lse, int32_t dtype, int64_t B,
+                                int64_t H, int64_t S, int64_t D, const int32_t* row_ptr,
+                                const int32_t* col_idx, int64_t nnz, const int32_t* col_ptr,
+                                const int32_t* row_idx, int64_t nnz_t, int32_t block,
+                                float sm_scale, void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

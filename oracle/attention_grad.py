@@ -128,7 +128,7 @@ def attention_backward_rows(q, k, v, do, row_ptr, col_idx, q_rows, k_rows, block
     dq_sel = scale * (ds @ kf)
     dk_sel = np.zeros((k_rows.shape[0], D))
     dv_sel = np.zeros((k_rows.shape[0], D))
-    for t0 in range(0, S, chunk):
+    for t0 in range(0, S if k_rows.size else 0, chunk):
         rows = np.arange(t0, min(S, t0 + chunk))
         m = allowed_key_mask(row_ptr, col_idx, S, block, rows)
         pr, _ = _row_stats(qf[rows], kf, m, scale)

@@ -31,7 +31,10 @@ def test_header_declares_the_entry_points():
     for required in ("tsa_build_schedule", "tsa_scheduled_attention_fwd", "tsa_dense_causal_schedule",
                      "tsa_segment_schedule", "tsa_segment_schedule_nnz", "tsa_schedule_max_nnz",
                      "tsa_build_schedule_ex",
-                     "tsa_build_schedule_workspace_bytes", "tsa_last_error", "tsa_version"):
+                     "tsa_build_schedule_workspace_bytes", "tsa_last_error", "tsa_version",
+                     "tsa_scheduled_attention_fwd_lse", "tsa_schedule_transpose",
+                     "tsa_schedule_transpose_workspace_bytes", "tsa_scheduled_attention_bwd",
+                     "tsa_scheduled_attention_bwd_workspace_bytes"):
         assert required in names
 
 
@@ -168,3 +171,86 @@ def test_dense_schedule_argument_checks_before_gpu(lib):
     assert lib.tsa_dense_causal_schedule(10, vp(None), vp(None), 54, vp(None)) == -4
     assert lib.tsa_dense_causal_schedule(10, vp(None), vp(None), 55, vp(None)) == -1
     assert lib.tsa_dense_causal_schedule(70000, vp(None), vp(None), 1 << 40, vp(None)) == -3
+
+
+def test_fwd_lse_requires_lse(lib):
+    vp = ctypes.c_void_p
+    base = 1 << 40  # never dereferenced: the NULL check precedes any GPU call
+    st = lib.tsa_scheduled_attention_fwd_lse(vp(base), vp(base + (1 << 24)), vp(base + (2 << 24)),
+                                             vp(base + (3 << 24)), vp(None), 1, 1, 1, 128, 64,
+                                             vp(base), vp(base), 3, 64, 0.0, vp(None))
+    assert st == -1 and b"NULL" in lib.tsa_last_error()
+    # lse overlapping out
+    st = lib.tsa_scheduled_attention_fwd_lse(vp(base), vp(base + (1 << 24)), vp(base + (2 << 24)),
+                                             vp(base + (3 << 24)), vp(base + (3 << 24) + 64), 1, 1, 1, 128,
+                                             64, vp(base), vp(base), 3, 64, 0.0, vp(None))
+    assert st == -1 and b"overlap" in lib.tsa_last_error()
+    assert lib.tsa_scheduled_attention_fwd_lse(vp(None), vp(None), vp(None), vp(None), vp(None), 1, 0, 1,
+                                               128, 64, vp(None), vp(None), 0, 64, 0.0, vp(None)) == 0
+
+
+def test_transpose_workspace_and_checks_before_gpu(lib):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    assert lib.tsa_schedule_transpose_workspace_bytes(0) == 0
+    assert lib.tsa_schedule_transpose_workspace_bytes(-3) == 0
+    assert lib.tsa_schedule_transpose_workspace_bytes(4097) == 0
+    for nb in (1, 31, 32, 33, 64, 512, 4096):
+        nw = -(-nb // 32)
+        assert lib.tsa_schedule_transpose_workspace_bytes(nb) == 4 * (nw * nb + nb)
+
+    def call(nb=10, nnz=55, cap=55, ws=1 << 20, rp=None, ci=None, cp=None, ri=None, wsp=None):
+        return lib.tsa_schedule_transpose(nb, vp(rp), vp(ci), nnz, vp(cp), vp(ri), cap, vp(wsp), ws, None,
+                                          vp(None))
+
+    assert call(nb=-1) == -1
+    assert call(nnz=-1) == -1
+    assert call(nb=4097, nnz=0, cap=0) == -2
+    assert call(cap=54) == -4  # min(nnz, nb(nb+1)/2) = 55
+    assert call(nnz=100, cap=54) == -4
+    assert b"row_capacity" in lib.tsa_last_error()
+    assert call() == -1  # NULL pointers
+    base = 1 << 40
+    assert call(rp=base, ci=base, cp=base, ri=base, wsp=base, ws=10) == -1
+    assert b"workspace" in lib.tsa_last_error()
+    assert call(rp=base, ci=base, cp=base, ri=base, wsp=base + 16) == -1
+    assert b"aligned" in lib.tsa_last_error()
+
+
+def _bwd(lib, **kw):
+    vp = ctypes.c_void_p
+    a = dict(q=None, k=None, v=None, out=None, dout=None, lse=None, dtype=1, B=1, H=1, S=128, D=64,
+             row_ptr=None, col_idx=None, nnz=3, col_ptr=None, row_idx=None, nnz_t=3, block=64, scale=0.0,
+             dq=None, dk=None, dv=None, ws=None, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.tsa_scheduled_attention_bwd(
+        vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["out"]), vp(a["dout"]), vp(a["lse"]), a["dtype"], a["B"],
+        a["H"], a["S"], a["D"], vp(a["row_ptr"]), vp(a["col_idx"]), a["nnz"], vp(a["col_ptr"]),
+        vp(a["row_idx"]), a["nnz_t"], a["block"], a["scale"], vp(a["dq"]), vp(a["dk"]), vp(a["dv"]),
+        vp(a["ws"]), a["ws_bytes"], vp(a["stream"]))
+
+
+def test_backward_workspace_and_checks_before_gpu(lib):
+    assert lib.tsa_scheduled_attention_bwd_workspace_bytes(4, 16, 4096) == 4 * 16 * 4096 * 8
+    assert lib.tsa_scheduled_attention_bwd_workspace_bytes(-1, 1, 1) == 0
+    assert lib.tsa_scheduled_attention_bwd_workspace_bytes(1, 1, 1 << 62) == 0
+    assert _bwd(lib, dtype=7) == -1
+    assert _bwd(lib, D=96) == -2
+    assert _bwd(lib, block=128) == -2
+    assert _bwd(lib, nnz_t=-1) == -1
+    assert _bwd(lib, scale=float("inf")) == -1
+    assert _bwd(lib) == -1 and b"NULL" in lib.tsa_last_error()
+    assert _bwd(lib, S=0) == 0 and _bwd(lib, H=0) == 0
+    base = 1 << 40  # never dereferenced: these checks precede any GPU call
+    mb = 1 << 24
+    good = dict(q=base, k=base + mb, v=base + 2 * mb, out=base + 3 * mb, dout=base + 4 * mb, lse=base + 5 * mb,
+                row_ptr=base, col_idx=base, col_ptr=base, row_idx=base, dq=base + 6 * mb, dk=base + 7 * mb,
+                dv=base + 8 * mb, ws=base + 9 * mb)
+    assert _bwd(lib, **{**good, "ws_bytes": 128 * 8 - 1}) == -1
+    assert b"workspace" in lib.tsa_last_error()
+    assert _bwd(lib, **{**good, "dq": base + 2 * mb + 256}) == -1  # dq overlaps v
+    assert b"overlap" in lib.tsa_last_error()
+    assert _bwd(lib, **{**good, "dv": base + 6 * mb + 512}) == -1  # dv overlaps dq
+    assert b"overlap" in lib.tsa_last_error()
+    assert _bwd(lib, **{**good, "ws": base + 5 * mb + 16}) == -1  # workspace overlaps lse
+    assert _bwd(lib, **{**good, "dk": base + 7 * mb + 8}) == -1  # misaligned
+    assert b"aligned" in lib.tsa_last_error()
