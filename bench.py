@@ -28,12 +28,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "scheduled-attn fwd effective TFLOP/s (% MFMA peak) + sparse/dense-CSR speedup"
 PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_causal_amd", "csrc", "attention_fwd.hip")
+# sources of the attention forward kernel (its own file and the shared device helpers)
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_causal_amd", "csrc", f) for f in ("attention_fwd.hip", "mfma_tile.h")]
 
 
 def _kernel_hash() -> str:
-    with open(ATTN_SOURCE, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(workload: str):
@@ -262,6 +266,38 @@ def main() -> int:
         seg_ms = d0.elapsed_time(d1) / reps
         seg = {"segment_tokens": 512, "nnz_blocks": seg_nnz, "ms": round(seg_ms, 5),
                "tflops": round(lanes * seg_nnz * 4 * 64 * 64 * w.D / (seg_ms * 1e-3) / 1e12, 3)}
+    # Backward pass over the same schedule: the forward with lse and the column
+    # view once, then back-to-back backward calls (dq kernel, then dk/dv kernel).
+    # Algorithmic work: 5 block products per visited block (S recomputed once, dP,
+    # dV, dQ, dK), 2.5x the forward's.
+    dout = workloads.random_normal(w.shape, w.dtype, 99).to(dev)
+    o_l, lse = tsa.scheduled_attention(q, k, v, rp, ci, return_lse=True)
+    for _ in range(3):
+        tsa.schedule_transpose(rp, ci)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for _ in range(reps):
+        cp, ri = tsa.schedule_transpose(rp, ci)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    tr_ms = d0.elapsed_time(d1) / reps
+    for _ in range(3):
+        grads = tsa.scheduled_attention_backward(q, k, v, o_l, dout, lse, rp, ci, cp, ri)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for _ in range(reps):
+        grads = tsa.scheduled_attention_backward(q, k, v, o_l, dout, lse, rp, ci, cp, ri)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = d0.elapsed_time(d1) / reps
+    if not all(bool(torch.isfinite(g).all()) for g in grads):
+        print("non-finite gradient", file=sys.stderr)
+        return 1
+    bwd_tflops = 2.5 * flops / (bwd_ms * 1e-3) / 1e12
+    backward = {"ms": round(bwd_ms, 5), "tflops": round(bwd_tflops, 3),
+                "frac_of_peak": round(bwd_tflops / PEAK_TFLOPS[w.dtype], 4),
+                "flops_per_block": "5 products of 64x64xD (2.5x forward)",
+                "transpose_ms": round(tr_ms, 5), "transpose_note": "host-synchronising call (reads nnz)"}
     if not bool(torch.isfinite(out).all()):
         print("non-finite output", file=sys.stderr)
         return 1
@@ -310,6 +346,7 @@ def main() -> int:
         "dense_csr_tflops": round(lanes * nnz_dense * 4 * 64 * 64 * w.D / (dense_ms * 1e-3) / 1e12, 3),
         "segment_csr": seg,
         "per_row_topk": per_row,
+        "backward": backward,
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tflops, 3),
