@@ -23,8 +23,8 @@
  *     negative = error.  On error nothing has been written to any output and
  *     tsa_last_error() returns a message (thread-local, valid until the next
  *     call on the same thread).
- *   - Arguments are checked before any GPU work (the pages' "validate ... before
- *     launch", Summary, fifth bullet): sizes and parameters first (no GPU call),
+ *   - Arguments are checked before any GPU work (PR page, Summary, fifth bullet:
+ *     inputs are validated ahead of the launch): sizes and parameters first (no GPU call),
  *     then every device pointer must be device memory on the current HIP device.
  *   - Device pointers are owned by the caller; libtsa allocates nothing.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
@@ -151,7 +151,7 @@ int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D,
 
 /*
  * The dense causal (lower-triangular) CSR for nb blocks: row i lists 0..i.
- * (PR page, Summary: "dense causal CSR layout"; Local benchmark: the dense CSR
+ * (PR page, Summary: the tests cover the dense causal CSR; Local benchmark: the dense CSR
  * path visits every causal block.)  row_ptr int32 [nb + 1] and col_idx int32
  * [col_capacity >= nb*(nb+1)/2], both device memory.
  */

@@ -192,7 +192,7 @@ def build_schedule(
 def dense_causal_schedule(nb: int) -> tuple[np.ndarray, np.ndarray]:
     """Lower-triangular CSR: row i lists blocks 0..i.
 
-    PR page, Summary (tests of the "dense causal CSR layout") and Local
+    PR page, Summary (its tests cover the dense causal CSR) and Local
     benchmark table (dense block counts 136 / 528 / 2080).
     """
     return _csr_from_rows([list(range(i + 1)) for i in range(nb)])
