@@ -204,6 +204,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
 #pragma unroll
   for (int dt = 0; dt < kTilesD; ++dt) o[dt] = f32x16{};
   float m_use = -__builtin_inff();  // exponent offset in use (log2 units)
+  float thr_raw = -__builtin_inff();  // trigger threshold for the raw-score max (below)
   float l_run = 0.0f;               // this lane's share of the denominator
 
   // LDS byte addresses (stage 0) of this lane's K and V operand reads; stage t
@@ -249,12 +250,17 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = max_with_other_half(mx) * scale_log2;
-    const bool grow = mx > m_use + kRescaleSlack;
-    if (__ballot(grow)) {
-      const float m_new = grow ? mx : m_use;
+    // The pair of half-waves holding one query must share its offset, but the
+    // pair's max is only needed when a half's own max can grow the offset: the
+    // trigger compares raw scores with a threshold a little below
+    // (m_use + slack) / scale_log2, and the exact test runs inside.
+    if (__ballot(mx > thr_raw)) {
+      const float mp = max_with_other_half(mx) * scale_log2;
+      const bool grow = mp > m_use + kRescaleSlack;
+      const float m_new = grow ? mp : m_use;
       const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
       m_use = m_new;
+      thr_raw = (m_new + kRescaleSlack) / scale_log2 * (1.0f - 0x1p-20f);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
