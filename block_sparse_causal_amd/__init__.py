@@ -13,6 +13,8 @@ triton-lang/kernels PR 22, Summary):
 * ``build_schedule``       sink + local window + top-k salient key blocks -> CSR
 * ``dense_causal_schedule`` the lower-triangular CSR
 * ``segment_schedule``      the fixed-segment (block-diagonal causal) CSR
+* ``refine_schedule``       a schedule over blocks of 128, 256, ... rows as the
+  equivalent 64-row-block CSR the attention entry points take
 * ``scheduled_attention``  forward causal attention over a CSR block schedule
   (optionally with each row's log-sum-exp)
 
@@ -39,6 +41,7 @@ __all__ = [
     "build_schedule_into",
     "dense_causal_schedule",
     "segment_schedule",
+    "refine_schedule",
     "scheduled_attention",
     "schedule_transpose",
     "scheduled_attention_backward",
@@ -103,6 +106,10 @@ def _load():
     lib.tsa_scheduled_attention_fwd_lse.argtypes = [
         vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, vp, vp, i64, i32, ctypes.c_float, vp
     ]
+    lib.tsa_refine_schedule_max_nnz.restype = i64
+    lib.tsa_refine_schedule_max_nnz.argtypes = [i64, i32, i64]
+    lib.tsa_refine_schedule.restype = ctypes.c_int
+    lib.tsa_refine_schedule.argtypes = [i64, i32, vp, vp, i64, vp, vp, i64, ctypes.POINTER(i64), vp]
     lib.tsa_schedule_transpose_workspace_bytes.restype = sz
     lib.tsa_schedule_transpose_workspace_bytes.argtypes = [i64]
     lib.tsa_schedule_transpose.restype = ctypes.c_int
@@ -162,8 +169,10 @@ def build_schedule(keys: torch.Tensor, block: int = BLOCK, sink: int = 1, local_
     """Topology-derived CSR schedule from the keys of lane (0, 0).
 
     keys: [S, D] or [B, H, S, D] float16/bfloat16 on a GPU.  Returns int32
-    (row_ptr [nb+1], col_idx [nnz]) on the keys' device, plus the fp64 salience
-    [nb] when ``return_salience``.  Waits for the stream to read back nnz.
+    (row_ptr [nb+1], col_idx [nnz]) on the keys' device, nb = ceil(S / block),
+    plus the fp64 salience [nb] when ``return_salience``.  Waits for the stream
+    to read back nnz.  block: a multiple of 64; schedules over blocks larger than
+    64 reach the attention entry points through ``refine_schedule``.
     per_row: each row takes its own top-k among its blocks j <= i instead of
     one global top-k set (TSA_TOPK_PER_ROW).
     """
@@ -180,7 +189,7 @@ def build_schedule(keys: torch.Tensor, block: int = BLOCK, sink: int = 1, local_
     code = _dtype_code(keys, "keys")
     S, D = keys.shape
     dev = keys.device
-    nb = -(-S // BLOCK)
+    nb = -(-S // block) if block > 0 else 0  # the library rejects unsupported blocks
     cap = schedule_max_nnz(nb, sink, local_radius, topk) if min(sink, local_radius, topk) >= 0 else 0
     ws_bytes = _lib.tsa_build_schedule_workspace_bytes(S, D, block)
     with torch.cuda.device(dev):
@@ -212,13 +221,14 @@ class ScheduleBuffers:
     """
 
     def __init__(self, S: int, D: int, sink: int, local_radius: int, topk: int, device,
-                 salience: bool = False, per_row: bool = False):
+                 salience: bool = False, per_row: bool = False, block: int = BLOCK):
         dev = torch.device(device)
         self.S, self.D, self.sink, self.local_radius, self.topk = S, D, sink, local_radius, topk
         self.per_row = per_row
-        self.nb = -(-S // BLOCK)
+        self.block = block
+        self.nb = -(-S // block)
         self.capacity = schedule_max_nnz(self.nb, sink, local_radius, topk)
-        self.ws_bytes = int(_lib.tsa_build_schedule_workspace_bytes(S, D, BLOCK))
+        self.ws_bytes = int(_lib.tsa_build_schedule_workspace_bytes(S, D, block))
         if self.ws_bytes == 0 and self.nb > 0:
             _check(-2, "ScheduleBuffers: unsupported size")
         self.row_ptr = torch.empty(self.nb + 1, dtype=torch.int32, device=dev)
@@ -241,12 +251,35 @@ def build_schedule_into(keys: torch.Tensor, bufs: ScheduleBuffers) -> None:
     code = _dtype_code(keys, "keys")
     with torch.cuda.device(keys.device):
         status = _lib.tsa_build_schedule_ex(
-            _ptr(keys), code, bufs.S, bufs.D, BLOCK, bufs.sink, bufs.local_radius, bufs.topk,
+            _ptr(keys), code, bufs.S, bufs.D, bufs.block, bufs.sink, bufs.local_radius, bufs.topk,
             1 if bufs.per_row else 0, _ptr(bufs.row_ptr), _ptr(bufs.col_idx), bufs.capacity,
             _ptr(bufs.salience), ctypes.c_void_p(bufs.ws_ptr), bufs.ws_bytes, None,
             _stream(keys.device),
         )
     _check(status, "build_schedule_into")
+
+
+def refine_schedule(row_ptr: torch.Tensor, col_idx: torch.Tensor, S: int, block: int):
+    """The CSR over 64-row blocks that allows exactly the keys the CSR over blocks
+    of ``block`` rows allows (tsa_refine_schedule), for the attention entry
+    points.  Returns int32 (row_ptr [ceil(S/64)+1], col_idx); waits for the
+    stream to read back the entry count."""
+    dev = row_ptr.device
+    _check_index("row_ptr", row_ptr, dev)
+    _check_index("col_idx", col_idx, dev)
+    nnz = col_idx.numel()
+    cap = int(_lib.tsa_refine_schedule_max_nnz(S, block, nnz))
+    if cap < 0:
+        _check(-1, "refine_schedule")
+    nb64 = -(-S // BLOCK)
+    with torch.cuda.device(dev):
+        rp = torch.empty(nb64 + 1, dtype=torch.int32, device=dev)
+        ci = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+        total = ctypes.c_int64(0)
+        status = _lib.tsa_refine_schedule(S, block, _ptr(row_ptr), _ptr(col_idx), nnz, _ptr(rp), _ptr(ci),
+                                          cap, ctypes.byref(total), _stream(dev))
+    _check(status, "refine_schedule")
+    return rp, ci[: total.value]
 
 
 def dense_causal_schedule(nb: int, device) -> tuple[torch.Tensor, torch.Tensor]:

@@ -45,11 +45,17 @@ struct ScheduleWorkspace {
 };
 constexpr int kLdsDistBlocks = 128;  // distance matrix kept in LDS up to this many blocks
 size_t schedule_workspace_bytes(int64_t nb, int64_t D);
-hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t D, int sink,
-                                 int local_radius, int topk, bool per_row, int32_t* row_ptr,
-                                 int32_t* col_idx, int64_t col_capacity, double* salience,
-                                 void* workspace,
-                                 hipStream_t stream);
+// block: rows per key block, a positive multiple of 64; nb = ceil(S / block).
+hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t D, int block,
+                                 int sink, int local_radius, int topk, bool per_row,
+                                 int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                 double* salience, void* workspace, hipStream_t stream);
+
+// Refinement of a CSR over blocks of `block` rows (a multiple of 64) to the CSR
+// over 64-row blocks that allows exactly the same keys (see schedule_refine.hip).
+hipError_t launch_refine_schedule(int64_t S, int block, const int32_t* row_ptr,
+                                  const int32_t* col_idx, int64_t nnz, int32_t* row_ptr64,
+                                  int32_t* col_idx64, hipStream_t stream);
 
 hipError_t launch_dense_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,
                                  hipStream_t stream);

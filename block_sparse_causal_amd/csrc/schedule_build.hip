@@ -358,14 +358,14 @@ __device__ void select_and_emit(const double* sal, int nb, int sink, int local_r
 // cent_t[d * nbe + j].  When `comp` is given, the larger-schedule
 // state is reset too: comp[j] = j, and counters {edges, done} = 0.
 __global__ __launch_bounds__(256) void centroid_kernel(const uint16_t* __restrict__ keys, bool bf16,
-                                                       int64_t S, int64_t D, int nb,
+                                                       int64_t S, int64_t D, int nb, int block,
                                                        double* __restrict__ cent_t,
                                                        int* __restrict__ comp,
                                                        int* __restrict__ counters) {
   __shared__ double part[32][65];
   const int64_t j = blockIdx.x;
-  const int64_t r0 = j * kBlock;
-  const int rows = (int)((r0 + kBlock < S) ? kBlock : S - r0);
+  const int64_t r0 = j * block;
+  const int rows = (int)((r0 + block < S) ? block : S - r0);
   const int tid = threadIdx.x, rg = tid >> 3, ch = tid & 7;
   const bool vec = (D % 8) == 0 && ((uintptr_t)keys % 16) == 0;  // 16-byte aligned rows
   for (int64_t d0 = 0; d0 < D; d0 += 64) {
@@ -928,7 +928,7 @@ __host__ __device__ constexpr size_t small_lds_bytes(int nb) {
 // flags hold older tokens.  flags: small_tile_count + 1 words of workspace.
 template <int SLOTS, int TILE, bool BF16>
 __global__ __launch_bounds__(kSmallThreads) void schedule_small(
-    const uint16_t* __restrict__ keys, int64_t S, int64_t D, int nb,
+    const uint16_t* __restrict__ keys, int64_t S, int64_t D, int nb, int block,
     double* dist_g, unsigned long long* flags, unsigned long long token, int sink,
     int local_radius, int topk, int per_row, int32_t* __restrict__ row_ptr,
     int32_t* __restrict__ col_idx, int64_t col_capacity,
@@ -953,49 +953,55 @@ __global__ __launch_bounds__(kSmallThreads) void schedule_small(
   // a diagonal tile's columns are its rows.
   auto slot_block = [&](int q) { return q < TILE ? ti * TILE + q : tj * TILE + (q - TILE); };
   auto block_rows = [&](int blk) -> int {
-    const int64_t r0 = (int64_t)blk * kBlock;
-    return blk < nb ? (int)(r0 + kBlock < S ? kBlock : S - r0) : 0;
+    const int64_t r0 = (int64_t)blk * block;
+    return blk < nb ? (int)(r0 + block < S ? block : S - r0) : 0;
   };
   {
     double* part = smem;                                     // [row group][slot][dim]
     double* ct = smem + kGroups * kSlots * kTileDims;        // [dim][16]
     const int c = tid & 7, g = (tid >> 3) % kGroups, q = tid / (8 * kGroups);  // 8 dims, group, slot
     const int blk = slot_block(q);
-    const int rows = (diag && q >= TILE) ? 0 : block_rows(blk);
+    const int rows_blk = (diag && q >= TILE) ? 0 : block_rows(blk);
     const int rlo = kRowsPer * g;
-    const uint16_t* kb = keys + (int64_t)blk * kBlock * D;
+    const uint16_t* kb_blk = keys + (int64_t)blk * block * D;
     const bool vec = (D % 8) == 0 && ((uintptr_t)keys % 16) == 0;  // 16-byte aligned rows
     double acc = 0.0;  // distance (ti*TILE + tid/TILE, tj*TILE + tid%TILE) for tid < TILE^2
     for (int64_t d0 = 0; d0 < D; d0 += kTileDims) {
       double sum8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       const int64_t dc = d0 + 8 * c;
-      if (rows > rlo && vec && dc + 8 <= D) {
-        // All rows of the group in flight at once (rows past the block's end
-        // re-read its last row and are not added).
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 x[kRowsPer];
+      // A block of `block` rows is walked in runs of kBlock rows; group g takes
+      // rows rlo .. rlo + kRowsPer - 1 of every run.
+      for (int run0 = 0; run0 < rows_blk; run0 += kBlock) {
+        const int rows = rows_blk - run0 < kBlock ? rows_blk - run0 : kBlock;
+        const uint16_t* kb = kb_blk + (int64_t)run0 * D;
+        if (rows > rlo && vec && dc + 8 <= D) {
+          // All rows of the group in flight at once (rows past the block's end
+          // re-read its last row and are not added).
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          u32x4 x[kRowsPer];
 #pragma unroll
-        for (int u = 0; u < kRowsPer; ++u) {
-          const int r = rlo + u < rows ? rlo + u : rows - 1;
-          x[u] = *(const u32x4*)(kb + (int64_t)r * D + dc);
-        }
+          for (int u = 0; u < kRowsPer; ++u) {
+            const int r = rlo + u < rows ? rlo + u : rows - 1;
+            x[u] = *(const u32x4*)(kb + (int64_t)r * D + dc);
+          }
 #pragma unroll
-        for (int u = 0; u < kRowsPer; ++u) {
-          if (rlo + u < rows) {
+          for (int u = 0; u < kRowsPer; ++u) {
+            if (rlo + u < rows) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              sum8[2 * e] += key_to_double((uint16_t)(x[u][e] & 0xffffu), BF16);
-              sum8[2 * e + 1] += key_to_double((uint16_t)(x[u][e] >> 16), BF16);
+              for (int e = 0; e < 4; ++e) {
+                sum8[2 * e] += key_to_double((uint16_t)(x[u][e] & 0xffffu), BF16);
+                sum8[2 * e + 1] += key_to_double((uint16_t)(x[u][e] >> 16), BF16);
+              }
             }
           }
-        }
-      } else if (rows > rlo) {
-        const int r1 = rows < rlo + kRowsPer ? rows : rlo + kRowsPer;
-        for (int r = rlo; r < r1; ++r) {
-          const uint16_t* row = kb + (int64_t)r * D;
+        } else if (rows > rlo) {
+          const int r1 = rows < rlo + kRowsPer ? rows : rlo + kRowsPer;
+          for (int r = rlo; r < r1; ++r) {
+            const uint16_t* row = kb + (int64_t)r * D;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (dc + e < D) sum8[e] += key_to_double(row[dc + e], BF16);
+            for (int e = 0; e < 8; ++e)
+              if (dc + e < D) sum8[e] += key_to_double(row[dc + e], BF16);
+          }
         }
       }
 #pragma unroll
@@ -1400,14 +1406,13 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 
 size_t schedule_workspace_bytes(int64_t nb, int64_t D) { return workspace_layout(nb, D).total; }
 
-hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t D, int sink,
-                                 int local_radius, int topk, bool per_row, int32_t* row_ptr,
-                                 int32_t* col_idx, int64_t col_capacity, double* salience,
-                                 void* workspace,
-                                 hipStream_t stream) {
-  const int64_t nb64 = (S + kBlock - 1) / kBlock;
-  if (nb64 == 0) return launch_dense_schedule(0, row_ptr, col_idx, stream);
-  const int nb = (int)nb64;
+hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t D, int block,
+                                 int sink, int local_radius, int topk, bool per_row,
+                                 int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                 double* salience, void* workspace, hipStream_t stream) {
+  const int64_t nbl = (S + block - 1) / block;
+  if (nbl == 0) return launch_dense_schedule(0, row_ptr, col_idx, stream);
+  const int nb = (int)nbl;
   const WorkspaceLayout L = workspace_layout(nb, D);
   char* ws = (char*)workspace;
   double* dist = (double*)(ws + L.dist);
@@ -1422,7 +1427,7 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
       hipError_t e = allow_lds(kernel, lds);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kernel, grid, dim3(kSmallThreads), lds, stream, (const uint16_t*)keys, S,
-                         D, nb, dist, flags, token, sink, local_radius, topk, (int)per_row,
+                         D, nb, block, dist, flags, token, sink, local_radius, topk, (int)per_row,
                          row_ptr, col_idx, col_capacity, salience);
       return hipGetLastError();
     };
@@ -1440,7 +1445,7 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
   int* comp = (int*)(ws + L.comp);
   int* state = (int*)(ws + L.state);
   hipLaunchKernelGGL(centroid_kernel, dim3((unsigned)nb), dim3(256), 0, stream,
-                     (const uint16_t*)keys, bf16, S, D, nb, cent_t, comp, state);
+                     (const uint16_t*)keys, bf16, S, D, nb, block, cent_t, comp, state);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const unsigned tiles = (unsigned)((nb + kDistTile - 1) / kDistTile);
   hipLaunchKernelGGL(distance_kernel, dim3(tiles, tiles), dim3(256), 0, stream, cent_t, nb, D,

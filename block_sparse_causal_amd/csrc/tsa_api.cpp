@@ -54,6 +54,11 @@ int check_device_ptr(const void* p, const char* name) {
   return TSA_OK;
 }
 
+// Block sizes the schedule builder and the refinement accept.
+bool block_ok(int32_t block) {
+  return block >= TSA_BLOCK && block <= TSA_MAX_SCHEDULE_BLOCK && block % TSA_BLOCK == 0;
+}
+
 int64_t row_cap(int32_t sink, int32_t local_radius, int32_t topk) {
   return (int64_t)sink + (int64_t)local_radius + 1 + (int64_t)topk;
 }
@@ -143,8 +148,8 @@ int64_t tsa_schedule_max_nnz(int64_t nb, int32_t sink, int32_t local_radius, int
 }
 
 size_t tsa_build_schedule_workspace_bytes(int64_t S, int64_t D, int32_t block) {
-  if (S < 0 || D <= 0 || block != TSA_BLOCK) return 0;
-  const int64_t nb = (S + TSA_BLOCK - 1) / TSA_BLOCK;
+  if (S < 0 || D <= 0 || !block_ok(block)) return 0;
+  const int64_t nb = (S + block - 1) / block;
   if (nb > TSA_MAX_SCHEDULE_BLOCKS) return 0;
   return tsa::schedule_workspace_bytes(nb, D) + 256;
 }
@@ -176,10 +181,11 @@ int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D,
     return fail(TSA_ERR_INVALID_ARG,
                 "tsa_build_schedule: sink, local_radius and topk must be >= 0 (%d, %d, %d)", sink,
                 local_radius, topk);
-  if (block != TSA_BLOCK)
-    return fail(TSA_ERR_UNSUPPORTED, "tsa_build_schedule: block must be %d, got %d", TSA_BLOCK,
-                block);
-  const int64_t nb = (S + TSA_BLOCK - 1) / TSA_BLOCK;
+  if (!block_ok(block))
+    return fail(TSA_ERR_UNSUPPORTED,
+                "tsa_build_schedule: block must be a multiple of %d up to %d, got %d", TSA_BLOCK,
+                TSA_MAX_SCHEDULE_BLOCK, block);
+  const int64_t nb = (S + block - 1) / block;
   if (nb > TSA_MAX_SCHEDULE_BLOCKS)
     return fail(TSA_ERR_UNSUPPORTED, "tsa_build_schedule: %lld blocks exceed the limit of %d",
                 (long long)nb, TSA_MAX_SCHEDULE_BLOCKS);
@@ -213,9 +219,9 @@ int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D,
     if (salience && (rc = check_device_ptr(salience, "salience")) != TSA_OK) return rc;
   }
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = tsa::launch_build_schedule(keys, dtype == TSA_BF16, S, D, sink, local_radius, topk,
-                                            topk_scope == TSA_TOPK_PER_ROW,
-                                            row_ptr, col_idx, col_capacity, salience, workspace, st);
+  hipError_t e = tsa::launch_build_schedule(keys, dtype == TSA_BF16, S, D, block, sink, local_radius,
+                                            topk, topk_scope == TSA_TOPK_PER_ROW, row_ptr, col_idx,
+                                            col_capacity, salience, workspace, st);
   if (e != hipSuccess) return hip_fail(e, "schedule kernels");
   if (nnz_host) {
     int32_t n = 0;
@@ -292,6 +298,56 @@ int tsa_scheduled_attention_fwd_lse(const void* q, const void* k, const void* v,
                                     int64_t nnz, int32_t block, float sm_scale, void* stream) {
   return attention_fwd("tsa_scheduled_attention_fwd_lse", q, k, v, out, lse, true, dtype, B, H, S, D,
                        row_ptr, col_idx, nnz, block, sm_scale, stream);
+}
+
+int64_t tsa_refine_schedule_max_nnz(int64_t S, int32_t block, int64_t nnz) {
+  if (S < 0 || nnz < 0 || !block_ok(block)) {
+    fail(TSA_ERR_INVALID_ARG, "tsa_refine_schedule_max_nnz: need S, nnz >= 0 and a valid block");
+    return -1;
+  }
+  const int64_t m = block / TSA_BLOCK, nb64 = (S + TSA_BLOCK - 1) / TSA_BLOCK;
+  const int64_t tri = nb64 * (nb64 + 1) / 2;
+  return nnz > tri / (m * m) ? tri : nnz * m * m;
+}
+
+int tsa_refine_schedule(int64_t S, int32_t block, const int32_t* row_ptr, const int32_t* col_idx,
+                        int64_t nnz, int32_t* row_ptr64, int32_t* col_idx64, int64_t capacity,
+                        int64_t* nnz_host, void* stream) {
+  const char* fn = "tsa_refine_schedule";
+  if (S < 0 || nnz < 0 || capacity < 0)
+    return fail(TSA_ERR_INVALID_ARG, "%s: S, nnz and capacity must be >= 0", fn);
+  if (!block_ok(block))
+    return fail(TSA_ERR_UNSUPPORTED, "%s: block must be a multiple of %d up to %d, got %d", fn,
+                TSA_BLOCK, TSA_MAX_SCHEDULE_BLOCK, block);
+  const int64_t nb64 = (S + TSA_BLOCK - 1) / TSA_BLOCK;
+  if (nb64 > TSA_MAX_REFINED_BLOCKS)
+    return fail(TSA_ERR_UNSUPPORTED, "%s: %lld 64-row blocks exceed the limit of %d", fn,
+                (long long)nb64, TSA_MAX_REFINED_BLOCKS);
+  const int64_t need = tsa_refine_schedule_max_nnz(S, block, nnz);
+  if (need > INT32_MAX)
+    return fail(TSA_ERR_SHAPE, "%s: the refined schedule may exceed int32 offsets", fn);
+  if (capacity < need)
+    return fail(TSA_ERR_SCHEDULE, "%s: capacity %lld < tsa_refine_schedule_max_nnz = %lld", fn,
+                (long long)capacity, (long long)need);
+  if (row_ptr == nullptr || row_ptr64 == nullptr || (nnz > 0 && col_idx == nullptr) ||
+      (need > 0 && col_idx64 == nullptr))
+    return fail(TSA_ERR_INVALID_ARG, "%s: NULL pointer argument", fn);
+  int rc;
+  if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
+  if ((rc = check_device_ptr(row_ptr64, "row_ptr64")) != TSA_OK) return rc;
+  if (nnz > 0 && (rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
+  if (need > 0 && (rc = check_device_ptr(col_idx64, "col_idx64")) != TSA_OK) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = tsa::launch_refine_schedule(S, block, row_ptr, col_idx, nnz, row_ptr64, col_idx64, st);
+  if (e != hipSuccess) return hip_fail(e, "refine kernels");
+  if (nnz_host) {
+    int32_t n = 0;
+    e = hipMemcpyAsync(&n, row_ptr64 + nb64, sizeof n, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "reading nnz");
+    *nnz_host = n;
+  }
+  return ok();
 }
 
 size_t tsa_schedule_transpose_workspace_bytes(int64_t nb) {

@@ -59,10 +59,15 @@ extern "C" {
 #define TSA_F16 0
 #define TSA_BF16 1
 
-/* The only supported block size (rows per query block and per key block). */
+/* Block size of the attention kernels (rows per query block and per key block).
+ * The schedule builder and tsa_refine_schedule also take schedules over blocks of
+ * any multiple of it up to TSA_MAX_SCHEDULE_BLOCK rows. */
 #define TSA_BLOCK 64
-/* Largest number of key blocks the schedule builder accepts (S <= 262144). */
+#define TSA_MAX_SCHEDULE_BLOCK 4096
+/* Largest number of key blocks the schedule builder accepts (S <= 262144 at block 64). */
 #define TSA_MAX_SCHEDULE_BLOCKS 4096
+/* Largest number of 64-row blocks tsa_refine_schedule emits (S <= 2^28). */
+#define TSA_MAX_REFINED_BLOCKS (1 << 22)
 
 /* Library version, e.g. 100 for 0.1.0. */
 int tsa_version(void);
@@ -91,8 +96,10 @@ size_t tsa_build_schedule_workspace_bytes(int64_t S, int64_t D, int32_t block);
  *
  *   keys        device, [S, D] of `dtype` (TSA_F16 / TSA_BF16), row-major.
  *               For [B, H, S, D] inputs pass lane (0, 0).
- *   block       must be 64.  nb = ceil(S / 64); a partial last block's centroid
- *               is the mean of its valid rows.
+ *   block       rows per block: a multiple of 64 up to TSA_MAX_SCHEDULE_BLOCK.
+ *               nb = ceil(S / block); a partial last block's centroid is the mean
+ *               of its valid rows.  A schedule over blocks larger than 64 is
+ *               handed to the attention entry points through tsa_refine_schedule.
  *   sink, local_radius, topk   >= 0.  Row i lists every block j <= i with
  *               j < sink, or j >= i - local_radius, or j among the topk blocks
  *               of highest salience (ties: lower index; topk >= nb: all).
@@ -148,6 +155,40 @@ int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D,
                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                           double* salience, void* workspace, size_t workspace_bytes,
                           int64_t* nnz_host, void* stream);
+
+/*
+ * Upper bound on the entries of tsa_refine_schedule's output: min(m^2 nnz,
+ * n(n+1)/2) with m = block / 64 and n = ceil(S / 64).  Host-only; -1 for negative
+ * sizes or an unsupported block.
+ */
+int64_t tsa_refine_schedule_max_nnz(int64_t S, int32_t block, int64_t nnz);
+
+/*
+ * The CSR over 64-row blocks that allows exactly the keys a CSR over blocks of
+ * `block` rows allows, for the attention entry points, which work on 64-row
+ * blocks.  (PR page, Summary, fifth bullet: a schedule's block size is validated;
+ * the Local benchmark uses 64.)  With m = block / 64 and I = i / m, row i of the
+ * output lists m*J + b (b = 0..m-1, m*J + b <= i) for every block J that row I
+ * of the input lists, ascending; query t then sees key u <= t exactly when
+ * u / block is listed in row t / block.  An input entry counts when the attention
+ * kernels would accept it (within 0..I and above every earlier entry of its row
+ * that lies in 0..I).
+ *   S           sequence length; the input has ceil(S / block) rows, the output
+ *               ceil(S / 64) <= TSA_MAX_REFINED_BLOCKS.
+ *   row_ptr, col_idx   device int32 input CSR, `nnz` readable entries.
+ *   row_ptr64   device int32 [ceil(S / 64) + 1], written.
+ *   col_idx64   device int32 [capacity], entries [0, row_ptr64[n]) written;
+ *               capacity >= tsa_refine_schedule_max_nnz(S, block, nnz).
+ *   nnz_host    host int64 or NULL: when not NULL the call waits for the stream
+ *               and stores the output's entry count there.
+ * block = 64 returns the input's accepted entries unchanged.  Errors: negative
+ * sizes (TSA_ERR_INVALID_ARG), an unsupported block or too many output rows
+ * (TSA_ERR_UNSUPPORTED), more entries than int32 offsets hold (TSA_ERR_SHAPE), a
+ * short capacity (TSA_ERR_SCHEDULE), NULL or non-device pointers.
+ */
+int tsa_refine_schedule(int64_t S, int32_t block, const int32_t* row_ptr, const int32_t* col_idx,
+                        int64_t nnz, int32_t* row_ptr64, int32_t* col_idx64, int64_t capacity,
+                        int64_t* nnz_host, void* stream);
 
 /*
  * The dense causal (lower-triangular) CSR for nb blocks: row i lists 0..i.

@@ -36,6 +36,7 @@ from .schedule import (
     fixed_segment_schedule,
     csr_to_block_sets,
     transpose_schedule,
+    refine_schedule,
 )
 from .attention import allowed_key_mask, masked_attention, masked_attention_rows
 from .attention_grad import masked_lse, attention_backward, attention_backward_rows
@@ -51,6 +52,7 @@ __all__ = [
     "fixed_segment_schedule",
     "csr_to_block_sets",
     "transpose_schedule",
+    "refine_schedule",
     "allowed_key_mask",
     "masked_attention",
     "masked_attention_rows",

@@ -235,3 +235,24 @@ def transpose_schedule(row_ptr, col_idx) -> tuple[np.ndarray, np.ndarray]:
     nb = len(sets)
     cols = [[i for i in range(nb) if j in sets[i] and j <= i] for j in range(nb)]
     return _csr_from_rows(cols)
+
+
+def refine_schedule(row_ptr, col_idx, S: int, block: int) -> tuple[np.ndarray, np.ndarray]:
+    """The CSR over 64-row blocks that allows exactly the keys a CSR over blocks
+    of ``block`` rows allows.
+
+    The pages validate a schedule's block size (PR page, Summary, fifth bullet)
+    and benchmark at 64.  With m = block / 64, fine row i lists block c exactly
+    when coarse row i // m lists c // m and c <= i; listed coarse blocks outside
+    0..i // m select no keys.  Returns int32 (row_ptr [ceil(S/64)+1], col_idx).
+    """
+    if block < 64 or block % 64:
+        raise ValueError("block must be a positive multiple of 64")
+    m = block // 64
+    sets = csr_to_block_sets(row_ptr, col_idx)
+    nb64 = -(-S // 64)
+    rows = []
+    for i in range(nb64):
+        I = i // m
+        rows.append([c for c in range(i + 1) if (c // m) in sets[I] and c // m <= I])
+    return _csr_from_rows(rows)

@@ -159,7 +159,8 @@ def test_builder_argument_checks_before_gpu(lib):
     assert call(dtype=3) == -1
     assert call(S=-1) == -1
     assert call(s=-2) == -1
-    assert call(block=128) == -2
+    assert call(block=96) == -2  # not a multiple of 64
+    assert call(block=128) == -1  # a valid block; the NULL row_ptr is what fails
     assert call(S=64 * 4097) == -2
     assert call() == -1  # NULL row_ptr
     assert b"row_ptr" in lib.tsa_last_error()
@@ -254,3 +255,39 @@ def test_backward_workspace_and_checks_before_gpu(lib):
     assert _bwd(lib, **{**good, "ws": base + 5 * mb + 16}) == -1  # workspace overlaps lse
     assert _bwd(lib, **{**good, "dk": base + 7 * mb + 8}) == -1  # misaligned
     assert b"aligned" in lib.tsa_last_error()
+
+
+def test_block_sizes_accepted_by_builder_and_refinement(lib):
+    vp = ctypes.c_void_p
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 128) > 0
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 4096) > 0
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 96) == 0
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 8192) == 0
+    # block 96 is not a multiple of 64: unsupported before any GPU call
+    assert lib.tsa_build_schedule(vp(None), 0, 4096, 64, 96, 1, 1, 2, vp(None), vp(None), 1000, vp(None),
+                                  vp(None), 1 << 20, None, vp(None)) == -2
+    # block 128 at S = 128 * 4097 blocks exceeds the builder's limit
+    assert lib.tsa_build_schedule(vp(None), 0, 128 * 4097, 64, 128, 1, 1, 2, vp(None), vp(None), 1 << 30,
+                                  vp(None), vp(None), 1 << 20, None, vp(None)) == -2
+
+
+@pytest.mark.parametrize("S,block,nnz", [(4096, 128, 100), (4096, 256, 10), (1000, 128, 0), (4096, 128, 10**6),
+                                         (0, 128, 5), (64 * 100, 64, 50)])
+def test_refine_max_nnz(lib, S, block, nnz):
+    m, nb64 = block // 64, -(-S // 64)
+    assert lib.tsa_refine_schedule_max_nnz(S, block, nnz) == min(m * m * nnz, nb64 * (nb64 + 1) // 2)
+
+
+def test_refine_checks_before_gpu(lib):
+    vp = ctypes.c_void_p
+    assert lib.tsa_refine_schedule_max_nnz(100, 96, 5) == -1
+    assert lib.tsa_refine_schedule_max_nnz(-1, 128, 5) == -1
+
+    def call(S=1024, block=128, nnz=10, cap=40, rp=None, ci=None, rp64=None, ci64=None):
+        return lib.tsa_refine_schedule(S, block, vp(rp), vp(ci), nnz, vp(rp64), vp(ci64), cap, None, vp(None))
+
+    assert call(S=-1) == -1
+    assert call(block=96) == -2
+    assert call(S=64 * ((1 << 22) + 1), nnz=0, cap=0) == -2
+    assert call(cap=39) == -4 and b"capacity" in lib.tsa_last_error()
+    assert call() == -1 and b"NULL" in lib.tsa_last_error()
