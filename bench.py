@@ -266,6 +266,47 @@ def main() -> int:
         seg_ms = d0.elapsed_time(d1) / reps
         seg = {"segment_tokens": 512, "nnz_blocks": seg_nnz, "ms": round(seg_ms, 5),
                "tflops": round(lanes * seg_nnz * 4 * 64 * 64 * w.D / (seg_ms * 1e-3) / 1e12, 3)}
+    # The same workload with a schedule over 128-row blocks (sink, window and top-k
+    # taken at the same token counts, rounded up), refined to the 64-row CSR the
+    # attention kernel takes: builder, refinement and attention, timed the same way.
+    coarse = None
+    if not w.dense:
+        cb = 128
+        csink, crad, ctop = -(-w.sink // 2), -(-w.local_radius // 2), max(1, w.topk // 2)
+        cbufs = tsa.ScheduleBuffers(w.S, w.D, csink, crad, ctop, dev, block=cb)
+        for _ in range(3):
+            tsa.build_schedule_into(keys, cbufs)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for _ in range(reps):
+            tsa.build_schedule_into(keys, cbufs)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        c_build_ms = d0.elapsed_time(d1) / reps
+        c_nnz = int(cbufs.row_ptr[-1].item())
+        crp, cci = tsa.refine_schedule(cbufs.row_ptr, cbufs.col_idx[:c_nnz], w.S, cb)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for _ in range(reps):
+            tsa.refine_schedule(cbufs.row_ptr, cbufs.col_idx[:c_nnz], w.S, cb)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        c_refine_ms = d0.elapsed_time(d1) / reps
+        f_nnz = int(cci.shape[0])
+        for _ in range(3):
+            tsa.scheduled_attention(q, k, v, crp, cci, out=out)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for _ in range(reps):
+            tsa.scheduled_attention(q, k, v, crp, cci, out=out)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        c_ms = d0.elapsed_time(d1) / reps
+        coarse = {"block": cb, "sink": csink, "local_radius": crad, "topk": ctop, "nnz_blocks": c_nnz,
+                  "nnz_blocks_64": f_nnz, "builder_ms": round(c_build_ms, 5),
+                  "refine_ms": round(c_refine_ms, 5), "refine_note": "host-synchronising call (reads nnz)",
+                  "attention_ms": round(c_ms, 5),
+                  "attention_tflops": round(lanes * f_nnz * 4 * 64 * 64 * w.D / (c_ms * 1e-3) / 1e12, 3)}
     # Backward pass over the same schedule: the forward with lse and the column
     # view once, then back-to-back backward calls (dq kernel, then dk/dv kernel).
     # Algorithmic work: 5 block products per visited block (S recomputed once, dP,
@@ -346,6 +387,7 @@ def main() -> int:
         "dense_csr_tflops": round(lanes * nnz_dense * 4 * 64 * 64 * w.D / (dense_ms * 1e-3) / 1e12, 3),
         "segment_csr": seg,
         "per_row_topk": per_row,
+        "block_128": coarse,
         "backward": backward,
         "roofline": {
             "bound": "mfma",
