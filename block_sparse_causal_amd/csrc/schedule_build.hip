@@ -144,14 +144,19 @@ __device__ __forceinline__ double read_lane(double v, int lane) {
 
 // Value of per-block register array `a` for block x (x uniform; block x lives
 // in lane x % 64, slot x / 64).
+// Every slot is read with readlane and the slot is chosen among the scalar
+// results: selecting among the VGPRs first lets the compiler turn the choice
+// into a dynamically indexed array, which it keeps in scratch memory.
 template <int SLOTS>
 __device__ __forceinline__ int block_value(const int (&a)[SLOTS], int x) {
-  const int s = x >> 6;
-  int val = a[0];
+  const int s = x >> 6, l = x & 63;
+  int val = read_lane(a[0], l);
 #pragma unroll
-  for (int k = 1; k < SLOTS; ++k)
-    if (s == k) val = a[k];
-  return read_lane(val, x & 63);
+  for (int k = 1; k < SLOTS; ++k) {
+    const int t = read_lane(a[k], l);
+    val = s == k ? t : val;
+  }
+  return val;
 }
 
 // ------------------------------------------------------------------ workgroup helpers
@@ -487,6 +492,44 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The elder rule of elder_ranks for the large path (nb <= 64 * SLOTS <= 512):
+// keys (size << 12) | (4095 - root), one vector register per lane holding its
+// SLOTS blocks' keys (a lookup then indexes it with the uniform slot).  Lane k
+// of each group of 64 edges records the block absorbed at edge base + k, and
+// the group's saliences (edge lengths) are stored to LDS after the group, so the
+// loop over edges waits for no memory access.  sal must hold zeros on entry
+// (the surviving root keeps its 0).  st / sd: tags and lengths, ascending.
+template <int SLOTS>
+__device__ __forceinline__ void elder_salience(const uint32_t* st, const double* sd, int ne,
+                                               double* sal) {
+  typedef uint32_t keys_t __attribute__((ext_vector_type(SLOTS)));
+  constexpr int kRootBits = 12;
+  constexpr uint32_t kRootMask = (1u << kRootBits) - 1u;
+  const int lane = threadIdx.x & 63;
+  keys_t ckey;
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) ckey[s] = (1u << kRootBits) | (kRootMask - (uint32_t)(lane + 64 * s));
+  for (int base = 0; base < ne; base += 64) {
+    const int r = base + lane;
+    const uint32_t tw = r < ne ? st[r] : 0u;
+    const double len = r < ne ? sd[r] : 0.0;
+    const int aw = (int)(tw >> 16), bw = (int)(tw & 0xffffu);
+    const int n = __builtin_amdgcn_readfirstlane(ne - base < 64 ? ne - base : 64);
+    int absorbed_at = -1;  // lane k: the block absorbed at edge base + k
+    for (int k = 0; k < n; ++k) {
+      const int a = read_lane(aw, k), b = read_lane(bw, k);
+      const uint32_t ka = (uint32_t)read_lane((int)ckey[a >> 6], a & 63);
+      const uint32_t kb = (uint32_t)read_lane((int)ckey[b >> 6], b & 63);
+      const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
+      const uint32_t grown = hi + (lo & ~kRootMask);
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) ckey[s] = (ckey[s] == ka || ckey[s] == kb) ? grown : ckey[s];
+      absorbed_at = lane == k ? (int)(kRootMask - (lo & kRootMask)) : absorbed_at;
+    }
+    if (absorbed_at >= 0) sal[absorbed_at] = len;
+  }
 }
 
 // Per-row top-k rows by one wavefront (nb <= 64 * SLOTS <= 128), from the exact
@@ -1273,8 +1316,9 @@ __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
   }
   __syncthreads();
 
-  // Elder rule: union-find in LDS, union by size with the elder tie rule; lanes
-  // 0 and 1 follow the parent chains of the two endpoints.
+  // Elder rule.  Up to 512 blocks: component keys in registers of one wavefront
+  // (elder_salience).  Beyond: union-find in LDS, union by size with the elder
+  // tie rule; lanes 0 and 1 follow the parent chains of the two endpoints.
   double* sal = R0;
   int* parent = R1;
   int* csize = R4;
@@ -1284,7 +1328,11 @@ __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
     csize[v] = 1;
   }
   __syncthreads();
-  if (tid < 64) {
+  if (nb <= 256) {
+    if (tid < 64) elder_salience<4>(st, sd, ne, sal);
+  } else if (nb <= 512) {
+    if (tid < 64) elder_salience<8>(st, sd, ne, sal);
+  } else if (tid < 64) {
     const int lane = tid;
     for (int base = 0; base < ne; base += 64) {
       const int r = base + lane;
