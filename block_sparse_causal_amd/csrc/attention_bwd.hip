@@ -65,7 +65,7 @@ __device__ __forceinline__ void fill_offsets(uint32_t (&off)[Geo<D>::kTileOps], 
     const int cc = chunk % (kBlock * G::kChunksPerRow);
     const int r = cc / G::kChunksPerRow, pc = cc % G::kChunksPerRow;
     const int row = (r & 32) | swap_bits23(r & 31);
-    off[op] = (uint32_t)(row * G::kRowBytes + 16 * (pc ^ (r & 7)));
+    off[op] = (uint32_t)(row * G::kRowBytes + 16 * (pc ^ (r & k_swizzle_mask<D>())));
   }
 }
 
@@ -84,7 +84,7 @@ template <int D>
 __device__ __forceinline__ uint32_t tr_read_addr(uint32_t base, int half, int g, int gi, int dt) {
   const int r0 = 32 * half + 4 * (g >> 1) + (gi >> 2);
   const int dchunk = 4 * dt + 2 * (g & 1) + ((gi & 3) >> 1);
-  return base + (uint32_t)(r0 * Geo<D>::kRowBytes + 16 * (dchunk ^ (r0 & 7)) + 8 * (gi & 1));
+  return base + (uint32_t)(r0 * Geo<D>::kRowBytes + 16 * (dchunk ^ (r0 & k_swizzle_mask<D>())) + 8 * (gi & 1));
 }
 
 // Issue the four transposing reads of one head-dim tile: block rows 16 gg + 8 h +
@@ -319,8 +319,11 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
   // Sum the two key halves: wave kh keeps tiles [kh, kh + 1) * kTilesD / 2 and
   // hands the others to its partner through LDS, then stores scale * sum.
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-  constexpr int kHalfTiles = kTilesD / 2;
-  constexpr int kSendStride = kHalfTiles * 16 + 4;
+  // Register groups of 4 (4 consecutive head dims each): kTilesD * 4 per lane.
+  // Wave kh keeps groups [kh, kh + 1) * kGroups / 2 and sends the others.
+  constexpr int kGroups = kTilesD * 4;
+  constexpr int kHalfGroups = kGroups / 2;
+  constexpr int kSendStride = kHalfGroups * 4 + 4;
   static_assert(4 * 64 * kSendStride * 4 <= 2 * kStageBytes, "merge area exceeds the ring");
   float* const xbase = (float*)&ring[0];
   typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -328,12 +331,11 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
     constexpr int KH = decltype(KHc)::value;
     float* send = xbase + ((qh * 2 + KH) * 64 + l) * kSendStride;
 #pragma unroll
-    for (int t = 0; t < kHalfTiles; ++t) {
-      constexpr int kSendBase = (1 - KH) * kHalfTiles;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *(f32x4*)(send + t * 16 + 4 * g4) = f32x4{acc[kSendBase + t][4 * g4], acc[kSendBase + t][4 * g4 + 1],
-                                                  acc[kSendBase + t][4 * g4 + 2], acc[kSendBase + t][4 * g4 + 3]};
+    for (int u = 0; u < kHalfGroups; ++u) {
+      constexpr int kSendBase = (1 - KH) * kHalfGroups;
+      const int gq = kSendBase + u;  // compile-time after unrolling
+      *(f32x4*)(send + 4 * u) = f32x4{acc[gq / 4][4 * (gq % 4)], acc[gq / 4][4 * (gq % 4) + 1],
+                                      acc[gq / 4][4 * (gq % 4) + 2], acc[gq / 4][4 * (gq % 4) + 3]};
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     ring_barrier();
@@ -341,19 +343,18 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
     if (qrow < S) {
       uint16_t* drow = dq + lane_off + (int64_t)qrow * D;
 #pragma unroll
-      for (int t = 0; t < kHalfTiles; ++t) {
-        constexpr int kKeepBase = KH * kHalfTiles;
+      for (int u = 0; u < kHalfGroups; ++u) {
+        constexpr int kKeepBase = KH * kHalfGroups;
+        const int gq = kKeepBase + u;
+        const f32x4 y = *(const f32x4*)(recv + 4 * u);
+        float x[4];
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const f32x4 y = *(const f32x4*)(recv + t * 16 + 4 * gg);
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = (acc[kKeepBase + t][4 * gg + e] + y[e]) * scale;
-          u32x2 val;
-          val[0] = E::pack(x[0], x[1]);
-          val[1] = E::pack(x[2], x[3]);
-          *(u32x2*)(drow + 32 * (kKeepBase + t) + 8 * gg + 4 * h) = val;
-        }
+        for (int e = 0; e < 4; ++e) x[e] = (acc[gq / 4][4 * (gq % 4) + e] + y[e]) * scale;
+        u32x2 val;
+        val[0] = E::pack(x[0], x[1]);
+        val[1] = E::pack(x[2], x[3]);
+        // group gq: tile gq / 4, register group gq % 4 -> dims 32 (gq / 4) + 8 (gq % 4) + 4h
+        *(u32x2*)(drow + 32 * (gq / 4) + 8 * (gq % 4) + 4 * h) = val;
       }
     }
   };
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
   constexpr int kStageBytes = 2 * kTileBytes + kStatBytes;  // [Q tile | dO tile | stats]
   constexpr int kFillOps = G::kTileOps + 1;
   // The ring, reused after the loop for the merge of the two query halves.
-  constexpr int kMergeBytes = 4 * 64 * (G::kTilesD * 16 + 4) * 4;
+  constexpr int kMergeBytes = 4 * 64 * (G::kTilesD * 16 + 4) * 4;  // 2 accumulators x half the groups
   constexpr int kRingBytes = 2 * kStageBytes > kMergeBytes ? 2 * kStageBytes : kMergeBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
 
@@ -552,27 +553,28 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
   // Sum the two query halves: wave qh keeps head-dim tiles [qh, qh + 1) *
   // kTilesD / 2 of dK and dV and hands the others to its partner.
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-  constexpr int kHalfTiles = kTilesD / 2;
-  constexpr int kSendStride = 2 * kHalfTiles * 16 + 4;
+  // Register groups of 4 head dims, kTilesD * 4 per accumulator; wave qh keeps
+  // groups [qh, qh + 1) * kGroups / 2 of dK and dV and sends the others.
+  constexpr int kGroups = kTilesD * 4;
+  constexpr int kHalfGroups = kGroups / 2;
+  constexpr int kSendStride = 2 * kHalfGroups * 4 + 4;
   static_assert(4 * 64 * kSendStride * 4 <= kRingBytes, "merge area exceeds the ring");
   float* const xbase = (float*)&ring[0];
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   auto merge = [&](auto QHc) {
     constexpr int QH = decltype(QHc)::value;
-    constexpr int kSendBase = (1 - QH) * kHalfTiles;
-    constexpr int kKeepBase = QH * kHalfTiles;
+    constexpr int kSendBase = (1 - QH) * kHalfGroups;
+    constexpr int kKeepBase = QH * kHalfGroups;
     float* send = xbase + ((kh * 2 + QH) * 64 + l) * kSendStride;
 #pragma unroll
-    for (int t = 0; t < kHalfTiles; ++t)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        *(f32x4*)(send + t * 16 + 4 * g4) =
-            f32x4{adk[kSendBase + t][4 * g4], adk[kSendBase + t][4 * g4 + 1],
-                  adk[kSendBase + t][4 * g4 + 2], adk[kSendBase + t][4 * g4 + 3]};
-        *(f32x4*)(send + (kHalfTiles + t) * 16 + 4 * g4) =
-            f32x4{adv[kSendBase + t][4 * g4], adv[kSendBase + t][4 * g4 + 1],
-                  adv[kSendBase + t][4 * g4 + 2], adv[kSendBase + t][4 * g4 + 3]};
-      }
+    for (int u = 0; u < kHalfGroups; ++u) {
+      const int gq = kSendBase + u;
+      *(f32x4*)(send + 4 * u) = f32x4{adk[gq / 4][4 * (gq % 4)], adk[gq / 4][4 * (gq % 4) + 1],
+                                      adk[gq / 4][4 * (gq % 4) + 2], adk[gq / 4][4 * (gq % 4) + 3]};
+      *(f32x4*)(send + 4 * (kHalfGroups + u)) =
+          f32x4{adv[gq / 4][4 * (gq % 4)], adv[gq / 4][4 * (gq % 4) + 1], adv[gq / 4][4 * (gq % 4) + 2],
+                adv[gq / 4][4 * (gq % 4) + 3]};
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     ring_barrier();
     const float* recv = xbase + ((kh * 2 + (1 - QH)) * 64 + l) * kSendStride;
@@ -580,21 +582,20 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
       uint16_t* krow_dk = dk + lane_off + (int64_t)krow * D;
       uint16_t* krow_dv = dv + lane_off + (int64_t)krow * D;
 #pragma unroll
-      for (int t = 0; t < kHalfTiles; ++t)
+      for (int u = 0; u < kHalfGroups; ++u) {
+        const int gq = kKeepBase + u;
+        const f32x4 yk = *(const f32x4*)(recv + 4 * u);
+        const f32x4 yv = *(const f32x4*)(recv + 4 * (kHalfGroups + u));
+        float xk[4], xv[4];
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const f32x4 yk = *(const f32x4*)(recv + t * 16 + 4 * gg);
-          const f32x4 yv = *(const f32x4*)(recv + (kHalfTiles + t) * 16 + 4 * gg);
-          float xk[4], xv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xk[e] = (adk[kKeepBase + t][4 * gg + e] + yk[e]) * scale;
-            xv[e] = adv[kKeepBase + t][4 * gg + e] + yv[e];
-          }
-          const int col = 32 * (kKeepBase + t) + 8 * gg + 4 * h;
-          *(u32x2*)(krow_dk + col) = u32x2{E::pack(xk[0], xk[1]), E::pack(xk[2], xk[3])};
-          *(u32x2*)(krow_dv + col) = u32x2{E::pack(xv[0], xv[1]), E::pack(xv[2], xv[3])};
+        for (int e = 0; e < 4; ++e) {
+          xk[e] = (adk[gq / 4][4 * (gq % 4) + e] + yk[e]) * scale;
+          xv[e] = adv[gq / 4][4 * (gq % 4) + e] + yv[e];
         }
+        const int col = 32 * (gq / 4) + 8 * (gq % 4) + 4 * h;
+        *(u32x2*)(krow_dk + col) = u32x2{E::pack(xk[0], xk[1]), E::pack(xk[2], xk[3])};
+        *(u32x2*)(krow_dv + col) = u32x2{E::pack(xv[0], xv[1]), E::pack(xv[2], xv[3])};
+      }
     }
   };
   if (qh == 0)
@@ -634,7 +635,9 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t stream) {
   if (a.D == 64) return a.bf16 ? launch_bwd_typed<64, true>(a, stream) : launch_bwd_typed<64, false>(a, stream);
-  return a.bf16 ? launch_bwd_typed<128, true>(a, stream) : launch_bwd_typed<128, false>(a, stream);
+  if (a.D == 128) return a.bf16 ? launch_bwd_typed<128, true>(a, stream) : launch_bwd_typed<128, false>(a, stream);
+  if (a.D == 32) return a.bf16 ? launch_bwd_typed<32, true>(a, stream) : launch_bwd_typed<32, false>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tsa

@@ -121,17 +121,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   u32x4 qop[kStepsD];
   {
     const uint16_t* qp = q + lane_off + (int64_t)qrow_c * D + 8 * h;
-    static_assert(kStepsD == 4 || kStepsD == 8, "head dim");
-    qop[0] = global_load_b128<0>(qp);
-    qop[1] = global_load_b128<32>(qp);
-    qop[2] = global_load_b128<64>(qp);
-    qop[3] = global_load_b128<96>(qp);
-    if constexpr (kStepsD == 8) {
-      qop[4] = global_load_b128<128>(qp);
-      qop[5] = global_load_b128<160>(qp);
-      qop[6] = global_load_b128<192>(qp);
-      qop[7] = global_load_b128<224>(qp);
-    }
+    load_row_operands<kStepsD>(qop, qp);
   }
 
   // Per-lane byte offset, inside a block's rows, of the 16 bytes each fill op
@@ -144,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     const int cc = is_v ? chunk - kBlock * kChunksPerRow : chunk;
     const int r = cc / kChunksPerRow, pc = cc % kChunksPerRow;
     const int key = is_v ? r : ((r & 32) | swap_bits23(r & 31));
-    const int c = is_v ? (pc ^ v_swizzle<D>(r)) : (pc ^ (r & 7));
+    const int c = is_v ? (pc ^ v_swizzle<D>(r)) : (pc ^ (r & k_swizzle_mask<D>()));
     fill_off[op] = (uint32_t)(key * kRowBytes + 16 * c);
   }
   // Queue the copy of K and V block j into one stage (no registers in between).
@@ -227,7 +217,11 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   }
 
   auto compute = [&](int j, auto T_c) {
-    constexpr int kStageOff = decltype(T_c)::value * 2 * kTileBytes;
+    // Stage offset: in the instructions' 16-bit offset field when it fits (D <= 128),
+    // else (D = 256, second stage at 64 KB) added to the lane addresses.
+    constexpr int kStageAll = decltype(T_c)::value * 2 * kTileBytes;
+    constexpr int kStageOff = kStageAll + 24 * kRowBytes < 65536 ? kStageAll : 0;
+    constexpr uint32_t kStageReg = (uint32_t)(kStageAll - kStageOff);
     // On the diagonal block the key half above the query half is fully masked.
     if (j == i && kh > qh) return;
     // S^T (32 keys of this half x 32 queries) = K . Q^T.
@@ -235,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     // compiler wait for the next block's in-flight copy into the other stage.
     u32x4 ka[kStepsD];
 #pragma unroll
-    for (int c = 0; c < kStepsD; ++c) ka[c] = lds_read_b128<kStageOff>(k_addr[c]);
+    for (int c = 0; c < kStepsD; ++c) ka[c] = lds_read_b128<kStageOff>(k_addr[c] + kStageReg);
     lds_wait_all(ka);
     f32x16 s = f32x16{};
 #pragma unroll
@@ -272,10 +266,11 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     u32x2 va[kTilesD * 4];
 #pragma unroll
     for (int dt = 0; dt < kTilesD; ++dt) {
-      va[dt * 4 + 0] = lds_read_tr16<kStageOff>(v_addr[dt]);
-      va[dt * 4 + 1] = lds_read_tr16<kStageOff + 4 * kRowBytes>(v_addr[dt]);
-      va[dt * 4 + 2] = lds_read_tr16<kStageOff + 16 * kRowBytes>(v_addr[dt]);
-      va[dt * 4 + 3] = lds_read_tr16<kStageOff + 20 * kRowBytes>(v_addr[dt]);
+      const uint32_t va_addr = v_addr[dt] + kStageReg;
+      va[dt * 4 + 0] = lds_read_tr16<kStageOff>(va_addr);
+      va[dt * 4 + 1] = lds_read_tr16<kStageOff + 4 * kRowBytes>(va_addr);
+      va[dt * 4 + 2] = lds_read_tr16<kStageOff + 16 * kRowBytes>(va_addr);
+      va[dt * 4 + 3] = lds_read_tr16<kStageOff + 20 * kRowBytes>(va_addr);
     }
     u32x4 pb[2];
 #pragma unroll
@@ -349,8 +344,11 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   // buffers are free here (every wave has passed the last barrier).
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no load of this wave outlives it (empty rows)
   const float l_half = sum_with_other_half(l_run);
+  // Wave kh keeps half of the O registers: whole tiles when there are two or more
+  // (kHalfTiles each), else (D = 32) register groups 2kh, 2kh + 1 of the one tile.
   constexpr int kHalfTiles = kTilesD / 2;
-  constexpr int kSendStride = kHalfTiles * 16 + 4;  // floats per lane (16-byte aligned, padded)
+  constexpr int kSendFloats = kTilesD >= 2 ? kHalfTiles * 16 : 8;
+  constexpr int kSendStride = kSendFloats + 4;  // floats per lane (16-byte aligned, padded)
   static_assert((4 * 64 * kSendStride + 2 * 2 * 2 * 64) * 4 <= kStages * 2 * kTileBytes,
                 "merge area exceeds the ring");
   float* const xbase = (float*)&stages[0][0];
@@ -361,14 +359,23 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   auto merge = [&](auto KHc) {
     constexpr int KH = decltype(KHc)::value;
     float* send = xbase + ((qh * 2 + KH) * 64 + l) * kSendStride;
+    if constexpr (kTilesD >= 2) {
 #pragma unroll
-    for (int t = 0; t < kHalfTiles; ++t) {
-      constexpr int kSendBase = (1 - KH) * kHalfTiles;  // tiles the partner keeps
+      for (int t = 0; t < kHalfTiles; ++t) {
+        constexpr int kSendBase = (1 - KH) * kHalfTiles;  // tiles the partner keeps
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *(f32x4*)(send + t * 16 + 4 * g4) =
-            f32x4{o[kSendBase + t][4 * g4], o[kSendBase + t][4 * g4 + 1],
-                  o[kSendBase + t][4 * g4 + 2], o[kSendBase + t][4 * g4 + 3]};
+        for (int g4 = 0; g4 < 4; ++g4)
+          *(f32x4*)(send + t * 16 + 4 * g4) =
+              f32x4{o[kSendBase + t][4 * g4], o[kSendBase + t][4 * g4 + 1],
+                    o[kSendBase + t][4 * g4 + 2], o[kSendBase + t][4 * g4 + 3]};
+      }
+    } else {
+#pragma unroll
+      for (int gl = 0; gl < 2; ++gl) {
+        constexpr int kSendGroup = 2 * (1 - KH);  // groups the partner keeps
+        *(f32x4*)(send + 4 * gl) = f32x4{o[0][4 * (kSendGroup + gl)], o[0][4 * (kSendGroup + gl) + 1],
+                                         o[0][4 * (kSendGroup + gl) + 2], o[0][4 * (kSendGroup + gl) + 3]};
+      }
     }
     mlbuf[((qh * 2 + KH) * 2 + 0) * 64 + l] = m_use;
     mlbuf[((qh * 2 + KH) * 2 + 1) * 64 + l] = l_half;
@@ -390,19 +397,34 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
           l_tot > 0.0f ? (m + __builtin_log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
     if (qrow < S) {
       uint16_t* orow = out + lane_off + (int64_t)qrow * D;
+      if constexpr (kTilesD >= 2) {
 #pragma unroll
-      for (int t = 0; t < kHalfTiles; ++t) {
-        constexpr int kKeepBase = KH * kHalfTiles;  // tiles this wave keeps
+        for (int t = 0; t < kHalfTiles; ++t) {
+          constexpr int kKeepBase = KH * kHalfTiles;  // tiles this wave keeps
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const f32x4 y = *(const f32x4*)(recv + t * 16 + 4 * gg);
+          for (int gg = 0; gg < 4; ++gg) {
+            const f32x4 y = *(const f32x4*)(recv + t * 16 + 4 * gg);
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = o[kKeepBase + t][4 * gg + e] * cs + y[e] * cp;
+            u32x2 val;
+            val[0] = E::pack(x[0], x[1]);
+            val[1] = E::pack(x[2], x[3]);
+            *(u32x2*)(orow + 32 * (kKeepBase + t) + 8 * gg + 4 * h) = val;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int gl = 0; gl < 2; ++gl) {
+          constexpr int kKeepGroup = 2 * KH;  // register groups this wave keeps
+          const f32x4 y = *(const f32x4*)(recv + 4 * gl);
           float x[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = o[kKeepBase + t][4 * gg + e] * cs + y[e] * cp;
+          for (int e = 0; e < 4; ++e) x[e] = o[0][4 * (kKeepGroup + gl) + e] * cs + y[e] * cp;
           u32x2 val;
           val[0] = E::pack(x[0], x[1]);
           val[1] = E::pack(x[2], x[3]);
-          *(u32x2*)(orow + 32 * (kKeepBase + t) + 8 * gg + 4 * h) = val;
+          *(u32x2*)(orow + 8 * (kKeepGroup + gl) + 4 * h) = val;
         }
       }
     }
@@ -438,12 +460,16 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
                                 bool bf16, int64_t lanes, int64_t S, int D, const int32_t* row_ptr,
                                 const int32_t* col_idx, int64_t nnz, float scale_log2,
                                 hipStream_t stream) {
-  if (D == 64) {
-    return bf16 ? launch_typed<64, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream)
-                : launch_typed<64, false>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream);
-  }
-  return bf16 ? launch_typed<128, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream)
-              : launch_typed<128, false>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream);
+#define TSA_FWD_CASE(DD)                                                                              \
+  if (D == DD)                                                                                      \
+    return bf16 ? launch_typed<DD, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream) \
+                : launch_typed<DD, false>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream);
+  TSA_FWD_CASE(64)
+  TSA_FWD_CASE(128)
+  TSA_FWD_CASE(32)
+  TSA_FWD_CASE(256)
+#undef TSA_FWD_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tsa

@@ -87,12 +87,21 @@ __device__ __forceinline__ int swap_bits23(int m) {
 // Byte offset, inside one tile, of the 16-byte chunk `c` (8 elements) of row `r`.
 // K rows use chunk ^ (r & 7); V rows use chunk ^ 2*t(r & 3), where t spreads the
 // four key rows that one transposing read touches over distinct bank groups.
+// The K-layout XOR mask: the chunk index is XORed with (r & mask), which must
+// stay below the row's chunk count (D / 8): 7 from D = 64 on, 3 at D = 32.
 template <int D>
-__device__ __forceinline__ int k_chunk_offset(int r, int c) {
-  return r * (D * 2) + 16 * (c ^ (r & 7));
+constexpr int k_swizzle_mask() {
+  return D >= 64 ? 7 : D / 8 - 1;
 }
 template <int D>
+__device__ __forceinline__ int k_chunk_offset(int r, int c) {
+  return r * (D * 2) + 16 * (c ^ (r & k_swizzle_mask<D>()));
+}
+// At D = 32 the four rows one transposing read touches already sit 64 bytes
+// apart, in distinct bank groups, so V rows are not swizzled.
+template <int D>
 __device__ __forceinline__ int v_swizzle(int r) {
+  if (D == 32) return 0;
   if (D == 64) return 2 * (r & 3);
   const int t = (0x6530 >> (4 * (r & 3))) & 0xF;  // 0, 3, 5, 6
   return 2 * t;
@@ -132,6 +141,15 @@ __device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
   u32x4 r;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOffset));
   return r;
+}
+// The B operands of one 32-query column: 16 bytes (dims 16c + 8h .. +7) for each
+// c < C from one row, through global_load_b128 at compile-time offsets.
+template <int C>
+__device__ __forceinline__ void load_row_operands(u32x4* dst, const uint16_t* p) {
+  if constexpr (C > 0) {
+    load_row_operands<C - 1>(dst, p);
+    dst[C - 1] = global_load_b128<32 * (C - 1)>(p);
+  }
 }
 // Wait for every outstanding LDS read of this wave; the values pass through the
 // asm statement so that no use of them can be scheduled above the wait.

@@ -65,16 +65,19 @@ int64_t row_cap(int32_t sink, int32_t local_radius, int32_t topk) {
 
 
 // Checks shared by the attention entry points (no GPU call); sets *lanes.
+// max_d: the largest head dim the entry point takes (256 forward, 128 backward);
+// the others are 32, 64 and 128.
 int check_attention_args(const char* fn, int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D,
-                         int64_t nnz, int32_t block, float sm_scale, int64_t* lanes) {
+                         int64_t nnz, int32_t block, float sm_scale, int64_t max_d, int64_t* lanes) {
   if (dtype != TSA_F16 && dtype != TSA_BF16)
     return fail(TSA_ERR_INVALID_ARG, "%s: dtype must be TSA_F16 or TSA_BF16", fn);
   if (B < 0 || H < 0 || S < 0 || nnz < 0)
     return fail(TSA_ERR_INVALID_ARG, "%s: B, H, S and nnz must be >= 0", fn);
   if (block != TSA_BLOCK)
     return fail(TSA_ERR_UNSUPPORTED, "%s: block must be %d, got %d", fn, TSA_BLOCK, block);
-  if (D != 64 && D != 128)
-    return fail(TSA_ERR_UNSUPPORTED, "%s: head dim must be 64 or 128, got %lld", fn, (long long)D);
+  if (!(D == 32 || D == 64 || D == 128 || D == 256) || D > max_d)
+    return fail(TSA_ERR_UNSUPPORTED, "%s: head dim must be 32, 64, 128%s, got %lld", fn,
+                max_d >= 256 ? " or 256" : "", (long long)D);
   if (std::isnan(sm_scale) || std::isinf(sm_scale))
     return fail(TSA_ERR_INVALID_ARG, "%s: sm_scale must be finite", fn);
   if (S > INT32_MAX - TSA_BLOCK) return fail(TSA_ERR_SHAPE, "%s: S=%lld too large", fn, (long long)S);
@@ -90,7 +93,7 @@ int attention_fwd(const char* fn, const void* q, const void* k, const void* v, v
                   bool lse_required, int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D, const int32_t* row_ptr,
                   const int32_t* col_idx, int64_t nnz, int32_t block, float sm_scale, void* stream) {
   int64_t lanes = 0;
-  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, &lanes);
+  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, 256, &lanes);
   if (rc != TSA_OK) return rc;
   if (lanes == 0 || S == 0) return ok();  // empty problem: nothing to read or write
   if (!q || !k || !v || !out || !row_ptr || (nnz > 0 && !col_idx) || (lse_required && !lse))
@@ -418,7 +421,7 @@ int tsa_scheduled_attention_bwd(const void* q, const void* k, const void* v, con
                                 size_t workspace_bytes, void* stream) {
   const char* fn = "tsa_scheduled_attention_bwd";
   int64_t lanes = 0;
-  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, &lanes);
+  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, 128, &lanes);
   if (rc != TSA_OK) return rc;
   if (nnz_t < 0) return fail(TSA_ERR_INVALID_ARG, "%s: nnz_t must be >= 0", fn);
   if (lanes == 0 || S == 0) return ok();

@@ -49,7 +49,7 @@ extern "C" {
 /* Status codes. */
 #define TSA_OK 0
 #define TSA_ERR_INVALID_ARG (-1) /* null pointer, negative size or parameter, bad dtype */
-#define TSA_ERR_UNSUPPORTED (-2) /* block != 64, head dim not 64/128, too many blocks */
+#define TSA_ERR_UNSUPPORTED (-2) /* unsupported block or head dim, too many blocks */
 #define TSA_ERR_SHAPE (-3)       /* sizes that overflow or do not fit together */
 #define TSA_ERR_SCHEDULE (-4)    /* CSR arguments inconsistent (nnz, capacity) */
 #define TSA_ERR_DEVICE (-5)      /* a pointer is not device memory of the current device */
@@ -229,7 +229,7 @@ int tsa_segment_schedule(int64_t nb, int32_t segment_blocks, int32_t* row_ptr, i
  *   q, k, v, out  device, [B, H, S, D] row-major of `dtype` (out has q's dtype).
  *                 [S, D] inputs are B = H = 1.  out must not overlap q, k, v; all four
  *                 must be 16-byte aligned.
- *   D             64 or 128.
+ *   D             32, 64, 128 or 256.
  *   row_ptr, col_idx  device int32 CSR with nb = ceil(S/64) rows; `nnz` is the
  *                 number of readable col_idx entries.  Row i must list key
  *                 blocks strictly ascending within 0..i.  For memory safety the
@@ -325,7 +325,7 @@ size_t tsa_scheduled_attention_bwd_workspace_bytes(int64_t B, int64_t H, int64_t
  *               column that are outside j..nb-1 or not above the previous accepted
  *               one; a column view that is not the CSR's transpose gives
  *               unspecified gradients (never an out-of-bounds access).
- *   block       must be 64;  D 64 or 128;  sm_scale as in the forward.
+ *   block       must be 64;  D 32, 64 or 128;  sm_scale as in the forward.
  *   dq, dk, dv  device, q's shape and dtype, written (rounded to nearest even).
  *   workspace   device, >= tsa_scheduled_attention_bwd_workspace_bytes(B, H, S)
  *               bytes, 16-byte aligned, any contents on entry; it holds each

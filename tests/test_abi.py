@@ -135,7 +135,10 @@ def test_attention_argument_checks_before_gpu(lib):
     assert _fwd(lib, B=-1) == -1
     assert _fwd(lib, block=32) == -2
     assert _fwd(lib, D=96) == -2
-    assert b"64 or 128" in lib.tsa_last_error()
+    assert b"32, 64, 128 or 256" in lib.tsa_last_error()
+    assert _fwd(lib, D=512) == -2
+    for d in (32, 256):
+        assert _fwd(lib, D=d) == -1  # a supported head dim: the NULL pointers are what fail
     assert _fwd(lib, scale=float("nan")) == -1
     assert _fwd(lib) == -1  # NULL pointers for a non-empty problem
     assert _fwd(lib, S=0) == 0  # empty problem is a no-op
@@ -236,6 +239,8 @@ def test_backward_workspace_and_checks_before_gpu(lib):
     assert lib.tsa_scheduled_attention_bwd_workspace_bytes(1, 1, 1 << 62) == 0
     assert _bwd(lib, dtype=7) == -1
     assert _bwd(lib, D=96) == -2
+    assert _bwd(lib, D=256) == -2  # the backward takes 32, 64 and 128
+    assert _bwd(lib, D=32) == -1
     assert _bwd(lib, block=128) == -2
     assert _bwd(lib, nnz_t=-1) == -1
     assert _bwd(lib, scale=float("inf")) == -1
