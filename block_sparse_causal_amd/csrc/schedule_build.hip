@@ -961,18 +961,22 @@ __host__ __device__ constexpr size_t small_lds_bytes(int nb) {
 // order.  Each distance is formed once and stored at (i, j) and (j, i).
 //
 // Then the workgroups elect the one that continues with small_topology.  A
-// workgroup publishes `token` (unique to this call) in its flag once its
-// distances are stored; one that then finds every flag equal to the token
-// tries to swap the token into the claim word, and the one that finds the
-// claim not yet holding it wins.  A workgroup reads the flags only after its
-// own flag store has completed, so the one whose store completes last sees
-// every flag: at least one workgroup reaches the swap, and the swap admits
-// one.  No workgroup waits for another, and no flag needs clearing: stale
-// flags hold older tokens.  flags: small_tile_count + 1 words of workspace.
+// workgroup publishes the call's token in its flag once its distances are
+// stored; one that then finds every flag equal to the token tries to swap the
+// token into the claim word, and the one that finds the claim not yet holding
+// it wins.  A workgroup reads the flags only after its own flag store has
+// completed, so the one whose store completes last sees every flag: at least
+// one workgroup reaches the swap, and the swap admits one.  No workgroup waits
+// for another, and no flag needs clearing: stale flags hold older tokens.
+// The token is host_token + epoch * K, with epoch a word of the workspace that
+// every workgroup reads before it publishes its flag and the elected one
+// advances: consecutive calls differ by 1 + K, and so do replays of a captured
+// launch (its host_token frozen) by K.  flags: small_tile_count + 2 words of
+// workspace (flags, claim, epoch).
 template <int SLOTS, int TILE, bool BF16>
 __global__ __launch_bounds__(kSmallThreads) void schedule_small(
     const uint16_t* __restrict__ keys, int64_t S, int64_t D, int nb, int block,
-    double* dist_g, unsigned long long* flags, unsigned long long token, int sink,
+    double* dist_g, unsigned long long* flags, unsigned long long host_token, int sink,
     int local_radius, int topk, int per_row, int32_t* __restrict__ row_ptr,
     int32_t* __restrict__ col_idx, int64_t col_capacity,
     double* __restrict__ salience) {
@@ -992,6 +996,8 @@ __global__ __launch_bounds__(kSmallThreads) void schedule_small(
   }
   const int tj = ti + w;
   const bool diag = ti == tj;
+  // Issued first; needed only at the election.
+  const unsigned long long epoch = tid < 64 ? load_coherent(&flags[ntiles + 1]) : 0ull;
   // Slot q (below TILE: row blocks, from TILE: column blocks) -> block index;
   // a diagonal tile's columns are its rows.
   auto slot_block = [&](int q) { return q < TILE ? ti * TILE + q : tj * TILE + (q - TILE); };
@@ -1095,15 +1101,19 @@ __global__ __launch_bounds__(kSmallThreads) void schedule_small(
   wait_vmem();  // this thread's distance stores have completed
   __syncthreads();
   if (tid < 64) {
+    const unsigned long long token = host_token + epoch * 0x9E3779B97F4A7C15ull;
     if (tid == 0) store_coherent(&flags[blockIdx.x], token);
     wait_vmem();  // the flag store completes before any flag is read
     bool mine = true;
     for (int t = tid; t < ntiles; t += 64)
       if (t != (int)blockIdx.x) mine = mine && load_coherent(&flags[t]) == token;
     const bool all = __ballot(!mine) == 0ull;
-    if (tid == 0)
+    if (tid == 0) {
       elected = all && __hip_atomic_exchange(&flags[ntiles], token, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT) != token;
+      // every workgroup has read epoch: its flag, derived from it, is stored
+      if (elected) store_coherent(&flags[ntiles + 1], epoch + 1ull);
+    }
     wait_vmem();
   }
   __syncthreads();
@@ -1423,7 +1433,7 @@ WorkspaceLayout workspace_layout(int64_t nb, int64_t D) {
   L.edge_d = take(n * sizeof(double));
   L.edge_t = take(n * sizeof(uint32_t));
   L.flags = take(nb <= kLdsDistBlocks
-                     ? (size_t)(small_tile_count((int)nb, small_tile_edge((int)nb)) + 1) * sizeof(unsigned long long)
+                     ? (size_t)(small_tile_count((int)nb, small_tile_edge((int)nb)) + 2) * sizeof(unsigned long long)
                      : 0);
   L.total = off;
   return L;
@@ -1467,7 +1477,7 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
   hipError_t err;
   if (nb <= kLdsDistBlocks) {
     unsigned long long* flags = (unsigned long long*)(ws + L.flags);
-    const unsigned long long token = next_call_token();
+    const unsigned long long token = next_call_token();  // host part of the call's token
     const size_t lds = small_lds_bytes(nb);
     const int tile = small_tile_edge(nb);
     const dim3 grid((unsigned)small_tile_count(nb, tile));

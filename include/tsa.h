@@ -115,11 +115,12 @@ size_t tsa_build_schedule_workspace_bytes(int64_t S, int64_t D, int32_t block);
  *               col_capacity must be >= tsa_schedule_max_nnz(nb, sink,
  *               local_radius, topk), so the build can never overflow it.
  *   salience    device double [nb] or NULL; written when not NULL.
- *   workspace   device, >= tsa_build_schedule_workspace_bytes(S, D, 64) bytes,
+ *   workspace   device, >= tsa_build_schedule_workspace_bytes(S, D, block) bytes,
  *               256-byte aligned.  Its contents on entry may be anything (it needs
  *               no clearing) and are unspecified on return.  Two builds that may
  *               run at the same time (on different streams) must not share one
- *               workspace.
+ *               workspace.  A build captured in a HIP graph rebuilds the schedule
+ *               on every replay (the call's state lives in the workspace).
  *   nnz_host    host int64 or NULL.  When not NULL the call waits for the
  *               stream and stores row_ptr[nb] (the number of entries) there.
  *   S == 0 builds an empty schedule (row_ptr = {0}).
