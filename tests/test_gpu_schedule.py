@@ -194,3 +194,11 @@ def test_reused_and_prefilled_workspace(tsa, nb, D):
         assert np.array_equal(rp, rp_o), label
         assert np.array_equal(bufs.col_idx[:nnz].cpu().numpy(), ci_o), label
         assert np.allclose(bufs.salience.cpu().numpy(), sal_o, rtol=1e-12, atol=0), label
+
+
+def test_largest_schedule(tsa):
+    """The builder's limit, 4096 blocks (S = 262,144; the multi-launch path with the
+    LDS union-find), bit-exact against the oracle's all-pairs scan."""
+    keys = workloads.random_normal((64 * 4096, 8), "fp16", 4096)
+    rp, ci = _compare(tsa, keys, 2, 2, 24, "nb 4096")
+    assert rp.shape[0] == 4097
