@@ -254,7 +254,10 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
       const float m_new = grow ? mp : m_use;
       const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
       m_use = m_new;
-      thr_raw = (m_new + kRescaleSlack) / scale_log2 * (1.0f - 0x1p-20f);
+      // a relative margin below the exact threshold, of either sign, covers the
+      // rounding of mx * scale_log2 and of the division
+      const float thr = (m_new + kRescaleSlack) / scale_log2;
+      thr_raw = thr - __builtin_fabsf(thr) * 0x1p-20f;
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
