@@ -220,3 +220,22 @@ def test_workload_parity(tsa, name):
         worst = max(worst, err)
     print(f"{name}: nnz {ci.shape[0]}, max abs err {worst:.2e} over lanes {lanes}")
     assert worst <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_all_scores_strongly_negative(tsa, dtype):
+    """Queries pointing against every key: every scaled score is far below zero, so
+    the softmax offset, and with it the rescale threshold, is negative.  The output
+    and lse still match the oracle."""
+    k = workloads.random_normal((640, 64), dtype, 31, std=0.2)
+    kf = k.double().numpy() + 1.0  # keys around +1 in every dim
+    k = workloads.cast(kf, dtype)
+    q = workloads.cast(-4.0 * np.ones((640, 64)) + workloads.random_normal((640, 64), "fp16", 32, std=0.1).double().numpy(), dtype)
+    v = workloads.random_normal((640, 64), dtype, 33)
+    rp, ci = workloads.random_csr(10, seed=34, density=0.6)
+    want = oracle.masked_attention(q, k, v, rp, ci, 64)
+    lse_want = oracle.masked_lse(q, k, rp, ci)
+    assert np.nanmax(lse_want) < -20.0
+    out, lse = tsa.scheduled_attention(*_dev(q, k, v), *_csr_dev(rp, ci), return_lse=True)
+    assert _max_err(out, want) <= TOL[dtype]
+    assert float(np.abs(lse.cpu().numpy() - lse_want).max()) <= (1e-3 if dtype == "fp16" else 4e-3)
