@@ -53,7 +53,7 @@ struct Geo {
 };
 
 // LDS row r of every tile holds block row (r & 32) | swap_bits23(r & 31) and the
-// 16-byte chunk c of that row sits at chunk c ^ (r & 7).  fill_offsets gives,
+// 16-byte chunk c of that row sits at chunk c ^ k_swizzle(r).  fill_offsets gives,
 // for each 1 KB copy op of wave w, the byte offset in the block's rows of the
 // 16 bytes lane l moves (op o fills LDS piece o * kWaves + w of [tile A | tile B]).
 template <int D>
@@ -65,7 +65,7 @@ __device__ __forceinline__ void fill_offsets(uint32_t (&off)[Geo<D>::kTileOps], 
     const int cc = chunk % (kBlock * G::kChunksPerRow);
     const int r = cc / G::kChunksPerRow, pc = cc % G::kChunksPerRow;
     const int row = (r & 32) | swap_bits23(r & 31);
-    off[op] = (uint32_t)(row * G::kRowBytes + 16 * (pc ^ (r & k_swizzle_mask<D>())));
+    off[op] = (uint32_t)(row * G::kRowBytes + 16 * (pc ^ k_swizzle<D>(r)));
   }
 }
 
@@ -76,25 +76,31 @@ __device__ __forceinline__ uint32_t row_read_addr(uint32_t base, int half, int n
   return base + (uint32_t)k_chunk_offset<D>(32 * half + n, 2 * c + h);
 }
 
-// LDS address of this lane's transposing read for head-dim tile dt: within each
-// 16-lane group, lane gi supplies the 8-byte piece (dims 4 (gi & 3) .. +3 of the
-// group's 16 dims) of row r0 = 32 half + 4 h + gi / 4, which holds block row
-// 32 half + 8 h + gi / 4; adding 8 rows gives block rows +4, adding 16 gives +16.
+// LDS addresses of this lane's transposing reads for head-dim tile dt: within
+// each 16-lane group, lane gi supplies the 8-byte piece (dims 4 (gi & 3) .. +3 of
+// the group's 16 dims) of row r0 = 32 half + 4 h + gi / 4, which holds block row
+// 32 half + 8 h + gi / 4 (a[0]), and of row r0 + 8, block row +4 (a[1]).  Adding
+// 16 rows (block rows +16) leaves k_swizzle unchanged, so that one is an offset.
 template <int D>
-__device__ __forceinline__ uint32_t tr_read_addr(uint32_t base, int half, int g, int gi, int dt) {
+__device__ __forceinline__ void tr_read_addrs(uint32_t (&a)[2], uint32_t base, int half, int g, int gi,
+                                              int dt) {
   const int r0 = 32 * half + 4 * (g >> 1) + (gi >> 2);
   const int dchunk = 4 * dt + 2 * (g & 1) + ((gi & 3) >> 1);
-  return base + (uint32_t)(r0 * Geo<D>::kRowBytes + 16 * (dchunk ^ (r0 & k_swizzle_mask<D>())) + 8 * (gi & 1));
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int r = r0 + 8 * e;
+    a[e] = base + (uint32_t)(r * Geo<D>::kRowBytes + 16 * (dchunk ^ k_swizzle<D>(r)) + 8 * (gi & 1));
+  }
 }
 
 // Issue the four transposing reads of one head-dim tile: block rows 16 gg + 8 h +
 // 4 e + 0..3 of the lane's half for (gg, e) = (0,0), (0,1), (1,0), (1,1).
 template <int kOff, int kRowBytes>
-__device__ __forceinline__ void tr_reads(u32x2* dst, uint32_t addr) {
-  dst[0] = lds_read_tr16<kOff>(addr);
-  dst[1] = lds_read_tr16<kOff + 8 * kRowBytes>(addr);
-  dst[2] = lds_read_tr16<kOff + 16 * kRowBytes>(addr);
-  dst[3] = lds_read_tr16<kOff + 24 * kRowBytes>(addr);
+__device__ __forceinline__ void tr_reads(u32x2* dst, const uint32_t (&a)[2]) {
+  dst[0] = lds_read_tr16<kOff>(a[0]);
+  dst[1] = lds_read_tr16<kOff>(a[1]);
+  dst[2] = lds_read_tr16<kOff + 16 * kRowBytes>(a[0]);
+  dst[3] = lds_read_tr16<kOff + 16 * kRowBytes>(a[1]);
 }
 // A operand of k-step gg from the reads of one tile.
 __device__ __forceinline__ u32x4 tr_operand(const u32x2* t, int gg) {
@@ -227,9 +233,9 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
   uint32_t a_addr[kStepsD];
 #pragma unroll
   for (int c = 0; c < kStepsD; ++c) a_addr[c] = row_read_addr<D>(base, kh, n, h, c);
-  uint32_t t_addr[kTilesD];
+  uint32_t t_addr[kTilesD][2];
 #pragma unroll
-  for (int dt = 0; dt < kTilesD; ++dt) t_addr[dt] = tr_read_addr<D>(base, kh, g, gi, dt);
+  for (int dt = 0; dt < kTilesD; ++dt) tr_read_addrs<D>(t_addr[dt], base, kh, g, gi, dt);
 
   f32x16 acc[kTilesD];
 #pragma unroll
@@ -441,9 +447,9 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
   uint32_t a_addr[kStepsD];
 #pragma unroll
   for (int c = 0; c < kStepsD; ++c) a_addr[c] = row_read_addr<D>(base, qh, n, h, c);
-  uint32_t t_addr[kTilesD];
+  uint32_t t_addr[kTilesD][2];
 #pragma unroll
-  for (int dt = 0; dt < kTilesD; ++dt) t_addr[dt] = tr_read_addr<D>(base, qh, g, gi, dt);
+  for (int dt = 0; dt < kTilesD; ++dt) tr_read_addrs<D>(t_addr[dt], base, qh, g, gi, dt);
   // Statistics of the query rows of this lane's result registers: register r
   // holds query row 32qh + 16 (r >> 3) + 8h + (r & 7).
   const uint32_t st_addr = base + 2 * kTileBytes + 8 * (32 * qh + 8 * h);

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     const int cc = is_v ? chunk - kBlock * kChunksPerRow : chunk;
     const int r = cc / kChunksPerRow, pc = cc % kChunksPerRow;
     const int key = is_v ? r : ((r & 32) | swap_bits23(r & 31));
-    const int c = is_v ? (pc ^ v_swizzle<D>(r)) : (pc ^ (r & k_swizzle_mask<D>()));
+    const int c = is_v ? (pc ^ v_swizzle<D>(r)) : (pc ^ k_swizzle<D>(r));
     fill_off[op] = (uint32_t)(key * kRowBytes + 16 * c);
   }
   // Queue the copy of K and V block j into one stage (no registers in between).

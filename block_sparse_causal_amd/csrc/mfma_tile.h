@@ -87,15 +87,26 @@ __device__ __forceinline__ int swap_bits23(int m) {
 // Byte offset, inside one tile, of the 16-byte chunk `c` (8 elements) of row `r`.
 // K rows use chunk ^ (r & 7); V rows use chunk ^ 2*t(r & 3), where t spreads the
 // four key rows that one transposing read touches over distinct bank groups.
-// The K-layout XOR mask: the chunk index is XORed with (r & mask), which must
-// stay below the row's chunk count (D / 8): 7 from D = 64 on, 3 at D = 32.
+// K-layout swizzle: 16-byte chunk c of data row r sits at chunk c ^ k_swizzle(r).
+// gfx950's LDS has 64 four-byte banks.  A row-wise operand read has 16 lanes
+// reading one 16-byte chunk each from 16 consecutive rows; a transposing read
+// has 32 lanes reading four chunks (64 bytes) from each of 4 consecutive rows.
+// Rows of 2D bytes start at bank 16 (r mod 128 / D) for D < 128 and at bank 0
+// from D = 128 on, so the XOR value must differ between same-bank-offset rows:
+//   D = 32:  the 4 rows of a bank offset among 16: bits 2-3 of r;
+//   D = 64:  8 same-parity rows among 16 (bits 1-3 of r), with rows r and r + 2
+//            of a 4-row group 4 chunks apart (bit 1 -> XOR bit 2);
+//   D >= 128: 16 rows (bits 0-3), the 4 rows of a group 4 chunks apart.
+// The value never exceeds the row's chunk count minus one.
 template <int D>
-constexpr int k_swizzle_mask() {
-  return D >= 64 ? 7 : D / 8 - 1;
+__device__ __forceinline__ int k_swizzle(int r) {
+  if constexpr (D == 32) return (r >> 2) & 3;
+  else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
 }
 template <int D>
 __device__ __forceinline__ int k_chunk_offset(int r, int c) {
-  return r * (D * 2) + 16 * (c ^ (r & k_swizzle_mask<D>()));
+  return r * (D * 2) + 16 * (c ^ k_swizzle<D>(r));
 }
 // At D = 32 the four rows one transposing read touches already sit 64 bytes
 // apart, in distinct bank groups, so V rows are not swizzled.
