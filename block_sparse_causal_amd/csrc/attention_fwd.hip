@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t nnz,
-    int S, int nb, int64_t lane_base, float scale_log2) {
+    int S, int nb, int64_t lane_base, float scale_log2, float inv_scale_log2) {
   using E = Elem<BF16>;
   constexpr int kStepsD = D / 16;                  // 16-deep steps of Q.K^T
   constexpr int kTilesD = D / 32;                  // 32-row tiles of O^T
@@ -125,13 +125,16 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   }
 
   // Per-lane byte offset, inside a block's rows, of the 16 bytes each fill op
-  // moves.  Op o of wave w fills the 1 KB piece (o * kWaves + w) of [K | V].
+  // moves.  Op o of wave w fills the 1 KB piece (o * kWaves + w) of [K | V]; a
+  // tile is a whole number of kWaves-piece rounds, so the first half of the ops
+  // fill K and the second half V (known at compile time).
+  static_assert((kTileBytes / 1024) % kWaves == 0 && kFillOps % 2 == 0, "fill ops split K | V");
   uint32_t fill_off[kFillOps];
 #pragma unroll
   for (int op = 0; op < kFillOps; ++op) {
-    const int chunk = (op * kWaves + w) * 64 + l;
-    const bool is_v = chunk >= kBlock * kChunksPerRow;
-    const int cc = is_v ? chunk - kBlock * kChunksPerRow : chunk;
+    constexpr int kHalfOps = kFillOps / 2;
+    const bool is_v = op >= kHalfOps;
+    const int cc = ((is_v ? op - kHalfOps : op) * kWaves + w) * 64 + l;
     const int r = cc / kChunksPerRow, pc = cc % kChunksPerRow;
     const int key = is_v ? r : ((r & 32) | swap_bits23(r & 31));
     const int c = is_v ? (pc ^ v_swizzle<D>(r)) : (pc ^ k_swizzle<D>(r));
@@ -196,6 +199,9 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   float m_use = -__builtin_inff();  // exponent offset in use (log2 units)
   float thr_raw = -__builtin_inff();  // trigger threshold for the raw-score max (below)
   float l_run = 0.0f;               // this lane's share of the denominator
+  // Until the first offset is set nothing has been accumulated (O and l are 0 in
+  // every lane), so that first rescale has nothing to scale (wave-uniform flag).
+  bool started = false;
 
   // LDS byte addresses (stage 0) of this lane's K and V operand reads; stage t
   // adds t * 2 * kTileBytes through the instructions' offset field.
@@ -216,6 +222,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     }
   }
 
+  const int diag_lim = n - 8 * h;
   auto compute = [&](int j, auto T_c) {
     // Stage offset: in the instructions' 16-bit offset field when it fits (D <= 128),
     // else (D = 256, second stage at 64 KB) added to the lane addresses.
@@ -235,11 +242,11 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
 #pragma unroll
     for (int c = 0; c < kStepsD; ++c) s = E::mfma(ka[c], qop[c], s);
     if (j == i && kh == qh) {  // diagonal sub-tile: key position must not exceed query position
+      // key position of s[r] is 16 (r >> 3) + 8 h + (r & 7); compare its constant
+      // part with n - 8 h
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kpos = 16 * (r >> 3) + 8 * h + (r & 7);
-        if (kpos > n) s[r] = -__builtin_inff();
-      }
+      for (int r = 0; r < 16; ++r)
+        if (16 * (r >> 3) + (r & 7) > diag_lim) s[r] = -__builtin_inff();
     }
     float mx = s[0];
 #pragma unroll
@@ -255,12 +262,15 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
       const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
       m_use = m_new;
       // a relative margin below the exact threshold, of either sign, covers the
-      // rounding of mx * scale_log2 and of the division
-      const float thr = (m_new + kRescaleSlack) / scale_log2;
+      // rounding of mx * scale_log2, of the reciprocal and of the product
+      const float thr = (m_new + kRescaleSlack) * inv_scale_log2;
       thr_raw = thr - __builtin_fabsf(thr) * 0x1p-20f;
-      l_run *= alpha;
+      if (started) {
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
+        for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
+      }
+      started = true;
     }
     // V^T operands for O^T += V^T . P^T over this half's two 16-key chunks come
     // from row-major V through transposing reads: lane (group g, index gi) gets
@@ -450,7 +460,8 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, void* out, 
     const int64_t nl = lanes - l0 < lanes_per_launch ? lanes - l0 : lanes_per_launch;
     hipLaunchKernelGGL((attention_fwd_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
                        stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (uint16_t*)out, lse, row_ptr, col_idx, nnz, (int)S, (int)nb, l0, scale_log2);
+                       (uint16_t*)out, lse, row_ptr, col_idx, nnz, (int)S, (int)nb, l0, scale_log2,
+                       1.0f / scale_log2);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

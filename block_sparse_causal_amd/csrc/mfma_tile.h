@@ -85,8 +85,8 @@ __device__ __forceinline__ int swap_bits23(int m) {
 }
 
 // Byte offset, inside one tile, of the 16-byte chunk `c` (8 elements) of row `r`.
-// K rows use chunk ^ (r & 7); V rows use chunk ^ 2*t(r & 3), where t spreads the
-// four key rows that one transposing read touches over distinct bank groups.
+// K rows use chunk ^ k_swizzle(r); V rows use chunk ^ 2*t(r & 3), where t spreads
+// the four key rows that one transposing read touches over distinct bank groups.
 // K-layout swizzle: 16-byte chunk c of data row r sits at chunk c ^ k_swizzle(r).
 // gfx950's LDS has 64 four-byte banks.  A row-wise operand read has 16 lanes
 // reading one 16-byte chunk each from 16 consecutive rows; a transposing read
