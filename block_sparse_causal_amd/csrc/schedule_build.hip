@@ -426,6 +426,7 @@ struct SmallState {
   double sort_d[kLdsDistBlocks];              // MST edges, ascending
   uint32_t sort_t[kLdsDistBlocks];
   int rank[kLdsDistBlocks];
+  int dead_at[kLdsDistBlocks];                // per block: rank of the edge that absorbs it
   int nedges;
 };
 static_assert(sizeof(SmallState) <= kStageBytes, "small-schedule state fits the staging area");
@@ -438,6 +439,13 @@ __device__ __forceinline__ void set_block(int (&a)[SLOTS], int x, int val) {
   for (int s = 0; s < SLOTS; ++s) a[s] = (lane + 64 * s == x) ? val : a[s];
 }
 
+// Orders this wavefront's earlier LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Elder rule over the MST edges in ascending order, one wavefront, nb <= 64 *
 // SLOTS <= 128.  Every component is named by key (size << 8) | (255 - root),
 // held by each of its blocks: of the two components an edge joins, the larger
@@ -446,33 +454,45 @@ __device__ __forceinline__ void set_block(int (&a)[SLOTS], int x, int val) {
 // block v (lane v % 64, slot v / 64): the rank of the edge at which v was
 // absorbed, or -1 for a root that never is.  The absorbed root's salience is
 // that edge's length.
+// The edges are taken 64 at a time with the loop over them unrolled, so that
+// every lane index is a constant; lane k records the block absorbed at edge
+// base + k, and after each group those ranks are scattered to the blocks
+// through dead_at (LDS, nb entries).
 template <int SLOTS>
-__device__ __forceinline__ void elder_ranks(const uint32_t* st, int ne, int (&dead)[SLOTS]) {
+__device__ __forceinline__ void elder_ranks(const uint32_t* st, int ne, int (&dead)[SLOTS], int* dead_at) {
   const int lane = threadIdx.x & 63;
   int ckey[SLOTS];
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     ckey[s] = (1 << 8) | (255 - (lane + 64 * s));
-    dead[s] = -1;
+    dead_at[lane + 64 * s] = -1;
   }
   for (int base = 0; base < ne; base += 64) {
     const int r = base + lane;
     const uint32_t tw = r < ne ? st[r] : 0u;
     const int aw = (int)(tw >> 16), bw = (int)(tw & 0xffffu);
     const int n = __builtin_amdgcn_readfirstlane(ne - base < 64 ? ne - base : 64);
-    for (int k = 0; k < n; ++k) {
-      const int a = read_lane(aw, k), b = read_lane(bw, k);
-      const uint32_t ka = (uint32_t)block_value<SLOTS>(ckey, a);
-      const uint32_t kb = (uint32_t)block_value<SLOTS>(ckey, b);
-      const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
-      const int absorbed = 255 - (int)(lo & 255u);
-      const int grown = (int)(hi + (lo & ~255u));
+    int absorbed = -1;  // lane k: the block absorbed at edge base + k
 #pragma unroll
-      for (int s = 0; s < SLOTS; ++s)
-        ckey[s] = ((uint32_t)ckey[s] == ka || (uint32_t)ckey[s] == kb) ? grown : ckey[s];
-      set_block<SLOTS>(dead, absorbed, base + k);
+    for (int k = 0; k < 64; ++k) {
+      if (k < n) {
+        const int a = read_lane(aw, k), b = read_lane(bw, k);
+        const uint32_t ka = (uint32_t)block_value<SLOTS>(ckey, a);
+        const uint32_t kb = (uint32_t)block_value<SLOTS>(ckey, b);
+        const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
+        const int grown = (int)(hi + (lo & ~255u));
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+          ckey[s] = ((uint32_t)ckey[s] == ka || (uint32_t)ckey[s] == kb) ? grown : ckey[s];
+        absorbed = lane == k ? 255 - (int)(lo & 255u) : absorbed;
+      }
     }
+    wave_lds_sync();
+    if (absorbed >= 0) dead_at[absorbed] = r;  // each block is absorbed at most once
   }
+  wave_lds_sync();
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) dead[s] = dead_at[lane + 64 * s];
 }
 
 // Inclusive prefix sum over the wavefront: shifts within each 16-lane row,
@@ -487,12 +507,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// Orders this wavefront's earlier LDS writes before its later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // The elder rule of elder_ranks for the large path (nb <= 64 * SLOTS <= 512):
 // keys (size << 12) | (4095 - root), one vector register per lane holding its
@@ -518,15 +532,18 @@ __device__ __forceinline__ void elder_salience(const uint32_t* st, const double*
     const int aw = (int)(tw >> 16), bw = (int)(tw & 0xffffu);
     const int n = __builtin_amdgcn_readfirstlane(ne - base < 64 ? ne - base : 64);
     int absorbed_at = -1;  // lane k: the block absorbed at edge base + k
-    for (int k = 0; k < n; ++k) {
-      const int a = read_lane(aw, k), b = read_lane(bw, k);
-      const uint32_t ka = (uint32_t)read_lane((int)ckey[a >> 6], a & 63);
-      const uint32_t kb = (uint32_t)read_lane((int)ckey[b >> 6], b & 63);
-      const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
-      const uint32_t grown = hi + (lo & ~kRootMask);
 #pragma unroll
-      for (int s = 0; s < SLOTS; ++s) ckey[s] = (ckey[s] == ka || ckey[s] == kb) ? grown : ckey[s];
-      absorbed_at = lane == k ? (int)(kRootMask - (lo & kRootMask)) : absorbed_at;
+    for (int k = 0; k < 64; ++k) {
+      if (k < n) {
+        const int a = read_lane(aw, k), b = read_lane(bw, k);
+        const uint32_t ka = (uint32_t)read_lane((int)ckey[a >> 6], a & 63);
+        const uint32_t kb = (uint32_t)read_lane((int)ckey[b >> 6], b & 63);
+        const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
+        const uint32_t grown = hi + (lo & ~kRootMask);
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) ckey[s] = (ckey[s] == ka || ckey[s] == kb) ? grown : ckey[s];
+        absorbed_at = lane == k ? (int)(kRootMask - (lo & kRootMask)) : absorbed_at;
+      }
     }
     if (absorbed_at >= 0) sal[absorbed_at] = len;
   }
@@ -926,7 +943,7 @@ __device__ __forceinline__ void small_topology(
 
   // ---- Elder rule, top-k and CSR rows.
   int dead[SLOTS];
-  elder_ranks<SLOTS>(A.sort_t, ne, dead);
+  elder_ranks<SLOTS>(A.sort_t, ne, dead, A.dead_at);
   select_and_emit_wave<SLOTS>(dead, A.sort_d, ne, nb, sink, local_radius, topk, per_row, A.rank,
                               row_ptr,
                               col_idx, col_capacity, salience);
@@ -1111,10 +1128,11 @@ __global__ __launch_bounds__(kSmallThreads) void schedule_small(
     if (tid == 0) {
       elected = all && __hip_atomic_exchange(&flags[ntiles], token, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT) != token;
-      // every workgroup has read epoch: its flag, derived from it, is stored
+      // every workgroup has read epoch: its flag, derived from it, is stored.
+      // Nothing in this launch reads epoch again, so the store is not waited
+      // for (the next launch sees it).
       if (elected) store_coherent(&flags[ntiles + 1], epoch + 1ull);
     }
-    wait_vmem();
   }
   __syncthreads();
   if (!elected) return;
