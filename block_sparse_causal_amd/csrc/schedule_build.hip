@@ -431,14 +431,6 @@ struct SmallState {
 };
 static_assert(sizeof(SmallState) <= kStageBytes, "small-schedule state fits the staging area");
 
-// Sets block x (uniform) of per-block register array `a` to `val` (uniform).
-template <int SLOTS>
-__device__ __forceinline__ void set_block(int (&a)[SLOTS], int x, int val) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int s = 0; s < SLOTS; ++s) a[s] = (lane + 64 * s == x) ? val : a[s];
-}
-
 // Orders this wavefront's earlier LDS writes before its later LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -532,18 +524,15 @@ __device__ __forceinline__ void elder_salience(const uint32_t* st, const double*
     const int aw = (int)(tw >> 16), bw = (int)(tw & 0xffffu);
     const int n = __builtin_amdgcn_readfirstlane(ne - base < 64 ? ne - base : 64);
     int absorbed_at = -1;  // lane k: the block absorbed at edge base + k
+    for (int k = 0; k < n; ++k) {
+      const int a = read_lane(aw, k), b = read_lane(bw, k);
+      const uint32_t ka = (uint32_t)read_lane((int)ckey[a >> 6], a & 63);
+      const uint32_t kb = (uint32_t)read_lane((int)ckey[b >> 6], b & 63);
+      const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
+      const uint32_t grown = hi + (lo & ~kRootMask);
 #pragma unroll
-    for (int k = 0; k < 64; ++k) {
-      if (k < n) {
-        const int a = read_lane(aw, k), b = read_lane(bw, k);
-        const uint32_t ka = (uint32_t)read_lane((int)ckey[a >> 6], a & 63);
-        const uint32_t kb = (uint32_t)read_lane((int)ckey[b >> 6], b & 63);
-        const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
-        const uint32_t grown = hi + (lo & ~kRootMask);
-#pragma unroll
-        for (int s = 0; s < SLOTS; ++s) ckey[s] = (ckey[s] == ka || ckey[s] == kb) ? grown : ckey[s];
-        absorbed_at = lane == k ? (int)(kRootMask - (lo & kRootMask)) : absorbed_at;
-      }
+      for (int s = 0; s < SLOTS; ++s) ckey[s] = (ckey[s] == ka || ckey[s] == kb) ? grown : ckey[s];
+      absorbed_at = lane == k ? (int)(kRootMask - (lo & kRootMask)) : absorbed_at;
     }
     if (absorbed_at >= 0) sal[absorbed_at] = len;
   }
