@@ -32,7 +32,7 @@
 //                       (the pair is launched ceil(log2 nb) times: every round
 //                       at least halves the number of components, and rounds
 //                       after the last merge return at once)
-//     finish_kernel     edge ranks, elder rule (union-find in LDS), top-k, CSR.
+//     finish_kernel     edge sort, elder rule (union-find in LDS), top-k, CSR.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <unistd.h>
@@ -210,6 +210,62 @@ __device__ __forceinline__ void count_ranks(int n, int* rank, Before before) {
     int c = 0;
     for (int f = f0; f < f1; ++f) c += before(f, e) ? 1 : 0;
     if (c) atomicAdd(&rank[e], c);
+  }
+}
+
+// Orders this wavefront's earlier LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Ascending in-place sort of the n edges (d[i], t[i]) (lengths, then tags; the
+// tags are distinct, so the order is total) by the whole workgroup: a bitonic
+// network over the next power of two P >= n in which every merge starts by
+// comparing each element with its mirror in the merge block, so that every
+// compare-exchange puts the smaller key at the lower index.  Positions n..P-1
+// stand for keys above every edge and are never touched: a pair whose upper
+// position is past n keeps its lower element.  Pair x is handled by thread
+// x % kThreads; while the pair distance is at most 32, the 64 pairs of a
+// wavefront stay inside one 128-element window of that wavefront, so such a
+// step needs only a wavefront-level sync before the next step of the same kind.
+// Ends with a workgroup barrier.
+template <int kThreads>
+__device__ void sort_edges(double* d, uint32_t* t, int n) {
+  int P = 1;
+  while (P < n) P <<= 1;
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int x = threadIdx.x; x < P / 2; x += kThreads) {
+        int lo, hi;
+        if (j == (k >> 1)) {  // mirror step of the merge
+          const int blk = x / j, off = x % j;
+          lo = blk * k + off;
+          hi = blk * k + k - 1 - off;
+        } else {
+          const int blk = x / j, off = x % j;
+          lo = blk * 2 * j + off;
+          hi = lo + j;
+        }
+        if (hi < n) {
+          const double dl = d[lo], dh = d[hi];
+          const uint32_t tl = t[lo], th = t[hi];
+          if (edge_less(dh, th, dl, tl)) {
+            d[lo] = dh;
+            t[lo] = th;
+            d[hi] = dl;
+            t[hi] = tl;
+          }
+        }
+      }
+      // distance of the next step: j / 2 within this merge, else the next merge's k
+      const int next = j > 1 ? (j >> 1) : k;
+      if (next > 32 || (j == 1 && 2 * k > P))
+        __syncthreads();
+      else
+        wave_lds_sync();
+    }
   }
 }
 
@@ -431,12 +487,6 @@ struct SmallState {
 };
 static_assert(sizeof(SmallState) <= kStageBytes, "small-schedule state fits the staging area");
 
-// Orders this wavefront's earlier LDS writes before its later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Elder rule over the MST edges in ascending order, one wavefront, nb <= 64 *
 // SLOTS <= 128.  Every component is named by key (size << 8) | (255 - root),
@@ -1289,13 +1339,13 @@ __global__ __launch_bounds__(kLargeThreads) void boruvka_merge(int nb, int* __re
   }
 }
 
-// Edge ranks, elder rule, top-k and CSR emission for nb > kLdsDistBlocks.
+// Edge sort, elder rule, top-k and CSR emission for nb > kLdsDistBlocks.
 // Dynamic LDS regions (reused across phases):
-//   R0 double[nb]  edge lengths   -> salience
-//   R1 int[nb+1]   edge tags      -> union-find parent -> top prefix
-//   R2 double[nb]  sorted lengths -> row sizes / starts (int[nb+1])
-//   R3 int[nb]     sorted tags    -> top-k list
-//   R4 int[nb+1]   edge ranks     -> component sizes -> block ranks
+//   R0 double[nb]  salience
+//   R1 int[nb+1]   union-find parent -> top prefix
+//   R2 double[nb]  edge lengths, sorted in place -> row sizes / starts (int[nb+1])
+//   R3 int[nb]     edge tags, sorted with them   -> top-k list
+//   R4 int[nb+1]   component sizes -> block ranks
 __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
     int nb, const int* __restrict__ state, const double* __restrict__ edge_d_g,
     const uint32_t* __restrict__ edge_t_g, int sink, int local_radius, int topk, int per_row,
@@ -1312,26 +1362,14 @@ __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
   const int tid = threadIdx.x;
   const int ne = state[0] < nb - 1 ? state[0] : nb - 1;
 
-  double* ed = R0;
-  uint32_t* et = (uint32_t*)R1;
   double* sd = R2;
   uint32_t* st = (uint32_t*)R3;
-  int* rank = R4;
   for (int e = tid; e < ne; e += kLargeThreads) {
-    ed[e] = edge_d_g[e];
-    et[e] = edge_t_g[e];
-    rank[e] = 0;
+    sd[e] = edge_d_g[e];
+    st[e] = edge_t_g[e];
   }
   __syncthreads();
-  count_ranks<kLargeThreads>(ne, rank, [&](int f, int e) {
-    return edge_less(ed[f], et[f], ed[e], et[e]);
-  });
-  __syncthreads();
-  for (int e = tid; e < ne; e += kLargeThreads) {
-    sd[rank[e]] = ed[e];
-    st[rank[e]] = et[e];
-  }
-  __syncthreads();
+  sort_edges<kLargeThreads>(sd, st, ne);  // ends with a barrier
 
   // Elder rule.  Up to 512 blocks: component keys in registers of one wavefront
   // (elder_salience).  Beyond: union-find in LDS, union by size with the elder
