@@ -230,7 +230,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // x % kThreads; while the pair distance is at most 32, the 64 pairs of a
 // wavefront stay inside one 128-element window of that wavefront, so such a
 // step needs only a wavefront-level sync before the next step of the same kind.
-// Ends with a workgroup barrier.
+// Ends with a workgroup barrier when n > 1 (no step runs otherwise).
 template <int kThreads>
 __device__ void sort_edges(double* d, uint32_t* t, int n) {
   int P = 1;
@@ -1369,7 +1369,7 @@ __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
     st[e] = edge_t_g[e];
   }
   __syncthreads();
-  sort_edges<kLargeThreads>(sd, st, ne);  // ends with a barrier
+  sort_edges<kLargeThreads>(sd, st, ne);  // the next phase reads sd, st after its own barrier
 
   // Elder rule.  Up to 512 blocks: component keys in registers of one wavefront
   // (elder_salience).  Beyond: union-find in LDS, union by size with the elder
