@@ -346,13 +346,22 @@ __device__ void select_and_emit(const double* sal, int nb, int sink, int local_r
                                 double* __restrict__ salience) {
   const int tid = threadIdx.x;
   const int kk = topk < nb ? topk : nb;
-  for (int v = tid; v < nb; v += kThreads) brank[v] = 0;
-  __syncthreads();
-  if (kk > 0 && kk < nb)
-    count_ranks<kThreads>(nb, brank, [&](int u, int v) {
-      const double su = sal[u], sv = sal[v];
-      return su > sv || (su == sv && u < v);
-    });
+  if (kk > 0 && kk < nb) {
+    // Rank under (-salience, index): sort the pairs (the regions of cnt and topidx
+    // are free until the ranks exist), then each position names its block.
+    double* skey = reinterpret_cast<double*>(cnt);
+    uint32_t* sidx = reinterpret_cast<uint32_t*>(topidx);
+    for (int v = tid; v < nb; v += kThreads) {
+      skey[v] = -sal[v];
+      sidx[v] = (uint32_t)v;
+    }
+    __syncthreads();
+    sort_edges<kThreads>(skey, sidx, nb);
+    __syncthreads();
+    for (int p = tid; p < nb; p += kThreads) brank[sidx[p]] = p;
+  } else {
+    for (int v = tid; v < nb; v += kThreads) brank[v] = 0;  // all blocks or none pass rank < kk
+  }
   __syncthreads();
   if (salience != nullptr)
     for (int v = tid; v < nb; v += kThreads) salience[v] = sal[v];
