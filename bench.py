@@ -12,7 +12,9 @@ tiles) / step time, in TFLOP/s.  The attention kernel is also timed on its own
 (HIP events on the stream it runs on, around every launch in the timed region)
 for the roofline entry, and the same kernel over the dense causal CSR gives the
 sparse-vs-dense-CSR speedup.  The fp64 CPU oracle is timed on a bounded sample
-of the same workload (cpu_baseline).
+of the same workload (cpu_baseline), and the lanes it computes are compared with
+the output of the last timed step (parity: max abs error, max |O|, CSR equality);
+the bench exits non-zero when that check fails.
 """
 from __future__ import annotations
 
@@ -28,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "scheduled-attn fwd effective TFLOP/s (% MFMA peak) + sparse/dense-CSR speedup"
 PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
+PARITY_BAR = {"fp16": 2e-3, "bf16": 1e-2}  # max abs error of the output against the fp64 oracle
 # sources of the attention forward kernel (its own file and the shared device helpers)
 ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_causal_amd", "csrc", f) for f in ("attention_fwd.hip", "mfma_tile.h")]
 
@@ -60,9 +63,13 @@ def _traffic(workload: str):
         return None
 
 
-def _cpu_baseline(w, q, k, v, budget_s: float):
+def _cpu_baseline(w, q, k, v, budget_s: float, gpu_out=None, gpu_csr=None):
     """Time the oracle on the host: schedule build (all pairs) + dense masked
-    attention lane by lane until the time budget is used (at least one lane)."""
+    attention lane by lane until the time budget is used (at least one lane).
+
+    When the GPU's output of the timed launch (and its CSR) is given, the oracle
+    lanes just computed are also compared with it: max abs error, max |O|, and
+    whether the GPU-built CSR equals the oracle's bit for bit."""
     import numpy as np
 
     import oracle
@@ -80,12 +87,25 @@ def _cpu_baseline(w, q, k, v, budget_s: float):
     else:
         rp, ci, _ = oracle.build_schedule(kl[0], 64, w.sink, w.local_radius, w.topk)
     lanes = 0
+    outs = []
     for lane in range(ql.shape[0]):
-        oracle.masked_attention(ql[lane], kl[lane], vl[lane], rp, ci, 64)
+        outs.append(oracle.masked_attention(ql[lane], kl[lane], vl[lane], rp, ci, 64))
         lanes += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    parity = None
+    if gpu_out is not None:
+        got = gpu_out.reshape(-1, w.S, w.D)[:lanes].double().numpy()
+        want = np.stack(outs)
+        grp, gci = gpu_csr
+        parity = {
+            "max_abs_err": float(np.abs(got - want).max()),
+            "max_abs_out": float(np.abs(want).max()),
+            "lanes_checked": lanes,
+            "rows_per_lane": w.S,
+            "csr_bit_exact": bool(np.array_equal(grp, rp) and np.array_equal(gci, ci)),
+        }
     flops = lanes * int(ci.shape[0]) * 4 * 64 * 64 * w.D
     return {
         "value": flops / dt / 1e12,
@@ -96,6 +116,7 @@ def _cpu_baseline(w, q, k, v, budget_s: float):
                   f"visited-block flops of those lanes / wall time; host has {os.cpu_count()} cpus",
         "seconds": dt,
         "lanes": lanes,
+        "parity": parity,
     }
 
 
@@ -201,6 +222,9 @@ def main() -> int:
     attn_ms_each = sorted(a.elapsed_time(b) for a, b in zip(ev_a, ev_b))
     attn_ms = sum(attn_ms_each) / len(attn_ms_each)
     build_ms = sum(s.elapsed_time(a) for s, a in zip(ev_s, ev_a)) / args.steps
+    # The output and CSR of the last timed step, checked against the oracle below.
+    timed_out = out.cpu()
+    timed_csr = (rp.cpu().numpy(), ci[:nnz].cpu().numpy())
 
     # Same kernel over the dense causal CSR at the same shape (like-for-like baseline).
     drp, dci = tsa.dense_causal_schedule(w.nb, dev)
@@ -399,12 +423,21 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    bad = None
     if not args.no_cpu_baseline:
         print(f"# timing the fp64 oracle for about {args.cpu_budget:.0f} s", file=sys.stderr, flush=True)
-        cb = _cpu_baseline(w, q_cpu, k_cpu, v_cpu, args.cpu_budget)
+        cb = _cpu_baseline(w, q_cpu, k_cpu, v_cpu, args.cpu_budget, timed_out, timed_csr)
         result["cpu_baseline"] = {key: cb[key] for key in ("value", "unit", "cores", "kind", "sample")}
         result["cpu_baseline"]["value"] = round(cb["value"], 6)
+        par = cb["parity"]
+        par["bar"] = PARITY_BAR[w.dtype]
+        result["parity"] = par
+        if par["max_abs_err"] > par["bar"] or not par["csr_bit_exact"]:
+            bad = f"timed output fails the oracle check: {par}"
     print(json.dumps(result), flush=True)
+    if bad:
+        print(bad, file=sys.stderr, flush=True)
+        return 1
     return 0
 
 

@@ -36,7 +36,7 @@ hipError_t launch_attention_bwd(const BwdArgs& args, hipStream_t stream);
 size_t transpose_workspace_bytes(int64_t nb);
 hipError_t launch_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* col_idx,
                                      int64_t nnz, int32_t* col_ptr, int32_t* row_idx,
-                                     void* workspace, hipStream_t stream);
+                                     int64_t row_capacity, void* workspace, hipStream_t stream);
 
 // Schedule builder: centroids -> distances -> MST -> elder rule -> top-k -> CSR.
 struct ScheduleWorkspace {
@@ -55,7 +55,7 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
 // over 64-row blocks that allows exactly the same keys (see schedule_refine.hip).
 hipError_t launch_refine_schedule(int64_t S, int block, const int32_t* row_ptr,
                                   const int32_t* col_idx, int64_t nnz, int32_t* row_ptr64,
-                                  int32_t* col_idx64, hipStream_t stream);
+                                  int32_t* col_idx64, int64_t capacity, hipStream_t stream);
 
 hipError_t launch_dense_schedule(int64_t nb, int32_t* row_ptr, int32_t* col_idx,
                                  hipStream_t stream);

@@ -80,10 +80,13 @@ __global__ __launch_bounds__(64) void refine_count_kernel(const int32_t* __restr
 }
 
 // In-place inclusive scan of row_ptr64[1 .. n] by one workgroup, in chunks of
-// kScanThreads entries.
+// kScanThreads entries.  Each fine row holds at most i + 1 entries, so a chunk's
+// sum fits int32; the running total is kept in int64 and stored saturated at
+// INT32_MAX (reachable only when coarse rows share entries), which the host
+// reports as an overflow of the output's capacity.
 __global__ __launch_bounds__(kScanThreads) void refine_scan_kernel(int n, int32_t* __restrict__ row_ptr64) {
   __shared__ int wsum[kScanThreads / 64];
-  __shared__ int carry_s;
+  __shared__ int64_t carry_s;
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
   if (t == 0) carry_s = 0;
   __syncthreads();
@@ -93,9 +96,9 @@ __global__ __launch_bounds__(kScanThreads) void refine_scan_kernel(int n, int32_
     const int incl = wave_sum_scan(x, l);
     if (l == 63) wsum[w] = incl;
     __syncthreads();
-    int before = carry_s;
+    int64_t before = carry_s;
     for (int v = 0; v < w; ++v) before += wsum[v];
-    if (k < n) row_ptr64[k + 1] = before + incl;
+    if (k < n) row_ptr64[k + 1] = (int32_t)min(before + incl, (int64_t)INT32_MAX);
     __syncthreads();
     if (t == kScanThreads - 1) carry_s = before + incl;
     __syncthreads();
@@ -106,14 +109,18 @@ __global__ __launch_bounds__(64) void refine_emit_kernel(const int32_t* __restri
                                                          const int32_t* __restrict__ col_idx,
                                                          int64_t nnz, int m,
                                                          const int32_t* __restrict__ row_ptr64,
-                                                         int32_t* __restrict__ col_idx64) {
+                                                         int32_t* __restrict__ col_idx64,
+                                                         int64_t capacity) {
   const int i = blockIdx.x, l = threadIdx.x, I = i / m;
-  int pos = row_ptr64[i];
+  int64_t pos = row_ptr64[i];
   for_accepted(row_ptr, col_idx, nnz, I, l, [&](int J, bool ok) {
     const int k = ok ? (J < I ? m : i - m * I + 1) : 0;
     const int incl = wave_sum_scan(k, l);
-    const int at = pos + incl - k;
-    for (int b = 0; b < k; ++b) col_idx64[at + b] = m * J + b;
+    const int64_t at = pos + incl - k;
+    // rows that share input entries (a row_ptr that is not non-decreasing) can
+    // push the total past the host's bound: such entries are counted, not written
+    for (int b = 0; b < k; ++b)
+      if (at + b < capacity) col_idx64[at + b] = m * J + b;
     pos += __shfl(incl, 63, 64);
   });
 }
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(64) void refine_emit_kernel(const int32_t* __restri
 
 hipError_t launch_refine_schedule(int64_t S, int block, const int32_t* row_ptr,
                                   const int32_t* col_idx, int64_t nnz, int32_t* row_ptr64,
-                                  int32_t* col_idx64, hipStream_t stream) {
+                                  int32_t* col_idx64, int64_t capacity, hipStream_t stream) {
   const int64_t nb64 = (S + 63) / 64;
   const int m = block / 64;
   if (nb64 == 0) return launch_dense_schedule(0, row_ptr64, col_idx64, stream);  // row_ptr64 = {0}
@@ -133,7 +140,7 @@ hipError_t launch_refine_schedule(int64_t S, int block, const int32_t* row_ptr,
   hipLaunchKernelGGL(refine_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, (int)nb64, row_ptr64);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(refine_emit_kernel, dim3((unsigned)nb64), dim3(64), 0, stream, row_ptr, col_idx, nnz,
-                     m, row_ptr64, col_idx64);
+                     m, row_ptr64, col_idx64, capacity);
   return hipGetLastError();
 }
 

@@ -95,10 +95,13 @@ __global__ __launch_bounds__(64) void col_count_kernel(const uint32_t* __restric
   if (l < 32 && 32 * w + l < nb) counts[32 * w + l] = mine;
 }
 
+// Entries at or past `capacity` are counted in col_ptr but not written: a
+// row_ptr that is not non-decreasing lets rows share entries, and then the
+// column view can hold more entries than the CSR has.
 __global__ __launch_bounds__(64) void col_emit_kernel(const uint32_t* __restrict__ bits,
                                                       const int32_t* __restrict__ counts, int nb,
                                                       int32_t* __restrict__ col_ptr,
-                                                      int32_t* __restrict__ row_idx) {
+                                                      int32_t* __restrict__ row_idx, int64_t capacity) {
   const int w = blockIdx.x, l = threadIdx.x;
   int part = 0;
   for (int c = l; c < 32 * w; c += 64) part += counts[c];
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(64) void col_emit_kernel(const uint32_t* __restrict
       const bool set = (word >> b) & 1u;
       const uint64_t m = __ballot(set);
       const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-      if (set) row_idx[run[b] + below] = i;
+      if (set && run[b] + below < capacity) row_idx[run[b] + below] = i;
       run[b] += __popcll(m);
     }
   }
@@ -136,7 +139,7 @@ size_t transpose_workspace_bytes(int64_t nb) {
 
 hipError_t launch_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* col_idx,
                                      int64_t nnz, int32_t* col_ptr, int32_t* row_idx,
-                                     void* workspace, hipStream_t stream) {
+                                     int64_t row_capacity, void* workspace, hipStream_t stream) {
   const int64_t nw = (nb + 31) / 32;
   uint32_t* bits = (uint32_t*)workspace;
   int32_t* counts = (int32_t*)(bits + nw * nb);
@@ -149,7 +152,7 @@ hipError_t launch_schedule_transpose(int64_t nb, const int32_t* row_ptr, const i
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(col_emit_kernel, dim3((unsigned)(nw > 0 ? nw : 1)), dim3(64), 0, stream, bits, counts,
-                     (int)nb, col_ptr, row_idx);
+                     (int)nb, col_ptr, row_idx, row_capacity);
   return hipGetLastError();
 }
 

@@ -341,7 +341,8 @@ int tsa_refine_schedule(int64_t S, int32_t block, const int32_t* row_ptr, const 
   if (nnz > 0 && (rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
   if (need > 0 && (rc = check_device_ptr(col_idx64, "col_idx64")) != TSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = tsa::launch_refine_schedule(S, block, row_ptr, col_idx, nnz, row_ptr64, col_idx64, st);
+  hipError_t e = tsa::launch_refine_schedule(S, block, row_ptr, col_idx, nnz, row_ptr64, col_idx64,
+                                             capacity, st);
   if (e != hipSuccess) return hip_fail(e, "refine kernels");
   if (nnz_host) {
     int32_t n = 0;
@@ -349,6 +350,11 @@ int tsa_refine_schedule(int64_t S, int32_t block, const int32_t* row_ptr, const 
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e, "reading nnz");
     *nnz_host = n;
+    if (n > capacity)
+      return fail(TSA_ERR_SCHEDULE,
+                  "%s: the refined schedule needs %lld entries > capacity %lld (rows of the input share "
+                  "entries: row_ptr is not non-decreasing); entries past the capacity were not written",
+                  fn, (long long)n, (long long)capacity);
   }
   return ok();
 }
@@ -392,7 +398,7 @@ int tsa_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* co
   if (nb > 0 && (rc = check_device_ptr(workspace, "workspace")) != TSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = tsa::launch_schedule_transpose(nb, row_ptr, col_idx, nnz, col_ptr, row_idx,
-                                                workspace, st);
+                                                row_capacity, workspace, st);
   if (e != hipSuccess) return hip_fail(e, "transpose kernels");
   if (nnz_host) {
     int32_t n = 0;
@@ -400,6 +406,11 @@ int tsa_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* co
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e, "reading nnz");
     *nnz_host = n;
+    if (n > row_capacity)
+      return fail(TSA_ERR_SCHEDULE,
+                  "%s: the column view has %lld entries > row_capacity %lld (rows share entries: "
+                  "row_ptr is not non-decreasing); entries past the capacity were not written",
+                  fn, (long long)n, (long long)row_capacity);
   }
   return ok();
 }

@@ -179,9 +179,16 @@ int64_t tsa_refine_schedule_max_nnz(int64_t S, int32_t block, int64_t nnz);
  *   row_ptr, col_idx   device int32 input CSR, `nnz` readable entries.
  *   row_ptr64   device int32 [ceil(S / 64) + 1], written.
  *   col_idx64   device int32 [capacity], entries [0, row_ptr64[n]) written;
- *               capacity >= tsa_refine_schedule_max_nnz(S, block, nnz).
+ *               capacity >= tsa_refine_schedule_max_nnz(S, block, nnz).  That
+ *               bound holds when row_ptr is non-decreasing.  Rows that share
+ *               input entries (a row_ptr that is not) can need more; entries at
+ *               or past `capacity` are then counted in row_ptr64 (saturated at
+ *               INT32_MAX) but never written.
  *   nnz_host    host int64 or NULL: when not NULL the call waits for the stream
- *               and stores the output's entry count there.
+ *               and stores the output's entry count there; a count above
+ *               `capacity` returns TSA_ERR_SCHEDULE (the one error found after
+ *               the kernels ran: row_ptr64 and the first `capacity` entries are
+ *               then written).
  * block = 64 returns the input's accepted entries unchanged.  Errors: negative
  * sizes (TSA_ERR_INVALID_ARG), an unsupported block or too many output rows
  * (TSA_ERR_UNSUPPORTED), more entries than int32 offsets hold (TSA_ERR_SHAPE), a
@@ -289,14 +296,19 @@ size_t tsa_schedule_transpose_workspace_bytes(int64_t nb);
  *               ascending within 0..i as the schedule contract asks).
  *   col_ptr     device int32 [nb + 1], written.
  *   row_idx     device int32 [row_capacity], entries [0, col_ptr[nb]) written;
- *               row_capacity >= min(nnz, nb*(nb+1)/2), so it can never overflow.
+ *               row_capacity >= min(nnz, nb*(nb+1)/2), which holds every entry
+ *               when row_ptr is non-decreasing.  Rows that share entries (a
+ *               row_ptr that is not) can need more; entries at or past
+ *               row_capacity are then counted in col_ptr but never written.
  *   workspace   device, >= tsa_schedule_transpose_workspace_bytes(nb) bytes,
  *               256-byte aligned, any contents on entry (NULL allowed when nb = 0).
  *   nnz_host    host int64 or NULL: when not NULL the call waits for the stream
- *               and stores col_ptr[nb] there.
+ *               and stores col_ptr[nb] there; a count above row_capacity returns
+ *               TSA_ERR_SCHEDULE (found after the kernels ran: col_ptr and the
+ *               first row_capacity entries are then written).
  * Errors: negative sizes (TSA_ERR_INVALID_ARG), nb > TSA_MAX_SCHEDULE_BLOCKS
  * (TSA_ERR_UNSUPPORTED), a short row_idx (TSA_ERR_SCHEDULE), a short or misaligned
- * workspace, NULL or non-device pointers.  Nothing is written on error.
+ * workspace, NULL or non-device pointers.  Nothing is written on these errors.
  */
 int tsa_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* col_idx,
                            int64_t nnz, int32_t* col_ptr, int32_t* row_idx, int64_t row_capacity,

@@ -1,5 +1,6 @@
 """Seeded sweep of mixed configurations through the C ABI against the fp64 oracle:
-head dim 32, 64, 128 or 256, fp16 or bf16, 1-2 batches x 1-2 heads, S from 1 to
+head dim 32, 64, 128 or 256, fp16 or bf16, 1, 2 or 4 batches x 1, 2 or 4 heads
+(so that lane counts of 8 and 16 take the kernels' per-XCD lane order), S from 1 to
 about 2200 (ragged tails, single partial blocks), and random, dense causal,
 fixed-segment or GPU-built topology schedules.  Each case checks the forward
 output, and for D <= 128 the lse and the three gradients, to the bars of the
@@ -33,7 +34,7 @@ def _config(case):
     D = int(rng.choice([32, 64, 128, 256]))
     dtype = "bf16" if rng.random() < 0.5 else "fp16"
     S = int(rng.integers(1, 2200 if D < 256 else 900))
-    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    B, H = int(rng.choice([1, 2, 4])), int(rng.choice([1, 2, 4]))  # lanes 1..16
     kind = ["random", "dense", "segments", "topology"][int(rng.integers(0, 4))]
     params = (float(rng.uniform(0.05, 0.9)), bool(rng.random() < 0.5), int(rng.integers(1, 6)),
               int(rng.integers(0, 3)), int(rng.integers(0, 4)), int(rng.integers(0, 8)))
