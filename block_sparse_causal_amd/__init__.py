@@ -92,6 +92,8 @@ def _load():
     lib.tsa_build_schedule_ex.argtypes = [
         vp, i32, i64, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, sz, ctypes.POINTER(i64), vp
     ]
+    lib.tsa_build_schedule_noalloc.restype = ctypes.c_int
+    lib.tsa_build_schedule_noalloc.argtypes = [vp, i32, i64, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp]
     lib.tsa_dense_causal_schedule.restype = ctypes.c_int
     lib.tsa_dense_causal_schedule.argtypes = [i64, vp, vp, i64, vp]
     lib.tsa_segment_schedule_nnz.restype = i64
@@ -257,6 +259,31 @@ def build_schedule_into(keys: torch.Tensor, bufs: ScheduleBuffers) -> None:
             _stream(keys.device),
         )
     _check(status, "build_schedule_into")
+
+
+def build_schedule_noalloc(keys: torch.Tensor, row_ptr: torch.Tensor, col_idx: torch.Tensor, block: int,
+                           sink: int, local_radius: int, topk: int, per_row: bool = False,
+                           salience: torch.Tensor | None = None) -> None:
+    """Queue a schedule build into caller-provided int32 ``row_ptr`` [nb+1] and
+    ``col_idx`` (capacity = its length) on the current stream, with the library's
+    fixed device workspace (tsa_build_schedule_noalloc): no allocation, no host
+    wait.  The entry count is row_ptr[nb]."""
+    if keys.dim() == 4:
+        keys = keys[0, 0]
+    if keys.dim() != 2 or not keys.is_contiguous() or not keys.is_cuda:
+        raise ValueError("keys must be a contiguous [S, D] GPU tensor")
+    code = _dtype_code(keys, "keys")
+    _check_index("row_ptr", row_ptr, keys.device)
+    _check_index("col_idx", col_idx, keys.device)
+    S, D = keys.shape
+    if row_ptr.numel() != -(-S // block) + 1:
+        raise ValueError(f"row_ptr must have ceil(S/block)+1 = {-(-S // block) + 1} entries")
+    with torch.cuda.device(keys.device):
+        status = _lib.tsa_build_schedule_noalloc(
+            _ptr(keys), code, S, D, block, sink, local_radius, topk, 1 if per_row else 0, _ptr(row_ptr),
+            _ptr(col_idx), col_idx.numel(), _ptr(salience), _stream(keys.device),
+        )
+    _check(status, "build_schedule_noalloc")
 
 
 def refine_schedule(row_ptr: torch.Tensor, col_idx: torch.Tensor, S: int, block: int):

@@ -45,6 +45,9 @@ struct ScheduleWorkspace {
 };
 constexpr int kLdsDistBlocks = 128;  // distance matrix kept in LDS up to this many blocks
 size_t schedule_workspace_bytes(int64_t nb, int64_t D);
+// Device address (current device) of the library's fixed builder workspace of
+// TSA_NOALLOC_SCRATCH_BYTES bytes (see schedule_build.hip).
+hipError_t noalloc_scratch(void** ptr);
 // block: rows per key block, a positive multiple of 64; nb = ceil(S / block).
 hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t D, int block,
                                  int sink, int local_radius, int topk, bool per_row,

@@ -39,8 +39,10 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 
 #include "kernels.h"
+#include "tsa.h"
 
 namespace tsa {
 namespace {
@@ -1517,6 +1519,39 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 }  // namespace
 
 size_t schedule_workspace_bytes(int64_t nb, int64_t D) { return workspace_layout(nb, D).total; }
+
+// The builder's workspace for callers that cannot allocate
+// (tsa_build_schedule_noalloc): a fixed array in device memory, one copy per
+// GPU, held until the process ends.  Every no-allocation build on a GPU uses
+// that GPU's copy, so two such builds that overlap on one GPU race.  The
+// builder needs no part of its workspace cleared.  In host code `scratch` only
+// names the symbol; its device address comes from noalloc_scratch().
+static __device__ __align__(256) unsigned char scratch[TSA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up (with that
+// device current) on the first call per device and kept.
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex lookup;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> hold(lookup);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t D, int block,
                                  int sink, int local_radius, int topk, bool per_row,

@@ -166,11 +166,12 @@ int tsa_build_schedule(const void* keys, int32_t dtype, int64_t S, int64_t D, in
                                nnz_host, stream);
 }
 
-int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
-                          int32_t sink, int32_t local_radius, int32_t topk, int32_t topk_scope,
-                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
-                          double* salience, void* workspace, size_t workspace_bytes,
-                          int64_t* nnz_host, void* stream) {
+namespace {
+
+// Checks of a schedule build that need no GPU call, except the workspace's.
+int check_build_args(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
+                     int32_t sink, int32_t local_radius, int32_t topk, int32_t topk_scope,
+                     int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity) {
   if (topk_scope != TSA_TOPK_GLOBAL && topk_scope != TSA_TOPK_PER_ROW)
     return fail(TSA_ERR_INVALID_ARG,
                 "tsa_build_schedule: topk_scope must be TSA_TOPK_GLOBAL or TSA_TOPK_PER_ROW, got %d",
@@ -202,10 +203,41 @@ int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D,
   if (need > INT32_MAX)
     return fail(TSA_ERR_SHAPE, "tsa_build_schedule: schedule would exceed int32 offsets");
   if (nb > 0) {
-    if (keys == nullptr || col_idx == nullptr || workspace == nullptr)
-      return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: keys, col_idx and workspace must be non-NULL");
+    if (keys == nullptr || col_idx == nullptr)
+      return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: keys and col_idx must be non-NULL");
     if (((uintptr_t)keys) % 2 != 0)
       return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: keys must be 2-byte aligned");
+  }
+  return TSA_OK;
+}
+
+// Device checks of the build's pointers (the workspace's are the caller's).
+int check_build_ptrs(const void* keys, int64_t nb, int32_t* row_ptr, int32_t* col_idx,
+                     double* salience) {
+  int rc;
+  if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
+  if (nb > 0) {
+    if ((rc = check_device_ptr(keys, "keys")) != TSA_OK) return rc;
+    if ((rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
+    if (salience && (rc = check_device_ptr(salience, "salience")) != TSA_OK) return rc;
+  }
+  return TSA_OK;
+}
+
+}  // namespace
+
+int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
+                          int32_t sink, int32_t local_radius, int32_t topk, int32_t topk_scope,
+                          int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                          double* salience, void* workspace, size_t workspace_bytes,
+                          int64_t* nnz_host, void* stream) {
+  int rc = check_build_args(keys, dtype, S, D, block, sink, local_radius, topk, topk_scope, row_ptr,
+                            col_idx, col_capacity);
+  if (rc != TSA_OK) return rc;
+  const int64_t nb = (S + block - 1) / block;
+  if (nb > 0) {
+    if (workspace == nullptr)
+      return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: workspace must be non-NULL");
     const size_t ws = tsa::schedule_workspace_bytes(nb, D);
     if (workspace_bytes < ws)
       return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: workspace of %zu bytes < required %zu",
@@ -213,14 +245,8 @@ int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D,
     if (((uintptr_t)workspace) % 256 != 0)
       return fail(TSA_ERR_INVALID_ARG, "tsa_build_schedule: workspace must be 256-byte aligned");
   }
-  int rc;
-  if ((rc = check_device_ptr(row_ptr, "row_ptr")) != TSA_OK) return rc;
-  if (nb > 0) {
-    if ((rc = check_device_ptr(keys, "keys")) != TSA_OK) return rc;
-    if ((rc = check_device_ptr(col_idx, "col_idx")) != TSA_OK) return rc;
-    if ((rc = check_device_ptr(workspace, "workspace")) != TSA_OK) return rc;
-    if (salience && (rc = check_device_ptr(salience, "salience")) != TSA_OK) return rc;
-  }
+  if ((rc = check_build_ptrs(keys, nb, row_ptr, col_idx, salience)) != TSA_OK) return rc;
+  if (nb > 0 && (rc = check_device_ptr(workspace, "workspace")) != TSA_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = tsa::launch_build_schedule(keys, dtype == TSA_BF16, S, D, block, sink, local_radius,
                                             topk, topk_scope == TSA_TOPK_PER_ROW, row_ptr, col_idx,
@@ -233,6 +259,34 @@ int tsa_build_schedule_ex(const void* keys, int32_t dtype, int64_t S, int64_t D,
     if (e != hipSuccess) return hip_fail(e, "reading nnz");
     *nnz_host = n;
   }
+  return ok();
+}
+
+int tsa_build_schedule_noalloc(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
+                               int32_t sink, int32_t local_radius, int32_t topk, int32_t topk_scope,
+                               int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                               double* salience, void* stream) {
+  const char* fn = "tsa_build_schedule_noalloc";
+  int rc = check_build_args(keys, dtype, S, D, block, sink, local_radius, topk, topk_scope, row_ptr,
+                            col_idx, col_capacity);
+  if (rc != TSA_OK) return rc;
+  const int64_t nb = (S + block - 1) / block;
+  const size_t ws = nb > 0 ? tsa::schedule_workspace_bytes(nb, D) : 0;
+  if (ws > TSA_NOALLOC_SCRATCH_BYTES)
+    return fail(TSA_ERR_UNSUPPORTED,
+                "%s: the build needs %zu bytes of workspace, more than the library's fixed %zu "
+                "(tsa_build_schedule takes a caller-owned workspace of any size)",
+                fn, ws, (size_t)TSA_NOALLOC_SCRATCH_BYTES);
+  if ((rc = check_build_ptrs(keys, nb, row_ptr, col_idx, salience)) != TSA_OK) return rc;
+  void* scratch = nullptr;
+  if (nb > 0) {
+    hipError_t e = tsa::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "looking up the builder's device scratch");
+  }
+  hipError_t e = tsa::launch_build_schedule(keys, dtype == TSA_BF16, S, D, block, sink, local_radius,
+                                            topk, topk_scope == TSA_TOPK_PER_ROW, row_ptr, col_idx,
+                                            col_capacity, salience, scratch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "schedule kernels");
   return ok();
 }
 

@@ -198,6 +198,34 @@ int tsa_refine_schedule(int64_t S, int32_t block, const int32_t* row_ptr, const 
                         int64_t nnz, int32_t* row_ptr64, int32_t* col_idx64, int64_t capacity,
                         int64_t* nnz_host, void* stream);
 
+/* Size of the library's fixed builder workspace on each GPU (tsa_build_schedule_noalloc). */
+#define TSA_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/*
+ * tsa_build_schedule_ex without a workspace argument and without allocating,
+ * for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The build runs in a
+ * fixed array of TSA_NOALLOC_SCRATCH_BYTES bytes that the library holds in each
+ * GPU's memory until the process ends; the call allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine) and does not wait for the stream.
+ *   Every argument is that of tsa_build_schedule_ex; the count of entries is
+ *   row_ptr[nb] (read it back after the stream is done).
+ *   Limit: builds whose tsa_build_schedule_workspace_bytes(S, D, block) exceeds
+ *   TSA_NOALLOC_SCRATCH_BYTES are rejected with TSA_ERR_UNSUPPORTED before any GPU
+ *   work (nb <= 512 blocks fits at D <= 256, e.g. 32768 tokens at block 64).
+ *   Concurrency: all no-allocation builds on one GPU share its array, so two of
+ *   them that may overlap in time (different streams, or different host threads
+ *   on one stream without ordering) race; calls ordered on one stream do not.
+ *   The array needs no clearing between calls (the builder's state carries a
+ *   per-call token), and a build captured in a HIP graph rebuilds on replay.
+ * Errors: those of tsa_build_schedule_ex, plus TSA_ERR_UNSUPPORTED for the limit
+ * and TSA_ERR_HIP if the array's device address cannot be looked up.
+ */
+int tsa_build_schedule_noalloc(const void* keys, int32_t dtype, int64_t S, int64_t D, int32_t block,
+                               int32_t sink, int32_t local_radius, int32_t topk, int32_t topk_scope,
+                               int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                               double* salience, void* stream);
+
 /*
  * The dense causal (lower-triangular) CSR for nb blocks: row i lists 0..i.
  * (PR page, Summary: the tests cover the dense causal CSR; Local benchmark: the dense CSR

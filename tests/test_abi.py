@@ -296,3 +296,23 @@ def test_refine_checks_before_gpu(lib):
     assert call(S=64 * ((1 << 22) + 1), nnz=0, cap=0) == -2
     assert call(cap=39) == -4 and b"capacity" in lib.tsa_last_error()
     assert call() == -1 and b"NULL" in lib.tsa_last_error()
+
+
+def test_noalloc_build_checks_before_gpu(lib):
+    """tsa_build_schedule_noalloc: the argument checks of tsa_build_schedule_ex, then
+    the fixed array's size limit, both before any GPU call."""
+    vp = ctypes.c_void_p
+    base = 1 << 40  # never dereferenced: every check below precedes any GPU call
+
+    def call(S=1024, D=64, block=64, scope=0, cap=1000, row_ptr=base):
+        return lib.tsa_build_schedule_noalloc(vp(base), 1, S, D, block, 1, 1, 2, scope, vp(row_ptr),
+                                              vp(base + (1 << 24)), cap, vp(None), vp(None))
+
+    assert call(scope=5) == -1
+    assert call(block=96) == -2
+    assert call(row_ptr=None) == -1
+    assert call(cap=3) == -4
+    big_S = 65536  # 1024 blocks: an 8 MB distance matrix does not fit the fixed array
+    assert lib.tsa_build_schedule_workspace_bytes(big_S, 64, 64) > (4 << 20)
+    assert call(S=big_S, cap=1 << 20) == -2
+    assert b"workspace" in lib.tsa_last_error()
