@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t nnz,
-    int S, int nb, int64_t lane_base, float scale_log2, float inv_scale_log2) {
+    int S, int nb, int64_t lane_base, int pos_base, float scale_log2, float inv_scale_log2) {
   using E = Elem<BF16>;
   constexpr int kStepsD = D / 16;                  // 16-deep steps of Q.K^T
   constexpr int kTilesD = D / 32;                  // 32-row tiles of O^T
@@ -92,22 +92,16 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   const int g = l >> 4;     // 16-lane group
   const int gi = l & 15;
 
-  // Workgroup b runs on XCD b % 8; XCD x takes lane group x (lanes / 8 lanes)
-  // and position u / lx = nb - 1 - i of its lanes in turn.
-  const uint32_t G = gridDim.x;
-  const uint32_t bid = blockIdx.x;
-  const int lanes = (int)(G / (uint32_t)nb);
+  // Grid: x = lane, y = position nb - 1 - i (from pos_base).  Workgroup x + y X
+  // runs on XCD x % 8; with X a multiple of 8, XCD c takes lanes c X/8 ..
+  // (c + 1) X/8 - 1, so its L2 holds those lanes' K/V.  No division.
+  const uint32_t X = gridDim.x, x = blockIdx.x;
   int64_t lane;
-  int i;
-  if (G % 8u == 0u && lanes % 8 == 0) {
-    const uint32_t lx = (uint32_t)lanes / 8u;
-    const uint32_t u = bid / 8u;
-    lane = lane_base + (int64_t)((bid % 8u) * lx + u % lx);
-    i = nb - 1 - (int)(u / lx);
-  } else {
-    lane = lane_base + (int64_t)(bid % (uint32_t)lanes);
-    i = nb - 1 - (int)(bid / (uint32_t)lanes);
-  }
+  if (X % 8u == 0u)
+    lane = lane_base + (int64_t)((x % 8u) * (X / 8u) + x / 8u);
+  else
+    lane = lane_base + (int64_t)x;
+  const int i = nb - 1 - (pos_base + (int)blockIdx.y);
 
   const int64_t lane_off = lane * (int64_t)S * D;
   const uint16_t* kg = k + lane_off;
@@ -129,12 +123,23 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   // tile is a whole number of kWaves-piece rounds, so the first half of the ops
   // fill K and the second half V (known at compile time).
   static_assert((kTileBytes / 1024) % kWaves == 0 && kFillOps % 2 == 0, "fill ops split K | V");
+  // Consecutive ops of a tile half are kOpRows rows apart.  When that is a
+  // multiple of 16 (D <= 128), the key permutation (bits 2, 3 of the row) and
+  // both swizzles (bits 0..3) agree between them, so later ops only add the row
+  // offset.
+  constexpr int kOpRows = kWaves * 64 / kChunksPerRow;
+  constexpr bool kDerive = kOpRows % 16 == 0;
   uint32_t fill_off[kFillOps];
 #pragma unroll
   for (int op = 0; op < kFillOps; ++op) {
     constexpr int kHalfOps = kFillOps / 2;
     const bool is_v = op >= kHalfOps;
-    const int cc = ((is_v ? op - kHalfOps : op) * kWaves + w) * 64 + l;
+    const int oh = is_v ? op - kHalfOps : op;  // op within its tile half
+    if (kDerive && oh > 0) {
+      fill_off[op] = fill_off[op - oh] + (uint32_t)(oh * kOpRows * kRowBytes);
+      continue;
+    }
+    const int cc = (oh * kWaves + w) * 64 + l;
     const int r = cc / kChunksPerRow, pc = cc % kChunksPerRow;
     const int key = is_v ? r : ((r & 32) | swap_bits23(r & 31));
     const int c = is_v ? (pc ^ v_swizzle<D>(r)) : (pc ^ k_swizzle<D>(r));
@@ -402,7 +407,8 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     const float fs = (m_use == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_use - m);
     const float fp = (m_p == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_p - m);
     const float l_tot = l_half * fs + l_p * fp;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    // v_rcp_f32 (1 ulp): l_tot >= 2^-8 here, far from the denormal range
+    const float inv = l_tot > 0.0f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
     const float cs = fs * inv, cp = fp * inv;
     // log of the row's denominator in natural units: log2(sum 2^(z log2 e)) = m + log2(l_tot)
     if (KH == 0 && lse != nullptr && qrow < S)
@@ -453,17 +459,22 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, void* out, 
                         int64_t S, const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                         float scale_log2, hipStream_t stream) {
   const int64_t nb = (S + kBlock - 1) / kBlock;
-  // Keep grid * block below 2^32 work-items per launch: split over lanes.
-  const int64_t max_wg = (int64_t(1) << 31) / kThreads;
-  const int64_t lanes_per_launch = max_wg / nb > 0 ? max_wg / nb : 1;
-  for (int64_t l0 = 0; l0 < lanes; l0 += lanes_per_launch) {
-    const int64_t nl = lanes - l0 < lanes_per_launch ? lanes - l0 : lanes_per_launch;
-    hipLaunchKernelGGL((attention_fwd_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
-                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (uint16_t*)out, lse, row_ptr, col_idx, nnz, (int)S, (int)nb, l0, scale_log2,
-                       1.0f / scale_log2);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+  // grid.x = lanes (at most 2^31 work-items per launch, in multiples of 8 lanes
+  // so that every launch keeps the per-XCD lane order), grid.y = positions (at
+  // most 65535 per launch); the positions of one lane range go longest first.
+  const int64_t max_lanes = ((int64_t(1) << 31) / kThreads) & ~int64_t(7);
+  constexpr int64_t kMaxPositions = 65535;
+  for (int64_t l0 = 0; l0 < lanes; l0 += max_lanes) {
+    const int64_t nl = lanes - l0 < max_lanes ? lanes - l0 : max_lanes;
+    for (int64_t p0 = 0; p0 < nb; p0 += kMaxPositions) {
+      const int64_t np = nb - p0 < kMaxPositions ? nb - p0 : kMaxPositions;
+      hipLaunchKernelGGL((attention_fwd_kernel<D, BF16>), dim3((unsigned)nl, (unsigned)np), dim3(kThreads),
+                         0, stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                         (uint16_t*)out, lse, row_ptr, col_idx, nnz, (int)S, (int)nb, l0, (int)p0,
+                         scale_log2, 1.0f / scale_log2);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
   }
   return hipSuccess;
 }
@@ -474,6 +485,11 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
                                 bool bf16, int64_t lanes, int64_t S, int D, const int32_t* row_ptr,
                                 const int32_t* col_idx, int64_t nnz, float scale_log2,
                                 hipStream_t stream) {
+  // Head dim 128: two query blocks per workgroup share each 32 KB K/V stage.  At
+  // 64 the one-block kernel's smaller workgroups are faster.
+  if (D == 128 && attention_fwd_pair_supported(D, S))
+    return launch_attention_fwd_pair(q, k, v, out, lse, bf16, lanes, S, D, row_ptr, col_idx, nnz,
+                                     scale_log2, stream);
 #define TSA_FWD_CASE(DD)                                                                              \
   if (D == DD)                                                                                      \
     return bf16 ? launch_typed<DD, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream) \
