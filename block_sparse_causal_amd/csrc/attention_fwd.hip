@@ -203,7 +203,15 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   for (int dt = 0; dt < kTilesD; ++dt) o[dt] = f32x16{};
   float m_use = -__builtin_inff();  // exponent offset in use (log2 units)
   float thr_raw = -__builtin_inff();  // trigger threshold for the raw-score max (below)
-  float l_run = 0.0f;               // this lane's share of the denominator
+  // Denominator.  At head dim <= 64 the softmax, not the matrix core, bounds
+  // the block loop, so the row sums of the rounded P run on the MFMA (two
+  // 16x16x32 products against a 0/1 selector, see row_sum_selector): lane l
+  // then holds the whole sum of query l % 32 over this key half in l_acc[0].
+  // Otherwise each lane sums its own half-wave's share with v_dot2.
+  constexpr bool kMfmaSums = D <= 64;
+  float l_run = 0.0f;
+  f32x4 l_acc = f32x4{};
+  const u32x4 sum_sel = row_sum_selector<E>(l);
   // Until the first offset is set nothing has been accumulated (O and l are 0 in
   // every lane), so that first rescale has nothing to scale (wave-uniform flag).
   bool started = false;
@@ -271,7 +279,10 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
       const float thr = (m_new + kRescaleSlack) * inv_scale_log2;
       thr_raw = thr - __builtin_fabsf(thr) * 0x1p-20f;
       if (started) {
-        l_run *= alpha;
+        if constexpr (kMfmaSums)
+          l_acc *= alpha;
+        else
+          l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
       }
@@ -302,7 +313,12 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) l_run = E::add_pair(pb[gg][x], l_run);
+      for (int x = 0; x < 4; ++x)
+        if constexpr (!kMfmaSums) l_run = E::add_pair(pb[gg][x], l_run);
+    if constexpr (kMfmaSums) {
+      l_acc = E::mfma16(sum_sel, pb[0], l_acc);
+      l_acc = E::mfma16(sum_sel, pb[1], l_acc);
+    }
     lds_wait_all(va);
 #pragma unroll
     for (int dt = 0; dt < kTilesD; ++dt)
@@ -361,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
   // after one barrier each wave combines and stores its half.  The stage
   // buffers are free here (every wave has passed the last barrier).
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));  // no load of this wave outlives it (empty rows)
-  const float l_half = sum_with_other_half(l_run);
+  const float l_half = kMfmaSums ? l_acc[0] : sum_with_other_half(l_run);
   // Wave kh keeps half of the O registers: whole tiles when there are two or more
   // (kHalfTiles each), else (D = 32) register groups 2kh, 2kh + 1 of the one tile.
   constexpr int kHalfTiles = kTilesD / 2;

@@ -13,6 +13,7 @@ namespace tile {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -35,6 +36,12 @@ struct Elem<false> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+  // 16x16x32 MFMA (A 16 x 32, B 32 x 16, C 16 x 16)
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static constexpr uint32_t kOnePair = 0x3C003C00u;  // two 1.0 halves
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     f16x2 r = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, r);
@@ -55,6 +62,11 @@ struct Elem<true> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static constexpr uint32_t kOnePair = 0x3F803F80u;  // two 1.0 bf16 values
   static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
     bf16x2 r = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, r);
@@ -68,6 +80,19 @@ struct Elem<true> {
                                            false);
   }
 };
+
+// A operand of a 16x16x32 MFMA that sums, for the query of each lane, a P^T
+// register group taken as its B operand.  A P^T group (8 values per lane: keys
+// 8h .. 8h+7 of a 16-key chunk for query l % 32, h = l / 32) read as the B
+// operand puts query 16 (kg % 2) + c in column c of k-group kg = l / 16.  With
+// A[m][k] = 1 exactly when (k / 8) % 2 == (m / 4) % 2, row m of C sums the
+// k-groups of parity (m / 4) % 2, and C's lane l (rows 4 (l / 16) .. +3, column
+// l % 16) then holds the chunk's sum for query l % 32 over both h.
+template <typename E>
+__device__ __forceinline__ u32x4 row_sum_selector(int l) {
+  const uint32_t v = ((l >> 4) & 1) == ((l >> 2) & 1) ? E::kOnePair : 0u;
+  return u32x4{v, v, v, v};
+}
 
 // Value of the partner lane l ^ 32, combined with the own value.
 __device__ __forceinline__ float max_with_other_half(float x) {
