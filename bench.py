@@ -32,7 +32,8 @@ METRIC = "scheduled-attn fwd effective TFLOP/s (% MFMA peak) + sparse/dense-CSR 
 PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
 PARITY_BAR = {"fp16": 2e-3, "bf16": 1e-2}  # max abs error of the output against the fp64 oracle
 # sources of the attention forward kernel (its own file and the shared device helpers)
-ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_causal_amd", "csrc", f) for f in ("attention_fwd.hip", "mfma_tile.h")]
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_causal_amd", "csrc", f)
+                for f in ("attention_fwd.hip", "attention_fwd_pair.hip", "mfma_tile.h")]
 
 
 def _kernel_hash() -> str:
@@ -43,10 +44,10 @@ def _kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str):
-    """HBM bytes per attention launch from a committed rocprofv3 --pmc summary,
-    only if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"attention_fwd_{workload}_pmc.txt")
+def _profile_fields(name: str):
+    """key: value lines of a committed rocprofv3 summary under profiles/, or None
+    when it is missing or was taken on another attention kernel source."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -57,8 +58,30 @@ def _traffic(workload: str):
                 fields[key.strip()] = val.strip()
     if fields.get("kernel_source_sha256_16") != _kernel_hash():
         return None
+    return fields
+
+
+def _traffic(workload: str):
+    """HBM bytes per attention launch from a committed rocprofv3 --pmc summary,
+    only if it was taken on the current kernel source."""
+    fields = _profile_fields(f"attention_fwd_{workload}_pmc.txt")
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields["hbm_bytes_per_launch"]) if fields else None
+    except (KeyError, ValueError):
+        return None
+
+
+def _sq_counters(workload: str):
+    """Matrix-core and VALU counters of the attention kernel from a committed
+    rocprofv3 --pmc summary (per launch), only if it was taken on the current
+    kernel source."""
+    fields = _profile_fields(f"attention_fwd_{workload}_sq.txt")
+    if not fields:
+        return None
+    keys = ("mfma_busy_frac", "clock_ghz", "valu_insts_per_mfma", "trans_insts_per_mfma",
+            "wait_inst_frac", "kernel_us")
+    try:
+        return {key: float(fields[key]) for key in keys}
     except (KeyError, ValueError):
         return None
 
@@ -422,6 +445,9 @@ def main() -> int:
             "traffic": traffic,
         },
         "cpu_baseline": None,
+        # per-launch SQ counters of the attention kernel (profiles/attention_fwd_<workload>_sq.txt):
+        # MFMA-busy fraction of all SIMD cycles at the measured clock, and instruction mix
+        "counters": _sq_counters(name),
     }
     bad = None
     if not args.no_cpu_baseline:
