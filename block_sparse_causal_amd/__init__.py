@@ -264,14 +264,24 @@ def refine_schedule(row_ptr: torch.Tensor, col_idx: torch.Tensor, S: int, block:
     return rp, ci[: total.value]
 
 
-def dense_causal_schedule(nb: int, device) -> tuple[torch.Tensor, torch.Tensor]:
-    """Lower-triangular CSR for nb blocks on ``device`` (int32 row_ptr, col_idx)."""
+def dense_causal_schedule(nb: int, device, out: tuple[torch.Tensor, torch.Tensor] | None = None
+                          ) -> tuple[torch.Tensor, torch.Tensor]:
+    """Lower-triangular CSR for nb blocks on ``device`` (int32 row_ptr, col_idx).
+    ``out``: preallocated (row_ptr [nb+1], col_idx [>= nb(nb+1)/2]) to write into,
+    so that the call allocates nothing."""
     dev = torch.device(device)
     nnz = nb * (nb + 1) // 2
     with torch.cuda.device(dev):
-        row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=dev)
-        col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
-        status = _lib.tsa_dense_causal_schedule(nb, _ptr(row_ptr), _ptr(col_idx), nnz, _stream(dev))
+        if out is None:
+            row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+            col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+        else:
+            row_ptr, col_idx = out
+            _check_index("row_ptr", row_ptr, dev)
+            _check_index("col_idx", col_idx, dev)
+            if row_ptr.numel() != nb + 1 or col_idx.numel() < nnz:
+                raise ValueError("out must hold row_ptr [nb+1] and col_idx [>= nb(nb+1)/2]")
+        status = _lib.tsa_dense_causal_schedule(nb, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(), _stream(dev))
     _check(status, "dense_causal_schedule")
     return row_ptr, col_idx[:nnz]
 
@@ -371,6 +381,34 @@ def scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_p
             )
     _check(status, "scheduled_attention")
     return (out, lse) if return_lse else out
+
+
+def prepare_scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                                col_idx: torch.Tensor, out: torch.Tensor, sm_scale: float | None = None):
+    """``scheduled_attention(q, k, v, row_ptr, col_idx, out=out)`` with the
+    arguments checked and marshalled once: returns a callable that queues the
+    forward on the current stream of q's device with one C ABI call (which
+    still validates its arguments).  For loops that launch the same call many
+    times, where the per-call Python work would otherwise set the pace."""
+    code, B, H, S, D = _attention_shape(q, k, v)
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        _check_index(name, t, q.device)
+    if row_ptr.numel() != -(-S // BLOCK) + 1:
+        raise ValueError("row_ptr must have nb+1 entries")
+    if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
+    keep = (q, k, v, row_ptr, col_idx, out)  # the callable holds the tensors alive
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), code, B, H, S, D, _ptr(row_ptr), _ptr(col_idx),
+            col_idx.numel(), BLOCK, _scale_arg(sm_scale))
+    fn, dev = _lib.tsa_scheduled_attention_fwd, q.device
+
+    def call():
+        status = fn(*args, _stream(dev))
+        if status != TSA_OK:
+            _check(status, "scheduled_attention")
+
+    call.tensors = keep
+    return call
 
 
 def schedule_transpose(row_ptr: torch.Tensor, col_idx: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
