@@ -202,6 +202,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
 #pragma unroll
   for (int dt = 0; dt < kTilesD; ++dt) o[dt] = f32x16{};
   float m_use = -__builtin_inff();  // exponent offset in use (log2 units)
+  float neg_m = __builtin_inff();    // -m_use, the FMA addend of the exponents (written only on a rescale)
   float thr_raw = -__builtin_inff();  // trigger threshold for the raw-score max (below)
   // Denominator.  At head dim <= 64 the softmax, not the matrix core, bounds
   // the block loop, so the row sums of the rounded P run on the MFMA (two
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
       const float m_new = grow ? mp : m_use;
       const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
       m_use = m_new;
+      neg_m = -m_new;
       // a relative margin below the exact threshold, of either sign, covers the
       // rounding of mx * scale_log2, of the reciprocal and of the product
       const float thr = (m_new + kRescaleSlack) * inv_scale_log2;
@@ -306,8 +308,8 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * gg + 2 * x], scale_log2, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * gg + 2 * x + 1], scale_log2, -m_use));
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * gg + 2 * x], scale_log2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * gg + 2 * x + 1], scale_log2, neg_m));
         pb[gg][x] = E::pack(p0, p1);
       }
 #pragma unroll
