@@ -161,6 +161,85 @@ __device__ __forceinline__ int block_value(const int (&a)[SLOTS], int x) {
   return val;
 }
 
+// Value of `v` in lane (lane ^ M), for the partner patterns of a bitonic
+// network: M = 1, 2, 4, ..., 32 and the mirrors 3, 7, 15, 31, 63.  Each is a
+// DPP move or a lane swap, or two of them (lane ^ A ^ B).
+template <int M>
+__device__ __forceinline__ int lane_xor(int v) {
+  if constexpr (M == 1) return xchg_quad1(v);
+  else if constexpr (M == 2) return xchg_quad2(v);
+  else if constexpr (M == 3) return __builtin_amdgcn_mov_dpp(v, 0x1B, 0xF, 0xF, false);  // quad reversed
+  else if constexpr (M == 7) return xchg_half_mirror(v);
+  else if constexpr (M == 15) return xchg_mirror(v);
+  else if constexpr (M == 16) return xchg_xor16(v);
+  else if constexpr (M == 32) return xchg_xor32(v);
+  else if constexpr (M == 4) return lane_xor<7>(lane_xor<3>(v));
+  else if constexpr (M == 8) return lane_xor<15>(lane_xor<7>(v));
+  else if constexpr (M == 31) return lane_xor<15>(lane_xor<16>(v));
+  else {
+    static_assert(M == 63, "bitonic partner pattern");
+    return lane_xor<31>(lane_xor<32>(v));
+  }
+}
+
+// Compare-exchange of one bitonic step: the lower position of the pair keeps
+// the smaller of (d, t) and (od, ot), the upper one the larger.
+__device__ __forceinline__ void cx_take(unsigned long long& d, uint32_t& t, unsigned long long od,
+                                        uint32_t ot, bool lower) {
+  const bool other_less = od < d || (od == d && ot < t);
+  const bool other_more = d < od || (d == od && t < ot);
+  if (lower ? other_less : other_more) {
+    d = od;
+    t = ot;
+  }
+}
+template <int M>
+__device__ __forceinline__ void cx_lanes(unsigned long long& d, uint32_t& t, bool lower) {
+  const uint32_t lo = (uint32_t)lane_xor<M>((int)(uint32_t)d);
+  const uint32_t hi = (uint32_t)lane_xor<M>((int)(uint32_t)(d >> 32));
+  const uint32_t ot = (uint32_t)lane_xor<M>((int)t);
+  cx_take(d, t, ((unsigned long long)hi << 32) | lo, ot, lower);
+}
+
+// Ascending sort of P <= kThreads keys (length bits, tag), one per thread in
+// position order (P a power of two; positions past the real keys hold kNoLen,
+// kNoEdge), by the bitonic network of sort_edges in registers: partners in the
+// same wavefront exchange values across lanes, the others meet in LDS (buf:
+// 2 * kThreads entries, the two halves taken in turn so that each such step
+// needs one barrier).  Every thread of the workgroup calls it.
+template <int kThreads>
+__device__ void sort_keys_in_registers(unsigned long long& d, uint32_t& t, int P, uint4* buf) {
+  const int x = threadIdx.x;
+  int half = 0;
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int m = j == (k >> 1) ? k - 1 : j;  // partner x ^ m
+      const bool lower = (x & j) == 0;
+      switch (m) {
+        case 1: cx_lanes<1>(d, t, lower); break;
+        case 2: cx_lanes<2>(d, t, lower); break;
+        case 3: cx_lanes<3>(d, t, lower); break;
+        case 4: cx_lanes<4>(d, t, lower); break;
+        case 7: cx_lanes<7>(d, t, lower); break;
+        case 8: cx_lanes<8>(d, t, lower); break;
+        case 15: cx_lanes<15>(d, t, lower); break;
+        case 16: cx_lanes<16>(d, t, lower); break;
+        case 31: cx_lanes<31>(d, t, lower); break;
+        case 32: cx_lanes<32>(d, t, lower); break;
+        case 63: cx_lanes<63>(d, t, lower); break;
+        default: {
+          uint4* b = buf + half * kThreads;
+          b[x] = make_uint4((uint32_t)d, (uint32_t)(d >> 32), t, 0u);
+          __syncthreads();
+          const uint4 o = b[x ^ m];  // x ^ m < kThreads: both are below a power of two >= P
+          cx_take(d, t, ((unsigned long long)o.y << 32) | o.x, o.z, lower);
+          half ^= 1;
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ workgroup helpers
 
 // Exclusive prefix sum of a[0, n) in LDS, in place; returns the total.  Every
@@ -335,38 +414,58 @@ __device__ void emit_rows_per_row(int nb, int sink, int local_radius, int topk, 
   }
 }
 
-// Top-k selection and CSR emission from the per-block salience (LDS).
-//   Blocks are ranked by (-salience, index); the first min(topk, nb) form the
-//   global top-k set.  Row i lists, ascending: sink blocks [0, min(sink, i+1)),
-//   top-k blocks in [sink, i - r - 1], local blocks [max(sink, i - r), i].
-// Scratch (LDS): brank[nb], top[nb + 1], topidx[nb], cnt[nb + 1], tmp.
+// Rank of every block under (salience descending, index ascending), for the
+// large path.  sd: MST edge lengths, ascending; dead[v]: rank of the edge that
+// absorbs block v, or -1 for a root (which has salience 0); absorbed[r]: the
+// block absorbed at edge r.  Equal saliences are runs of equal lengths in sd,
+// so the rank of v is the number of blocks absorbed by longer edges, plus the
+// blocks of its own run with a lower index, plus the roots below v when its
+// salience is 0.  One root when the tree spans all nb blocks (root_blk).
 template <int kThreads>
-__device__ void select_and_emit(const double* sal, int nb, int sink, int local_radius, int topk,
-                                bool per_row, int* brank, int* top, int* topidx, int* cnt,
-                                int* tmp, int32_t* __restrict__ row_ptr,
+__device__ void rank_blocks(const double* sd, int ne, int nb, const int* dead, const int* absorbed,
+                            int root_blk, int* brank) {
+  for (int v = threadIdx.x; v < nb; v += kThreads) {
+    const int r = dead[v];
+    const double len = r >= 0 ? sd[r] : 0.0;
+    int lo = 0, hi = 0;
+    if (r >= 0) {
+      lo = r;
+      while (lo > 0 && sd[lo - 1] == len) --lo;
+      hi = r + 1;
+    }
+    while (hi < ne && sd[hi] == len) ++hi;
+    int rank = ne - hi;
+    for (int q = lo; q < hi; ++q) rank += absorbed[q] < v ? 1 : 0;
+    if (len == 0.0) {
+      if (ne == nb - 1) {
+        rank += root_blk < v ? 1 : 0;
+      } else {
+        for (int u = 0; u < v; ++u) rank += dead[u] < 0 ? 1 : 0;
+      }
+    }
+    brank[v] = rank;
+  }
+}
+
+// Top-k selection and CSR emission from the block ranks (brank, valid when
+// 0 < topk < nb) for the large path.  The first min(topk, nb) blocks form the
+// global top-k set.  Row i lists, ascending: sink blocks [0, min(sink, i+1)),
+// top-k blocks in [sink, i - r - 1], local blocks [max(sink, i - r), i].
+// Scratch (LDS): top[nb + 1], topidx[nb], cnt[nb + 1], tmp.  salience (if
+// given) gets the per-block saliences.
+template <int kThreads>
+__device__ void select_and_emit(const double* sd, const int* dead, int nb, int sink,
+                                int local_radius, int topk, bool per_row, int* brank, int* top,
+                                int* topidx, int* cnt, int* tmp, int32_t* __restrict__ row_ptr,
                                 int32_t* __restrict__ col_idx, int64_t col_capacity,
                                 double* __restrict__ salience) {
   const int tid = threadIdx.x;
   const int kk = topk < nb ? topk : nb;
-  if (kk > 0 && kk < nb) {
-    // Rank under (-salience, index): sort the pairs (the regions of cnt and topidx
-    // are free until the ranks exist), then each position names its block.
-    double* skey = reinterpret_cast<double*>(cnt);
-    uint32_t* sidx = reinterpret_cast<uint32_t*>(topidx);
-    for (int v = tid; v < nb; v += kThreads) {
-      skey[v] = -sal[v];
-      sidx[v] = (uint32_t)v;
-    }
-    __syncthreads();
-    sort_edges<kThreads>(skey, sidx, nb);
-    __syncthreads();
-    for (int p = tid; p < nb; p += kThreads) brank[sidx[p]] = p;
-  } else {
+  if (!(kk > 0 && kk < nb))
     for (int v = tid; v < nb; v += kThreads) brank[v] = 0;  // all blocks or none pass rank < kk
-  }
   __syncthreads();
   if (salience != nullptr)
-    for (int v = tid; v < nb; v += kThreads) salience[v] = sal[v];
+    for (int v = tid; v < nb; v += kThreads) salience[v] = dead[v] >= 0 ? sd[dead[v]] : 0.0;
   if (per_row) {
     emit_rows_per_row<kThreads>(nb, sink, local_radius, topk, brank, top, cnt, tmp, row_ptr,
                                 col_idx, col_capacity);
@@ -561,41 +660,68 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 }
 
 
-// The elder rule of elder_ranks for the large path (nb <= 64 * SLOTS <= 512):
-// keys (size << 12) | (4095 - root), one vector register per lane holding its
-// SLOTS blocks' keys (a lookup then indexes it with the uniform slot).  Lane k
-// of each group of 64 edges records the block absorbed at edge base + k, and
-// the group's saliences (edge lengths) are stored to LDS after the group, so the
-// loop over edges waits for no memory access.  sal must hold zeros on entry
-// (the surviving root keeps its 0).  st / sd: tags and lengths, ascending.
-template <int SLOTS>
-__device__ __forceinline__ void elder_salience(const uint32_t* st, const double* sd, int ne,
-                                               double* sal) {
-  typedef uint32_t keys_t __attribute__((ext_vector_type(SLOTS)));
-  constexpr int kRootBits = 12;
-  constexpr uint32_t kRootMask = (1u << kRootBits) - 1u;
+// The elder rule of elder_ranks for the large path (any nb up to 4096), by one
+// wavefront over the MST edges in ascending order (tags st[0, ne)), 32 edges
+// at a time.  Between chunks the components are a union-find over the blocks:
+// parent[] leads every block to its component's surviving root, and csize[]
+// holds the size at each root.  The edges of one chunk touch at most 64
+// components.  Each of those gets a local id (the lane of one of its
+// occurrences, agreed through lid[]) and, in that lane, the key
+// (size << 12) | (4095 - root), and the chunk's edges are applied to the keys
+// in order as in elder_ranks.  Outputs: dead[v] = rank of the edge at which
+// root v is absorbed (dead[] must hold -1 on entry), absorbed[r] = the root
+// absorbed at edge r.
+__device__ void elder_chunked(const uint32_t* st, int ne, int* parent, int* csize, int* lid,
+                              int* dead, int* absorbed) {
   const int lane = threadIdx.x & 63;
-  keys_t ckey;
-#pragma unroll
-  for (int s = 0; s < SLOTS; ++s) ckey[s] = (1u << kRootBits) | (kRootMask - (uint32_t)(lane + 64 * s));
-  for (int base = 0; base < ne; base += 64) {
-    const int r = base + lane;
-    const uint32_t tw = r < ne ? st[r] : 0u;
-    const double len = r < ne ? sd[r] : 0.0;
-    const int aw = (int)(tw >> 16), bw = (int)(tw & 0xffffu);
-    const int n = __builtin_amdgcn_readfirstlane(ne - base < 64 ? ne - base : 64);
-    int absorbed_at = -1;  // lane k: the block absorbed at edge base + k
-    for (int k = 0; k < n; ++k) {
-      const int a = read_lane(aw, k), b = read_lane(bw, k);
-      const uint32_t ka = (uint32_t)read_lane((int)ckey[a >> 6], a & 63);
-      const uint32_t kb = (uint32_t)read_lane((int)ckey[b >> 6], b & 63);
-      const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
-      const uint32_t grown = hi + (lo & ~kRootMask);
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s) ckey[s] = (ckey[s] == ka || ckey[s] == kb) ? grown : ckey[s];
-      absorbed_at = lane == k ? (int)(kRootMask - (lo & kRootMask)) : absorbed_at;
+  const int k = lane >> 1;  // the chunk edge of this lane; lane & 1 picks its endpoint
+  for (int c0 = 0; c0 < ne; c0 += 32) {
+    const int m = ne - c0 < 32 ? ne - c0 : 32;
+    int root = 0;
+    if (k < m) {
+      const uint32_t tw = st[c0 + k];
+      int x = (lane & 1) ? (int)(tw & 0xffffu) : (int)(tw >> 16);
+      // Root of x, halving the path on the way (every write points a block at
+      // one of its ancestors, so lanes that walk the same path concurrently
+      // still end at the root).
+      for (;;) {
+        const int px = parent[x];
+        if (px == x) break;
+        const int gx = parent[px];
+        parent[x] = gx;
+        x = gx;
+      }
+      root = x;
+      lid[root] = lane;  // among the lanes of one root, one write stays
     }
-    if (absorbed_at >= 0) sal[absorbed_at] = len;
+    wave_lds_sync();
+    int id = 0, key = 0;
+    if (k < m) {
+      id = lid[root];
+      if (id == lane) key = (csize[root] << 12) | (4095 - root);
+    }
+    int lost = -1;  // lane e: the root absorbed at edge c0 + e
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      if (e < m) {
+        const int ia = read_lane(id, 2 * e), ib = read_lane(id, 2 * e + 1);
+        const uint32_t ka = (uint32_t)read_lane(key, ia), kb = (uint32_t)read_lane(key, ib);
+        const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
+        const int grown = (int)(hi + (lo & ~4095u));
+        key = ((uint32_t)key == ka || (uint32_t)key == kb) ? grown : key;
+        lost = lane == e ? 4095 - (int)(lo & 4095u) : lost;
+      }
+    }
+    if (lane < m) {
+      dead[lost] = c0 + lane;
+      absorbed[c0 + lane] = lost;
+    }
+    if (k < m && id == lane) {
+      const int survivor = 4095 - (key & 4095);
+      parent[root] = survivor;
+      csize[survivor] = key >> 12;  // every local id merged into it writes the same size
+    }
+    wave_lds_sync();
   }
 }
 
@@ -1351,93 +1477,83 @@ __global__ __launch_bounds__(kLargeThreads) void boruvka_merge(int nb, int* __re
 }
 
 // Edge sort, elder rule, top-k and CSR emission for nb > kLdsDistBlocks.
-// Dynamic LDS regions (reused across phases):
-//   R0 double[nb]  salience
-//   R1 int[nb+1]   union-find parent -> top prefix
-//   R2 double[nb]  edge lengths, sorted in place -> row sizes / starts (int[nb+1])
-//   R3 int[nb]     edge tags, sorted with them   -> top-k list
-//   R4 int[nb+1]   component sizes -> block ranks
+// Dynamic LDS (finish_lds_bytes): sd double[nb], the MST edge lengths in
+// ascending order; then int regions of n1 = nb + 1 rounded up to even: st
+// (their tags), dead (per block, the rank of the edge that absorbs it, or -1),
+// absorbed (per edge, the block it absorbs), W0, W1, W2 (the elder rule's
+// parent, size and local ids; then ranks, top-k prefix and top-k list); then,
+// when the edges fit one per thread, the sort's exchange buffer.
+__host__ __device__ constexpr size_t finish_lds_base(int nb) {
+  return ((size_t)nb * sizeof(double) + 6 * (size_t)((nb + 2) & ~1) * sizeof(int) + 15) & ~(size_t)15;
+}
+__host__ __device__ constexpr size_t finish_lds_bytes(int nb) {
+  return finish_lds_base(nb) + (nb - 1 <= kLargeThreads ? 2 * kLargeThreads * 16 : 0);
+}
+
 __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
     int nb, const int* __restrict__ state, const double* __restrict__ edge_d_g,
     const uint32_t* __restrict__ edge_t_g, int sink, int local_radius, int topk, int per_row,
     int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_capacity,
     double* __restrict__ salience) {
   extern __shared__ __attribute__((aligned(16))) double lds_f64[];
-  const int n1 = (nb + 2) & ~1;  // nb + 1 rounded up to even (keeps doubles aligned)
-  double* R0 = lds_f64;
-  double* R2 = R0 + nb;
-  int* R1 = (int*)(R2 + nb);
-  int* R3 = R1 + n1;
-  int* R4 = R3 + n1;
+  const int n1 = (nb + 2) & ~1;
+  double* sd = lds_f64;
+  uint32_t* st = reinterpret_cast<uint32_t*>(sd + nb);
+  int* dead = reinterpret_cast<int*>(st + n1);
+  int* absorbed = dead + n1;
+  int* W0 = absorbed + n1;
+  int* W1 = W0 + n1;
+  int* W2 = W1 + n1;
   __shared__ int tmp[kLargeThreads / 64];
+  __shared__ int root_blk;
   const int tid = threadIdx.x;
   const int ne = state[0] < nb - 1 ? state[0] : nb - 1;
 
-  double* sd = R2;
-  uint32_t* st = (uint32_t*)R3;
-  for (int e = tid; e < ne; e += kLargeThreads) {
-    sd[e] = edge_d_g[e];
-    st[e] = edge_t_g[e];
-  }
-  __syncthreads();
-  sort_edges<kLargeThreads>(sd, st, ne);  // the next phase reads sd, st after its own barrier
-
-  // Elder rule.  Up to 512 blocks: component keys in registers of one wavefront
-  // (elder_salience).  Beyond: union-find in LDS, union by size with the elder
-  // tie rule; lanes 0 and 1 follow the parent chains of the two endpoints.
-  double* sal = R0;
-  int* parent = R1;
-  int* csize = R4;
-  for (int v = tid; v < nb; v += kLargeThreads) {
-    sal[v] = 0.0;
-    parent[v] = v;
-    csize[v] = 1;
-  }
-  __syncthreads();
-  if (nb <= 256) {
-    if (tid < 64) elder_salience<4>(st, sd, ne, sal);
-  } else if (nb <= 512) {
-    if (tid < 64) elder_salience<8>(st, sd, ne, sal);
-  } else if (tid < 64) {
-    const int lane = tid;
-    for (int base = 0; base < ne; base += 64) {
-      const int r = base + lane;
-      const int tw = r < ne ? (int)st[r] : 0;
-      const double dw = r < ne ? sd[r] : 0.0;
-      const int n = ne - base < 64 ? ne - base : 64;
-      for (int k = 0; k < n; ++k) {
-        const int t = read_lane(tw, k);
-        const int a = (int)((uint32_t)t >> 16), b = t & 0xffff;
-        int x = lane == 0 ? a : b;
-        if (lane < 2) {
-          // parents only ever point at a root of the moment, so chains are
-          // acyclic and at most log2(nb) long
-          for (int h = 0; h < nb; ++h) {
-            const int p = parent[x];
-            if (p == x) break;
-            x = p;
-          }
-        }
-        const int ra = read_lane(x, 0), rb = read_lane(x, 1);
-        const int sa = csize[ra], sb = csize[rb];
-        const bool a_survives = sa > sb || (sa == sb && ra < rb);
-        const int surv = a_survives ? ra : rb, absorbed = a_survives ? rb : ra;
-        const double w = read_lane(dw, k);
-        if (lane == 0) {
-          parent[absorbed] = surv;
-          parent[a] = surv;
-          parent[b] = surv;
-          csize[surv] = sa + sb;
-          sal[absorbed] = w;
-        }
-      }
+  // ---- MST edges in ascending (length, tag) order.
+  if (ne <= kLargeThreads) {
+    uint4* sbuf = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_f64) + finish_lds_base(nb));
+    int P = 1;
+    while (P < ne) P <<= 1;
+    unsigned long long d = kNoLen;
+    uint32_t t = kNoEdge;
+    if (tid < ne) {
+      d = len_bits(edge_d_g[tid]);
+      t = edge_t_g[tid];
     }
+    sort_keys_in_registers<kLargeThreads>(d, t, P, sbuf);
+    if (tid < ne) {
+      sd[tid] = bits_len(d);
+      st[tid] = t;
+    }
+  } else {
+    for (int e = tid; e < ne; e += kLargeThreads) {
+      sd[e] = edge_d_g[e];
+      st[e] = edge_t_g[e];
+    }
+    __syncthreads();
+    sort_edges<kLargeThreads>(sd, st, ne);
+  }
+  for (int v = tid; v < nb; v += kLargeThreads) {
+    W0[v] = v;  // union-find parent
+    W1[v] = 1;  // component size, at roots
+    dead[v] = -1;
   }
   __syncthreads();
 
-  select_and_emit<kLargeThreads>(sal, nb, sink, local_radius, topk, per_row != 0, R4, R1, R3,
-                                 (int*)R2, tmp,
-                                 row_ptr, col_idx, col_capacity, salience);
+  // ---- Elder rule (one wavefront).
+  if (tid < 64) elder_chunked(st, ne, W0, W1, W2, dead, absorbed);
+  __syncthreads();
+
+  // ---- Block ranks, top-k and CSR rows.
+  const int kk = topk < nb ? topk : nb;
+  if (kk > 0 && kk < nb) {
+    for (int v = tid; v < nb; v += kLargeThreads)
+      if (dead[v] < 0) root_blk = v;  // one root when ne == nb - 1
+    __syncthreads();
+    rank_blocks<kLargeThreads>(sd, ne, nb, dead, absorbed, root_blk, W0);
+  }
+  select_and_emit<kLargeThreads>(sd, dead, nb, sink, local_radius, topk, per_row != 0, W0, W1, W2,
+                                 absorbed, tmp, row_ptr, col_idx, col_capacity, salience);
 }
 
 __global__ void dense_schedule_kernel(int64_t nb, int32_t* __restrict__ row_ptr,
@@ -1614,8 +1730,7 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
                        state, best_d, best_t, edge_d, edge_t);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  const size_t n1 = (size_t)((nb + 2) & ~1);
-  const size_t finish_lds = 2 * (size_t)nb * sizeof(double) + 3 * n1 * sizeof(int);
+  const size_t finish_lds = finish_lds_bytes(nb);
   if ((err = allow_lds(finish_kernel, finish_lds)) != hipSuccess) return err;
   hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kLargeThreads), finish_lds, stream, nb, state,
                      edge_d, edge_t, sink, local_radius, topk, (int)per_row, row_ptr, col_idx,
