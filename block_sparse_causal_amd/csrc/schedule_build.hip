@@ -26,13 +26,16 @@
 //                       d * nbe + j, nbe = nb rounded up to even);
 //     distance_kernel   the nb x nb distance matrix, one entry per thread over
 //                       many CUs;
-//     boruvka_nearest   per block, the least edge to another component;
-//     boruvka_merge     one workgroup: per-component least edge, hooking,
-//                       pointer jumping, new labels, the new MST edges;
-//                       (the pair is launched ceil(log2 nb) times: every round
-//                       at least halves the number of components, and rounds
-//                       after the last merge return at once)
-//     finish_kernel     edge sort, elder rule (union-find in LDS), top-k, CSR.
+//     boruvka_round     ceil(log2 nb) launches (every round at least halves
+//                       the number of components): per block, the least edge
+//                       to another component, one wavefront each; then the
+//                       workgroups elect one (as above) that merges the
+//                       components (hooking, pointer jumping, new labels, the
+//                       new MST edges).  In the last launch the elected
+//                       workgroup goes on: MST edges sorted (bitonic network
+//                       in registers), elder rule 32 edges at a time (one
+//                       wavefront), blocks ranked from runs of equal edge
+//                       lengths, top-k, CSR rows emitted.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <unistd.h>
@@ -53,8 +56,8 @@ constexpr unsigned long long kNoLen = ~0ull;       // above the bits of +inf
 constexpr int kStageBytes = 16384;                 // least LDS staging of centroid dims
 constexpr int kSmallThreads = 512;
 constexpr int kLargeThreads = 1024;
-constexpr int kLargePerThread = 4;                 // blocks per thread in boruvka_merge
-static_assert(kLargeThreads * kLargePerThread >= 4096, "boruvka_merge covers 4096 blocks");
+constexpr int kLargePerThread = 4;                 // blocks per thread in merge_components
+static_assert(kLargeThreads * kLargePerThread >= 4096, "merge_components covers 4096 blocks");
 
 __device__ __forceinline__ double key_to_double(uint16_t bits, bool bf16) {
   if (bf16) return (double)__uint_as_float((uint32_t)bits << 16);
@@ -183,15 +186,13 @@ __device__ __forceinline__ int lane_xor(int v) {
 }
 
 // Compare-exchange of one bitonic step: the lower position of the pair keeps
-// the smaller of (d, t) and (od, ot), the upper one the larger.
+// the smaller of (d, t) and (od, ot), the upper one the larger (keys are
+// distinct but for the padding, whose copies are equal).
 __device__ __forceinline__ void cx_take(unsigned long long& d, uint32_t& t, unsigned long long od,
                                         uint32_t ot, bool lower) {
-  const bool other_less = od < d || (od == d && ot < t);
-  const bool other_more = d < od || (d == od && t < ot);
-  if (lower ? other_less : other_more) {
-    d = od;
-    t = ot;
-  }
+  const bool take = (od < d || (od == d && ot < t)) == lower;
+  d = take ? od : d;
+  t = take ? ot : t;
 }
 template <int M>
 __device__ __forceinline__ void cx_lanes(unsigned long long& d, uint32_t& t, bool lower) {
@@ -201,42 +202,64 @@ __device__ __forceinline__ void cx_lanes(unsigned long long& d, uint32_t& t, boo
   cx_take(d, t, ((unsigned long long)hi << 32) | lo, ot, lower);
 }
 
-// Ascending sort of P <= kThreads keys (length bits, tag), one per thread in
-// position order (P a power of two; positions past the real keys hold kNoLen,
-// kNoEdge), by the bitonic network of sort_edges in registers: partners in the
-// same wavefront exchange values across lanes, the others meet in LDS (buf:
-// 2 * kThreads entries, the two halves taken in turn so that each such step
-// needs one barrier).  Every thread of the workgroup calls it.
-template <int kThreads>
-__device__ void sort_keys_in_registers(unsigned long long& d, uint32_t& t, int P, uint4* buf) {
-  const int x = threadIdx.x;
-  int half = 0;
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int m = j == (k >> 1) ? k - 1 : j;  // partner x ^ m
-      const bool lower = (x & j) == 0;
-      switch (m) {
-        case 1: cx_lanes<1>(d, t, lower); break;
-        case 2: cx_lanes<2>(d, t, lower); break;
-        case 3: cx_lanes<3>(d, t, lower); break;
-        case 4: cx_lanes<4>(d, t, lower); break;
-        case 7: cx_lanes<7>(d, t, lower); break;
-        case 8: cx_lanes<8>(d, t, lower); break;
-        case 15: cx_lanes<15>(d, t, lower); break;
-        case 16: cx_lanes<16>(d, t, lower); break;
-        case 31: cx_lanes<31>(d, t, lower); break;
-        case 32: cx_lanes<32>(d, t, lower); break;
-        case 63: cx_lanes<63>(d, t, lower); break;
-        default: {
-          uint4* b = buf + half * kThreads;
-          b[x] = make_uint4((uint32_t)d, (uint32_t)(d >> 32), t, 0u);
-          __syncthreads();
-          const uint4 o = b[x ^ m];  // x ^ m < kThreads: both are below a power of two >= P
-          cx_take(d, t, ((unsigned long long)o.y << 32) | o.x, o.z, lower);
-          half ^= 1;
-        }
+// The steps of the bitonic network of sort_edges for P keys, from merge width
+// K and step J on, unrolled: the first step of a merge pairs position x with
+// x ^ (K - 1), the later ones with x ^ J.  Partners in the same wavefront
+// exchange values across lanes; the others meet in LDS (buf: 2 * kThreads
+// entries, the halves taken in turn so that each such step needs one barrier).
+// Wavefronts past the P keys only join the barriers.
+template <int kThreads, int P, int K, int J, int HALF>
+__device__ __forceinline__ void bitonic_steps(unsigned long long& d, uint32_t& t, uint4* buf) {
+  if constexpr (K <= P) {
+    constexpr int M = J == K / 2 ? K - 1 : J;
+    const int x = threadIdx.x;
+    const bool lower = (x & J) == 0;
+    constexpr int kNextHalf = M < 64 ? HALF : HALF ^ 1;
+    if constexpr (M < 64) {
+      if ((x & ~63) < P) cx_lanes<M>(d, t, lower);
+    } else {
+      uint4* b = buf + HALF * kThreads;
+      if (x < P) b[x] = make_uint4((uint32_t)d, (uint32_t)(d >> 32), t, 0u);
+      __syncthreads();
+      if (x < P) {
+        const uint4 o = b[x ^ M];
+        cx_take(d, t, ((unsigned long long)o.y << 32) | o.x, o.z, lower);
       }
     }
+    if constexpr (J > 1)
+      bitonic_steps<kThreads, P, K, J / 2, kNextHalf>(d, t, buf);
+    else
+      bitonic_steps<kThreads, P, K * 2, K, kNextHalf>(d, t, buf);
+  }
+}
+
+// Ascending sort of n <= kThreads keys (length bits, tag), one per thread in
+// position order (threads at and past n hold kNoLen, kNoEdge, which sort last),
+// by the bitonic network of sort_edges in registers.  Every thread of the
+// workgroup calls it.
+template <int kThreads>
+__device__ void sort_keys_in_registers(unsigned long long& d, uint32_t& t, int n, uint4* buf) {
+  static_assert(kThreads <= 1024, "unrolled networks up to 1024 keys");
+  if (n <= 2) {
+    bitonic_steps<kThreads, 2, 2, 1, 0>(d, t, buf);
+  } else if (n <= 4) {
+    bitonic_steps<kThreads, 4, 2, 1, 0>(d, t, buf);
+  } else if (n <= 8) {
+    bitonic_steps<kThreads, 8, 2, 1, 0>(d, t, buf);
+  } else if (n <= 16) {
+    bitonic_steps<kThreads, 16, 2, 1, 0>(d, t, buf);
+  } else if (n <= 32) {
+    bitonic_steps<kThreads, 32, 2, 1, 0>(d, t, buf);
+  } else if (n <= 64) {
+    bitonic_steps<kThreads, 64, 2, 1, 0>(d, t, buf);
+  } else if (n <= 128) {
+    bitonic_steps<kThreads, 128, 2, 1, 0>(d, t, buf);
+  } else if (n <= 256) {
+    bitonic_steps<kThreads, 256, 2, 1, 0>(d, t, buf);
+  } else if (n <= 512) {
+    bitonic_steps<kThreads, 512, 2, 1, 0>(d, t, buf);
+  } else {
+    bitonic_steps<kThreads, 1024, 2, 1, 0>(d, t, buf);
   }
 }
 
@@ -494,27 +517,20 @@ __device__ void select_and_emit(const double* sd, const int* dead, int nb, int s
   block_exclusive_scan<kThreads>(cnt, nb + 1, tmp);  // also leaves cnt[nb] = nnz
   for (int i = tid; i <= nb; i += kThreads) row_ptr[i] = cnt[i];
 
-  // Entries: one wavefront per row, one entry per lane.
-  const int lane = tid & 63;
-  for (int i = tid >> 6; i < nb; i += kThreads / 64) {
+  // Entries: one thread per row.
+  for (int i = tid; i < nb; i += kThreads) {
     const int a_n = sink < i + 1 ? sink : i + 1;
     const int loc_lo = (i - local_radius > sink) ? i - local_radius : sink;
-    const int b_n = loc_lo <= i ? i - loc_lo + 1 : 0;
     const int t_hi = i - local_radius - 1;
     const int c_n = t_hi >= sink ? top[t_hi + 1] - top[sink] : 0;
     const int c0 = t_hi >= sink ? top[sink] : 0;
-    const int n = a_n + c_n + b_n;
-    const int64_t start = cnt[i];
-    for (int k = lane; k < n; k += 64) {
-      int j;
-      if (k < a_n)
-        j = k;
-      else if (k < a_n + c_n)
-        j = topidx[c0 + k - a_n];
-      else
-        j = loc_lo + (k - a_n - c_n);
-      if (start + k < col_capacity) col_idx[start + k] = j;
-    }
+    int64_t at = cnt[i];
+    for (int j = 0; j < a_n; ++j, ++at)
+      if (at < col_capacity) col_idx[at] = j;
+    for (int q = 0; q < c_n; ++q, ++at)
+      if (at < col_capacity) col_idx[at] = topidx[c0 + q];
+    for (int j = loc_lo; j <= i; ++j, ++at)
+      if (at < col_capacity) col_idx[at] = j;
   }
 }
 
@@ -1125,12 +1141,57 @@ __device__ __forceinline__ void small_topology(
                               col_idx, col_capacity, salience);
 }
 
+// Election of the one workgroup of a launch of nwg workgroups that goes on
+// alone (the scheme is described at schedule_small).  Every value that
+// crosses workgroups (results, flags, the claim) moves by device-coherent
+// accesses that bypass the non-coherent caches, so ordering needs only waits
+// for completion, not cache write-back or invalidation.  Every thread calls it
+// once its cross-workgroup stores are issued; epoch is flags[nwg + 1] as
+// loaded by threads 0..63 at the start of the launch.  The answer is the same
+// in every thread of a workgroup.  flags: nwg + 2 words (flags, claim, epoch),
+// nwg <= kMaxElectFlags.
+constexpr int kMaxElectFlags = 256;
+__device__ bool elect_last_workgroup(unsigned long long* flags, int nwg,
+                                     unsigned long long host_token, unsigned long long epoch) {
+  __shared__ int elected;
+  const int tid = threadIdx.x;
+  wait_vmem();  // this thread's cross-workgroup stores have completed
+  __syncthreads();
+  if (tid < 64) {
+    const unsigned long long token = host_token + epoch * 0x9E3779B97F4A7C15ull;
+    if (tid == 0) store_coherent(&flags[blockIdx.x], token);
+    wait_vmem();  // the flag store completes before any flag is read
+    unsigned long long f[kMaxElectFlags / 64];  // all loads in flight before any is compared
+#pragma unroll
+    for (int u = 0; u < kMaxElectFlags / 64; ++u) {
+      const int t = tid + 64 * u;
+      f[u] = (t < nwg && t != (int)blockIdx.x) ? load_coherent(&flags[t]) : token;
+    }
+    bool mine = true;
+#pragma unroll
+    for (int u = 0; u < kMaxElectFlags / 64; ++u) mine &= f[u] == token;
+    const bool all = __ballot(!mine) == 0ull;
+    if (tid == 0) {
+      elected = all && __hip_atomic_exchange(&flags[nwg], token, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) != token;
+      // every workgroup has read epoch: its flag, derived from it, is stored.
+      // Nothing in this launch reads epoch again, so the store is not waited
+      // for (the next launch sees it).
+      if (elected) store_coherent(&flags[nwg + 1], epoch + 1ull);
+    }
+  }
+  __syncthreads();
+  return elected != 0;
+}
+
 // schedule_small splits the upper triangle of the distance matrix into tiles
 // of TILE x TILE blocks, one per workgroup; TILE is the smallest of 2, 4, 8
 // that keeps the tile count within one workgroup per CU, since a smaller tile
 // means fewer centroids formed per workgroup.
 constexpr int kTileDims = 64;  // centroid dims per pass
 constexpr int kMaxTiles = 256;
+static_assert(kMaxTiles <= kMaxElectFlags, "one election flag per tile");
+static_assert(4096 / (kLargeThreads / 64) <= kMaxElectFlags, "one election flag per round workgroup");
 __host__ __device__ constexpr int small_tile_count(int nb, int tile) {
   return ((nb + tile - 1) / tile) * ((nb + tile - 1) / tile + 1) / 2;
 }
@@ -1178,7 +1239,6 @@ __global__ __launch_bounds__(kSmallThreads) void schedule_small(
   constexpr int kGroups = kSmallThreads / (8 * kSlots);      // row groups per block
   constexpr int kRowsPer = kBlock / kGroups;                 // rows per group (= 2 * TILE)
   extern __shared__ __attribute__((aligned(16))) double smem[];
-  __shared__ int elected;
   const int tid = threadIdx.x;
   const int T = (nb + TILE - 1) / TILE;
   const int ntiles = T * (T + 1) / 2;
@@ -1287,31 +1347,7 @@ __global__ __launch_bounds__(kSmallThreads) void schedule_small(
       }
     }
   }
-  // ---- Election of the workgroup that builds the schedule.  Every value
-  // that crosses workgroups (distances, flags, the claim) moves by a device-
-  // coherent access that bypasses the non-coherent caches, so ordering needs
-  // only waits for completion, not cache write-back or invalidation.
-  wait_vmem();  // this thread's distance stores have completed
-  __syncthreads();
-  if (tid < 64) {
-    const unsigned long long token = host_token + epoch * 0x9E3779B97F4A7C15ull;
-    if (tid == 0) store_coherent(&flags[blockIdx.x], token);
-    wait_vmem();  // the flag store completes before any flag is read
-    bool mine = true;
-    for (int t = tid; t < ntiles; t += 64)
-      if (t != (int)blockIdx.x) mine = mine && load_coherent(&flags[t]) == token;
-    const bool all = __ballot(!mine) == 0ull;
-    if (tid == 0) {
-      elected = all && __hip_atomic_exchange(&flags[ntiles], token, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) != token;
-      // every workgroup has read epoch: its flag, derived from it, is stored.
-      // Nothing in this launch reads epoch again, so the store is not waited
-      // for (the next launch sees it).
-      if (elected) store_coherent(&flags[ntiles + 1], epoch + 1ull);
-    }
-  }
-  __syncthreads();
-  if (!elected) return;
+  if (!elect_last_workgroup(flags, ntiles, host_token, epoch)) return;
   small_topology<SLOTS>(smem, dist_g, nb, sink, local_radius, topk, per_row != 0, row_ptr, col_idx,
                         col_capacity, salience);
 }
@@ -1363,17 +1399,12 @@ __global__ __launch_bounds__(256) void distance_kernel(const double* __restrict_
   if (i < nb && j < nb) dist[(int64_t)i * nb + j] = finite_or_inf(__builtin_sqrt(acc));
 }
 
-// One wavefront per block v: the least edge from v to a block of another
-// component.  state = {MST edges so far, done}.
-__global__ __launch_bounds__(256) void boruvka_nearest(const double* __restrict__ dist, int nb,
-                                                       const int* __restrict__ comp,
-                                                       const int* __restrict__ state,
-                                                       double* __restrict__ best_d,
-                                                       uint32_t* __restrict__ best_t) {
-  if (state[1]) return;
-  const int v = blockIdx.x * 4 + (threadIdx.x >> 6);
+// Per block v (one wavefront each): the least edge from v to a block of
+// another component, stored by device-coherent stores for the merge of the
+// same launch.
+__device__ void nearest_edge(const double* __restrict__ dist, int nb, const int* __restrict__ comp,
+                             int v, double* best_d, uint32_t* best_t) {
   const int lane = threadIdx.x & 63;
-  if (v >= nb) return;  // whole wavefront
   const int cv = comp[v];
   const double* row = dist + (int64_t)v * nb;
   double bd = __builtin_inf();
@@ -1389,42 +1420,54 @@ __global__ __launch_bounds__(256) void boruvka_nearest(const double* __restrict_
   }
   wave_edge_min(bd, bt);
   if (lane == 0) {
-    best_d[v] = bd;
-    best_t[v] = bt;
+    store_coherent(best_d + v, len_bits(bd));
+    __hip_atomic_store(best_t + v, bt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// One workgroup: per-component least edge, hooking, pointer jumping, new
-// labels; the round's MST edges are appended to edge_d / edge_t.
-// Dynamic LDS: comp, hook, par (int), cmin_t (u32), cmin_d (u64), nb each.
-__global__ __launch_bounds__(kLargeThreads) void boruvka_merge(int nb, int* __restrict__ comp,
-                                                               int* __restrict__ state,
-                                                               const double* __restrict__ best_d,
-                                                               const uint32_t* __restrict__ best_t,
-                                                               double* __restrict__ edge_d,
-                                                               uint32_t* __restrict__ edge_t) {
-  if (state[1]) return;
-  extern __shared__ __attribute__((aligned(16))) unsigned long long lds_u64[];
-  unsigned long long* cmin_d = lds_u64;
+// Per-component least edge, hooking, pointer jumping, new labels, by one
+// workgroup of kLargeThreads; the round's MST edges are appended to edge_d /
+// edge_t, and the new edge count is returned (in every thread).  best_d /
+// best_t come from the other workgroups of the launch (device-coherent loads).
+// LDS at lds: cmin_d (u64), cmin_t (u32), lcomp, hook, par (int), nb each.
+__device__ int merge_components(int nb, int* __restrict__ comp, int* __restrict__ state, int nedges0,
+                                const double* best_d, const uint32_t* best_t,
+                                double* __restrict__ edge_d, uint32_t* __restrict__ edge_t,
+                                unsigned long long* lds) {
+  unsigned long long* cmin_d = lds;
   uint32_t* cmin_t = (uint32_t*)(cmin_d + nb);
   int* lcomp = (int*)(cmin_t + nb);
   int* hook = lcomp + nb;
   int* par = hook + nb;
   __shared__ int nedges, changed;
   const int tid = threadIdx.x;
-  if (tid == 0) nedges = state[0];
-  for (int v = tid; v < nb; v += kLargeThreads) {
-    lcomp[v] = comp[v];
-    cmin_d[v] = kNoLen;
-    cmin_t[v] = kNoEdge;
+  if (tid == 0) nedges = nedges0;
+  unsigned long long bd[kLargePerThread];
+  uint32_t bt[kLargePerThread];
+#pragma unroll
+  for (int k = 0; k < kLargePerThread; ++k) {
+    const int v = tid + k * kLargeThreads;
+    bd[k] = kNoLen;
+    bt[k] = kNoEdge;
+    if (v < nb) {
+      bd[k] = load_coherent(reinterpret_cast<const unsigned long long*>(best_d) + v);
+      bt[k] = __hip_atomic_load(best_t + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lcomp[v] = comp[v];
+      cmin_d[v] = kNoLen;
+      cmin_t[v] = kNoEdge;
+    }
   }
   __syncthreads();
-  for (int v = tid; v < nb; v += kLargeThreads)
-    if (best_t[v] != kNoEdge) atomicMin(&cmin_d[lcomp[v]], len_bits(best_d[v]));
+#pragma unroll
+  for (int k = 0; k < kLargePerThread; ++k) {
+    const int v = tid + k * kLargeThreads;
+    if (v < nb && bt[k] != kNoEdge) atomicMin(&cmin_d[lcomp[v]], bd[k]);
+  }
   __syncthreads();
-  for (int v = tid; v < nb; v += kLargeThreads) {
-    const uint32_t t = best_t[v];
-    if (t != kNoEdge && len_bits(best_d[v]) == cmin_d[lcomp[v]]) atomicMin(&cmin_t[lcomp[v]], t);
+#pragma unroll
+  for (int k = 0; k < kLargePerThread; ++k) {
+    const int v = tid + k * kLargeThreads;
+    if (v < nb && bt[k] != kNoEdge && bd[k] == cmin_d[lcomp[v]]) atomicMin(&cmin_t[lcomp[v]], bt[k]);
   }
   __syncthreads();
   for (int c = tid; c < nb; c += kLargeThreads)
@@ -1440,9 +1483,9 @@ __global__ __launch_bounds__(kLargeThreads) void boruvka_merge(int nb, int* __re
       const bool mutual = hook[c2] == c;
       if (!mutual || c < c2) {
         const int pos = atomicAdd(&nedges, 1);  // < nb - 1: each edge joins two components
-        if (pos < nb) {
-          edge_d[pos] = bits_len(cmin_d[c]);
-          edge_t[pos] = cmin_t[c];
+        if (pos < nb) {  // device-coherent: the last round reads them back in this workgroup
+          store_coherent(edge_d + pos, cmin_d[c]);
+          __hip_atomic_store(edge_t + pos, cmin_t[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       par[c] = (mutual && c < c2) ? c : c2;
@@ -1470,10 +1513,12 @@ __global__ __launch_bounds__(kLargeThreads) void boruvka_merge(int nb, int* __re
   }
   for (int v = tid; v < nb; v += kLargeThreads) comp[v] = par[lcomp[v]];
   __syncthreads();
+  const int n = nedges;
   if (tid == 0) {
-    state[0] = nedges;
-    state[1] = nedges >= nb - 1 ? 1 : 0;
+    state[0] = n;
+    state[1] = n >= nb - 1 ? 1 : 0;
   }
+  return n;
 }
 
 // Edge sort, elder rule, top-k and CSR emission for nb > kLdsDistBlocks.
@@ -1490,12 +1535,11 @@ __host__ __device__ constexpr size_t finish_lds_bytes(int nb) {
   return finish_lds_base(nb) + (nb - 1 <= kLargeThreads ? 2 * kLargeThreads * 16 : 0);
 }
 
-__global__ __launch_bounds__(kLargeThreads) void finish_kernel(
-    int nb, const int* __restrict__ state, const double* __restrict__ edge_d_g,
-    const uint32_t* __restrict__ edge_t_g, int sink, int local_radius, int topk, int per_row,
-    int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int64_t col_capacity,
-    double* __restrict__ salience) {
-  extern __shared__ __attribute__((aligned(16))) double lds_f64[];
+__device__ void finish_schedule(int nb, int nedges, const double* edge_d_g, const uint32_t* edge_t_g,
+                                int sink, int local_radius, int topk, bool per_row,
+                                int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
+                                int64_t col_capacity, double* __restrict__ salience,
+                                double* lds_f64) {
   const int n1 = (nb + 2) & ~1;
   double* sd = lds_f64;
   uint32_t* st = reinterpret_cast<uint32_t*>(sd + nb);
@@ -1507,28 +1551,26 @@ __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
   __shared__ int tmp[kLargeThreads / 64];
   __shared__ int root_blk;
   const int tid = threadIdx.x;
-  const int ne = state[0] < nb - 1 ? state[0] : nb - 1;
+  const int ne = nedges < nb - 1 ? nedges : nb - 1;
 
   // ---- MST edges in ascending (length, tag) order.
   if (ne <= kLargeThreads) {
     uint4* sbuf = reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds_f64) + finish_lds_base(nb));
-    int P = 1;
-    while (P < ne) P <<= 1;
     unsigned long long d = kNoLen;
     uint32_t t = kNoEdge;
-    if (tid < ne) {
-      d = len_bits(edge_d_g[tid]);
-      t = edge_t_g[tid];
+    if (tid < ne) {  // stored by this workgroup: coherent loads skip stale cache lines
+      d = load_coherent(reinterpret_cast<const unsigned long long*>(edge_d_g) + tid);
+      t = __hip_atomic_load(edge_t_g + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    sort_keys_in_registers<kLargeThreads>(d, t, P, sbuf);
+    sort_keys_in_registers<kLargeThreads>(d, t, ne, sbuf);
     if (tid < ne) {
       sd[tid] = bits_len(d);
       st[tid] = t;
     }
   } else {
     for (int e = tid; e < ne; e += kLargeThreads) {
-      sd[e] = edge_d_g[e];
-      st[e] = edge_t_g[e];
+      sd[e] = bits_len(load_coherent(reinterpret_cast<const unsigned long long*>(edge_d_g) + e));
+      st[e] = __hip_atomic_load(edge_t_g + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     sort_edges<kLargeThreads>(sd, st, ne);
@@ -1552,8 +1594,41 @@ __global__ __launch_bounds__(kLargeThreads) void finish_kernel(
     __syncthreads();
     rank_blocks<kLargeThreads>(sd, ne, nb, dead, absorbed, root_blk, W0);
   }
-  select_and_emit<kLargeThreads>(sd, dead, nb, sink, local_radius, topk, per_row != 0, W0, W1, W2,
+  select_and_emit<kLargeThreads>(sd, dead, nb, sink, local_radius, topk, per_row, W0, W1, W2,
                                  absorbed, tmp, row_ptr, col_idx, col_capacity, salience);
+}
+
+// One Boruvka round of the schedule build for nb > kLdsDistBlocks, in one
+// launch of ceil(nb / 16) workgroups: every wavefront finds the least edge out
+// of one block's component (nearest_edge); the workgroups then elect the one
+// that ends last (elect_last_workgroup), which merges the components
+// (merge_components) and, in the build's last round (FINISH: by then one
+// component is left), sorts the MST edges, applies the elder rule and emits
+// the CSR rows (finish_schedule).  Rounds after the tree is complete skip the
+// search and the merge.  flags: ceil(nb / 16) + 2 words of workspace.
+template <bool FINISH>
+__global__ __launch_bounds__(kLargeThreads) void boruvka_round(
+    const double* __restrict__ dist, int nb, int* __restrict__ comp, int* __restrict__ state,
+    double* best_d, uint32_t* best_t, double* edge_d, uint32_t* edge_t,
+    unsigned long long* flags, unsigned long long host_token, int sink, int local_radius, int topk,
+    int per_row, int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
+    int64_t col_capacity, double* __restrict__ salience) {
+  extern __shared__ __attribute__((aligned(16))) unsigned long long lds_u64[];
+  const int tid = threadIdx.x;
+  const unsigned long long epoch = tid < 64 ? load_coherent(&flags[gridDim.x + 1]) : 0ull;
+  const int nedges0 = state[0];
+  const bool done = state[1] != 0;
+  const int v = (int)blockIdx.x * (kLargeThreads / 64) + (tid >> 6);
+  if (!done && v < nb) nearest_edge(dist, nb, comp, v, best_d, best_t);
+  if (!elect_last_workgroup(flags, (int)gridDim.x, host_token, epoch)) return;
+  const int nedges =
+      done ? nedges0 : merge_components(nb, comp, state, nedges0, best_d, best_t, edge_d, edge_t, lds_u64);
+  if (FINISH) {
+    wait_vmem();  // the merge's edge stores have completed before they are read back
+    __syncthreads();  // and its LDS is reused
+    finish_schedule(nb, nedges, edge_d, edge_t, sink, local_radius, topk, per_row != 0, row_ptr,
+                    col_idx, col_capacity, salience, reinterpret_cast<double*>(lds_u64));
+  }
 }
 
 __global__ void dense_schedule_kernel(int64_t nb, int32_t* __restrict__ row_ptr,
@@ -1604,9 +1679,10 @@ WorkspaceLayout workspace_layout(int64_t nb, int64_t D) {
   L.best_t = take(n * sizeof(uint32_t));
   L.edge_d = take(n * sizeof(double));
   L.edge_t = take(n * sizeof(uint32_t));
-  L.flags = take(nb <= kLdsDistBlocks
-                     ? (size_t)(small_tile_count((int)nb, small_tile_edge((int)nb)) + 2) * sizeof(unsigned long long)
-                     : 0);
+  L.flags = take((nb <= kLdsDistBlocks ? (size_t)small_tile_count((int)nb, small_tile_edge((int)nb))
+                                       : (size_t)((nb + kLargeThreads / 64 - 1) / (kLargeThreads / 64))) *
+                     sizeof(unsigned long long) +
+                 2 * sizeof(unsigned long long));
   L.total = off;
   return L;
 }
@@ -1719,23 +1795,27 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
   uint32_t* best_t = (uint32_t*)(ws + L.best_t);
   double* edge_d = (double*)(ws + L.edge_d);
   uint32_t* edge_t = (uint32_t*)(ws + L.edge_t);
+  unsigned long long* flags = (unsigned long long*)(ws + L.flags);
   const size_t merge_lds = (size_t)nb * (sizeof(unsigned long long) + sizeof(uint32_t) + 3 * sizeof(int));
-  if ((err = allow_lds(boruvka_merge, merge_lds)) != hipSuccess) return err;
+  const size_t last_lds = merge_lds > finish_lds_bytes(nb) ? merge_lds : finish_lds_bytes(nb);
+  if ((err = allow_lds(boruvka_round<false>, merge_lds)) != hipSuccess) return err;
+  if ((err = allow_lds(boruvka_round<true>, last_lds)) != hipSuccess) return err;
+  const dim3 grid((unsigned)((nb + kLargeThreads / 64 - 1) / (kLargeThreads / 64)));
   int rounds = 0;
   while ((1 << rounds) < nb) ++rounds;  // components at least halve per round
   for (int r = 0; r < rounds; ++r) {
-    hipLaunchKernelGGL(boruvka_nearest, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, stream, dist,
-                       nb, comp, state, best_d, best_t);
-    hipLaunchKernelGGL(boruvka_merge, dim3(1), dim3(kLargeThreads), merge_lds, stream, nb, comp,
-                       state, best_d, best_t, edge_d, edge_t);
+    const unsigned long long token = next_call_token();
+    if (r + 1 < rounds)
+      hipLaunchKernelGGL(boruvka_round<false>, grid, dim3(kLargeThreads), merge_lds, stream, dist, nb,
+                         comp, state, best_d, best_t, edge_d, edge_t, flags, token, sink,
+                         local_radius, topk, (int)per_row, row_ptr, col_idx, col_capacity, salience);
+    else
+      hipLaunchKernelGGL(boruvka_round<true>, grid, dim3(kLargeThreads), last_lds, stream, dist, nb,
+                         comp, state, best_d, best_t, edge_d, edge_t, flags, token, sink,
+                         local_radius, topk, (int)per_row, row_ptr, col_idx, col_capacity, salience);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  const size_t finish_lds = finish_lds_bytes(nb);
-  if ((err = allow_lds(finish_kernel, finish_lds)) != hipSuccess) return err;
-  hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kLargeThreads), finish_lds, stream, nb, state,
-                     edge_d, edge_t, sink, local_radius, topk, (int)per_row, row_ptr, col_idx,
-                     col_capacity, salience);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_segment_schedule(int64_t nb, int64_t segment_blocks, int32_t* row_ptr,
