@@ -297,26 +297,6 @@ __device__ int block_exclusive_scan(int* a, int n, int* tmp) {
   return carry;
 }
 
-// rank[e] += number of items f in [0, n) with before(f, e), for a strict total
-// order `before`; the n^2 comparisons are spread over the workgroup (item e
-// and one part of the f range per thread).  rank must be zero on entry; the
-// caller synchronises afterwards.
-template <int kThreads, typename Before>
-__device__ __forceinline__ void count_ranks(int n, int* rank, Before before) {
-  if (n <= 0) return;
-  const int np = (n + 63) & ~63;
-  const int parts = np >= kThreads ? 1 : kThreads / np;
-  const int len = (n + parts - 1) / parts;
-  for (int x = threadIdx.x; x < np * parts; x += kThreads) {
-    const int e = x % np, q = x / np;
-    if (e >= n) continue;
-    const int f0 = q * len, f1 = (f0 + len < n) ? f0 + len : n;
-    int c = 0;
-    for (int f = f0; f < f1; ++f) c += before(f, e) ? 1 : 0;
-    if (c) atomicAdd(&rank[e], c);
-  }
-}
-
 // Orders this wavefront's earlier LDS writes before its later LDS reads.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1119,18 +1099,24 @@ __device__ __forceinline__ void small_topology(
   }
   const int ne = A.nedges < nb - 1 ? A.nedges : nb - 1;
 
-  // ---- MST edges in ascending (length, tag) order.
-  count_ranks<kSmallThreads>(ne, A.rank, [&](int f, int e) {
-    return edge_less(A.edge_d[f], A.edge_t[f], A.edge_d[e], A.edge_t[e]);
-  });
-  __syncthreads();
-  if (tid < ne) {
-    const int r = A.rank[tid];
-    A.sort_d[r] = A.edge_d[tid];
-    A.sort_t[r] = A.edge_t[tid];
+  // ---- MST edges in ascending (length, tag) order: one key per thread in
+  // registers (the distance matrix is no longer needed; its LDS, at least
+  // 66 x 66 doubles when there are more than 64 edges, holds the exchanges
+  // between wavefronts).
+  {
+    unsigned long long d = kNoLen;
+    uint32_t t = kNoEdge;
+    if (tid < ne) {
+      d = len_bits(A.edge_d[tid]);
+      t = A.edge_t[tid];
+    }
+    sort_keys_in_registers<kSmallThreads>(d, t, ne, reinterpret_cast<uint4*>(smem));
+    if (tid < ne) {
+      A.sort_d[tid] = bits_len(d);
+      A.sort_t[tid] = t;
+    }
   }
   __syncthreads();
-
   if (tid >= 64) return;  // one wavefront from here on
 
   // ---- Elder rule, top-k and CSR rows.
