@@ -1387,16 +1387,21 @@ __global__ __launch_bounds__(256) void distance_kernel(const double* __restrict_
 
 // Per block v (one wavefront each): the least edge from v to a block of
 // another component, stored by device-coherent stores for the merge of the
-// same launch.
-__device__ void nearest_edge(const double* __restrict__ dist, int nb, const int* __restrict__ comp,
-                             int v, double* best_d, uint32_t* best_t) {
+// same launch.  COHERENT: comp was stored in this launch (device-coherent
+// loads skip stale cache lines).
+__device__ __forceinline__ int load_comp(const int* comp, int v, bool coherent) {
+  return coherent ? __hip_atomic_load(comp + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : comp[v];
+}
+template <bool COHERENT>
+__device__ void nearest_edge(const double* __restrict__ dist, int nb, const int* comp, int v,
+                             double* best_d, uint32_t* best_t) {
   const int lane = threadIdx.x & 63;
-  const int cv = comp[v];
+  const int cv = load_comp(comp, v, COHERENT);
   const double* row = dist + (int64_t)v * nb;
   double bd = __builtin_inf();
   uint32_t bt = kNoEdge;
   for (int j = lane; j < nb; j += 64) {
-    if (comp[j] == cv) continue;
+    if (load_comp(comp, j, COHERENT) == cv) continue;
     const double d = row[j];
     const uint32_t t = edge_tag(v, j);
     if (edge_less(d, t, bd, bt)) {
@@ -1438,7 +1443,7 @@ __device__ int merge_components(int nb, int* __restrict__ comp, int* __restrict_
     if (v < nb) {
       bd[k] = load_coherent(reinterpret_cast<const unsigned long long*>(best_d) + v);
       bt[k] = __hip_atomic_load(best_t + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      lcomp[v] = comp[v];
+      lcomp[v] = load_comp(comp, v, true);
       cmin_d[v] = kNoLen;
       cmin_t[v] = kNoEdge;
     }
@@ -1497,7 +1502,8 @@ __device__ int merge_components(int nb, int* __restrict__ comp, int* __restrict_
     __syncthreads();
     if (!changed) break;
   }
-  for (int v = tid; v < nb; v += kLargeThreads) comp[v] = par[lcomp[v]];
+  for (int v = tid; v < nb; v += kLargeThreads)
+    __hip_atomic_store(comp + v, par[lcomp[v]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int n = nedges;
   if (tid == 0) {
@@ -1588,10 +1594,12 @@ __device__ void finish_schedule(int nb, int nedges, const double* edge_d_g, cons
 // launch of ceil(nb / 16) workgroups: every wavefront finds the least edge out
 // of one block's component (nearest_edge); the workgroups then elect the one
 // that ends last (elect_last_workgroup), which merges the components
-// (merge_components) and, in the build's last round (FINISH: by then one
-// component is left), sorts the MST edges, applies the elder rule and emits
-// the CSR rows (finish_schedule).  Rounds after the tree is complete skip the
-// search and the merge.  flags: ceil(nb / 16) + 2 words of workspace.
+// (merge_components).  In the build's last launch (FINISH) that workgroup runs
+// any rounds still needed by itself, then sorts the MST edges, applies the
+// elder rule and emits the CSR rows (finish_schedule).  A launch that starts
+// with the tree complete has nothing to hand between workgroups: it returns
+// at once, except workgroup 0 of the last one, which finishes.  flags:
+// ceil(nb / 16) + 2 words of workspace.
 template <bool FINISH>
 __global__ __launch_bounds__(kLargeThreads) void boruvka_round(
     const double* __restrict__ dist, int nb, int* __restrict__ comp, int* __restrict__ state,
@@ -1601,20 +1609,34 @@ __global__ __launch_bounds__(kLargeThreads) void boruvka_round(
     int64_t col_capacity, double* __restrict__ salience) {
   extern __shared__ __attribute__((aligned(16))) unsigned long long lds_u64[];
   const int tid = threadIdx.x;
-  const unsigned long long epoch = tid < 64 ? load_coherent(&flags[gridDim.x + 1]) : 0ull;
-  const int nedges0 = state[0];
-  const bool done = state[1] != 0;
-  const int v = (int)blockIdx.x * (kLargeThreads / 64) + (tid >> 6);
-  if (!done && v < nb) nearest_edge(dist, nb, comp, v, best_d, best_t);
-  if (!elect_last_workgroup(flags, (int)gridDim.x, host_token, epoch)) return;
-  const int nedges =
-      done ? nedges0 : merge_components(nb, comp, state, nedges0, best_d, best_t, edge_d, edge_t, lds_u64);
-  if (FINISH) {
+  int nedges = state[0];
+  if (state[1] != 0) {  // tree complete before this launch
+    if (!FINISH || blockIdx.x != 0) return;
+  } else {
+    const unsigned long long epoch = tid < 64 ? load_coherent(&flags[gridDim.x + 1]) : 0ull;
+    const int v = (int)blockIdx.x * (kLargeThreads / 64) + (tid >> 6);
+    if (v < nb) nearest_edge<false>(dist, nb, comp, v, best_d, best_t);
+    if (!elect_last_workgroup(flags, (int)gridDim.x, host_token, epoch)) return;
+    nedges = merge_components(nb, comp, state, nedges, best_d, best_t, edge_d, edge_t, lds_u64);
+    if (!FINISH) return;
+    // Rounds past the launched ones: every round adds at least one edge while
+    // two components remain (and at least halves their number), so the loop
+    // ends well within its bound.
+    for (int extra = 0; nedges < nb - 1 && extra < 16; ++extra) {
+      wait_vmem();  // this workgroup's comp stores have completed
+      __syncthreads();
+      for (int u = tid >> 6; u < nb; u += kLargeThreads / 64)
+        nearest_edge<true>(dist, nb, comp, u, best_d, best_t);
+      wait_vmem();
+      __syncthreads();
+      nedges = merge_components(nb, comp, state, nedges, best_d, best_t, edge_d, edge_t, lds_u64);
+    }
     wait_vmem();  // the merge's edge stores have completed before they are read back
     __syncthreads();  // and its LDS is reused
+  }
+  if (FINISH)
     finish_schedule(nb, nedges, edge_d, edge_t, sink, local_radius, topk, per_row != 0, row_ptr,
                     col_idx, col_capacity, salience, reinterpret_cast<double*>(lds_u64));
-  }
 }
 
 __global__ void dense_schedule_kernel(int64_t nb, int32_t* __restrict__ row_ptr,
@@ -1787,8 +1809,11 @@ hipError_t launch_build_schedule(const void* keys, bool bf16, int64_t S, int64_t
   if ((err = allow_lds(boruvka_round<false>, merge_lds)) != hipSuccess) return err;
   if ((err = allow_lds(boruvka_round<true>, last_lds)) != hipSuccess) return err;
   const dim3 grid((unsigned)((nb + kLargeThreads / 64 - 1) / (kLargeThreads / 64)));
-  int rounds = 0;
-  while ((1 << rounds) < nb) ++rounds;  // components at least halve per round
+  // Launched rounds: half the worst case (components at least halve per round)
+  // plus two; typical inputs need fewer, and the last launch runs any others.
+  int log2nb = 0;
+  while ((1 << log2nb) < nb) ++log2nb;
+  const int rounds = log2nb / 2 + 2;
   for (int r = 0; r < rounds; ++r) {
     const unsigned long long token = next_call_token();
     if (r + 1 < rounds)
