@@ -196,9 +196,22 @@ def test_reused_and_prefilled_workspace(tsa, nb, D):
         assert np.allclose(bufs.salience.cpu().numpy(), sal_o, rtol=1e-12, atol=0), label
 
 
+@pytest.mark.parametrize("nb", [256, 512])
+def test_more_boruvka_rounds_than_launched(tsa, nb):
+    """Block v's rows sit at the point whose coordinate l is 2^l times bit l of v.
+    Every Boruvka round then pairs each component with the one that differs in
+    its lowest free bit (all such edges tie in length), so the tree needs exactly
+    log2(nb) rounds, more than the large path launches: the last launch's
+    elected workgroup runs the remaining rounds itself.  Every merge is between
+    equal sizes, so the elder rule's index tie-break decides each one."""
+    bits = int(np.log2(nb))
+    pts = np.array([[((v >> b) & 1) * 2.0 ** b for b in range(bits)] for v in range(nb)])
+    _compare_tied(tsa, _keys_at(pts, D=16), 1, 2, 5, f"binary nb {nb}")
+
+
 def test_largest_schedule(tsa):
     """The builder's limit, 4096 blocks (S = 262,144; the multi-launch path with the
-    LDS union-find), bit-exact against the oracle's all-pairs scan."""
+    LDS edge sort), bit-exact against the oracle's all-pairs scan."""
     keys = workloads.random_normal((64 * 4096, 8), "fp16", 4096)
     rp, ci = _compare(tsa, keys, 2, 2, 24, "nb 4096")
     assert rp.shape[0] == 4097
