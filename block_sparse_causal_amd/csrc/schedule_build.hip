@@ -43,6 +43,7 @@
 #include <atomic>
 #include <chrono>
 #include <mutex>
+#include <type_traits>
 
 #include "kernels.h"
 #include "tsa.h"
@@ -140,6 +141,23 @@ __device__ __forceinline__ void wave_edge_min(double& d, uint32_t& t) {
 }
 
 __device__ __forceinline__ int read_lane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+// v with lane LANE replaced by the uniform value x: one v_writelane_b32 (no
+// builtin for it in this compiler; the lane is an inline constant, so the
+// instruction reads one scalar register).
+template <int LANE>
+__device__ __forceinline__ int write_lane(int v, int x) {
+  static_assert(LANE >= 0 && LANE < 64, "lane");
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x), "n"(LANE));
+  return v;
+}
+// f(integral_constant<int, I>) for I = FIRST .. LAST - 1, unrolled at compile time.
+template <int FIRST, int LAST, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (FIRST < LAST) {
+    f(std::integral_constant<int, FIRST>{});
+    static_for<FIRST + 1, LAST>(f);
+  }
+}
 __device__ __forceinline__ double read_lane(double v, int lane) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
   const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, lane);
@@ -621,8 +639,8 @@ __device__ __forceinline__ void elder_ranks(const uint32_t* st, int ne, int (&de
     const int aw = (int)(tw >> 16), bw = (int)(tw & 0xffffu);
     const int n = __builtin_amdgcn_readfirstlane(ne - base < 64 ? ne - base : 64);
     int absorbed = -1;  // lane k: the block absorbed at edge base + k
-#pragma unroll
-    for (int k = 0; k < 64; ++k) {
+    static_for<0, 64>([&](auto KC) {
+      constexpr int k = decltype(KC)::value;
       if (k < n) {
         const int a = read_lane(aw, k), b = read_lane(bw, k);
         const uint32_t ka = (uint32_t)block_value<SLOTS>(ckey, a);
@@ -632,9 +650,9 @@ __device__ __forceinline__ void elder_ranks(const uint32_t* st, int ne, int (&de
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s)
           ckey[s] = ((uint32_t)ckey[s] == ka || (uint32_t)ckey[s] == kb) ? grown : ckey[s];
-        absorbed = lane == k ? 255 - (int)(lo & 255u) : absorbed;
+        absorbed = write_lane<k>(absorbed, 255 - (int)(lo & 255u));
       }
-    }
+    });
     wave_lds_sync();
     if (absorbed >= 0) dead_at[absorbed] = r;  // each block is absorbed at most once
   }
@@ -697,17 +715,17 @@ __device__ void elder_chunked(const uint32_t* st, int ne, int* parent, int* csiz
       if (id == lane) key = (csize[root] << 12) | (4095 - root);
     }
     int lost = -1;  // lane e: the root absorbed at edge c0 + e
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
+    static_for<0, 32>([&](auto EC) {
+      constexpr int e = decltype(EC)::value;
       if (e < m) {
         const int ia = read_lane(id, 2 * e), ib = read_lane(id, 2 * e + 1);
         const uint32_t ka = (uint32_t)read_lane(key, ia), kb = (uint32_t)read_lane(key, ib);
         const uint32_t hi = ka > kb ? ka : kb, lo = ka > kb ? kb : ka;
         const int grown = (int)(hi + (lo & ~4095u));
         key = ((uint32_t)key == ka || (uint32_t)key == kb) ? grown : key;
-        lost = lane == e ? 4095 - (int)(lo & 4095u) : lost;
+        lost = write_lane<e>(lost, 4095 - (int)(lo & 4095u));
       }
-    }
+    });
     if (lane < m) {
       dead[lost] = c0 + lane;
       absorbed[c0 + lane] = lost;
