@@ -869,6 +869,13 @@ __device__ __forceinline__ void select_and_emit_wave(const int (&dead)[SLOTS], c
   if (kk >= nb || kk == 0) {
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) topm[s] = kk == 0 ? 0ull : (uint64_t)__ballot(lane + 64 * s < nb);
+  } else if (const int cut = ne - kk; cut >= 0 && grp[cut] == cut && !(cut == 0 && zero_grp == 0)) {
+    // No run of equal lengths crosses edge rank cut (and the root, salience 0,
+    // does not tie with a selected block): every block absorbed at an edge of
+    // rank >= cut has a larger key than every other block, so those kk blocks
+    // are the set.
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) topm[s] = (uint64_t)__ballot(lane + 64 * s < nb && dead[s] >= cut);
   } else {
     int thr = 0;
 #pragma unroll
