@@ -78,6 +78,12 @@ __device__ __forceinline__ unsigned long long len_bits(double d) {
   return __builtin_bit_cast(unsigned long long, d);
 }
 __device__ __forceinline__ double bits_len(unsigned long long b) { return __builtin_bit_cast(double, b); }
+// The edge order on length bits, with bitwise operators so that no condition
+// short-circuits into control flow (for loops that take the lesser edge).
+__device__ __forceinline__ bool edge_less_bits(unsigned long long d1, uint32_t t1,
+                                               unsigned long long d2, uint32_t t2) {
+  return (d1 < d2) | ((d1 == d2) & (t1 < t2));
+}
 // NaN (from NaN keys) is treated as +inf so that the edge order stays total.
 __device__ __forceinline__ double finite_or_inf(double d) { return d == d ? d : __builtin_inf(); }
 
@@ -1003,7 +1009,7 @@ __device__ __forceinline__ void small_topology(
     // lanes on distinct banks.
     {
       const int v = tid % nbp, q = tid / nbp;
-      double bd = kInf;
+      unsigned long long bd = len_bits(kInf);
       uint32_t bt = kNoEdge;
       if (v < nb) {
         const int cv = A.comp[v];
@@ -1021,13 +1027,14 @@ __device__ __forceinline__ void small_topology(
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             const uint32_t t = edge_tag(v, j0 + u);
-            const bool take = j0 + u < j1 && cj[u] != cv && edge_less(dj[u], t, bd, bt);
-            bd = take ? dj[u] : bd;
+            const unsigned long long db = len_bits(dj[u]);
+            const bool take = (j0 + u < j1) & (cj[u] != cv) & edge_less_bits(db, t, bd, bt);
+            bd = take ? db : bd;
             bt = take ? t : bt;
           }
         }
       }
-      A.part_d[tid] = bd;
+      A.part_d[tid] = bits_len(bd);
       A.part_t[tid] = bt;
     }
     __syncthreads();
@@ -1423,20 +1430,20 @@ __device__ void nearest_edge(const double* __restrict__ dist, int nb, const int*
   const int lane = threadIdx.x & 63;
   const int cv = load_comp(comp, v, COHERENT);
   const double* row = dist + (int64_t)v * nb;
-  double bd = __builtin_inf();
+  unsigned long long bd = len_bits(__builtin_inf());
   uint32_t bt = kNoEdge;
   for (int j = lane; j < nb; j += 64) {
-    if (load_comp(comp, j, COHERENT) == cv) continue;
-    const double d = row[j];
+    const int cj = load_comp(comp, j, COHERENT);
+    const unsigned long long d = len_bits(row[j]);
     const uint32_t t = edge_tag(v, j);
-    if (edge_less(d, t, bd, bt)) {
-      bd = d;
-      bt = t;
-    }
+    const bool take = (cj != cv) & edge_less_bits(d, t, bd, bt);
+    bd = take ? d : bd;
+    bt = take ? t : bt;
   }
-  wave_edge_min(bd, bt);
+  double bdd = bits_len(bd);
+  wave_edge_min(bdd, bt);
   if (lane == 0) {
-    store_coherent(best_d + v, len_bits(bd));
+    store_coherent(best_d + v, len_bits(bdd));
     __hip_atomic_store(best_t + v, bt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
