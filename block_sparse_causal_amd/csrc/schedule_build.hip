@@ -1161,14 +1161,26 @@ __device__ __forceinline__ void small_topology(
 
 // Election of the one workgroup of a launch of nwg workgroups that goes on
 // alone (the scheme is described at schedule_small).  Every value that
-// crosses workgroups (results, flags, the claim) moves by device-coherent
-// accesses that bypass the non-coherent caches, so ordering needs only waits
-// for completion, not cache write-back or invalidation.  Every thread calls it
-// once its cross-workgroup stores are issued; epoch is flags[nwg + 1] as
-// loaded by threads 0..63 at the start of the launch.  The answer is the same
-// in every thread of a workgroup.  flags: nwg + 2 words (flags, claim, epoch),
-// nwg <= kMaxElectFlags.
+// crosses workgroups (results, flags, the claim, the counter) moves by
+// device-coherent accesses that bypass the non-coherent caches, so ordering
+// needs only waits for completion, not cache write-back or invalidation.
+// Every thread calls it once its cross-workgroup stores are issued; epoch is
+// flags[nwg + 1] as loaded by threads 0..63 at the start of the launch.  The
+// answer is the same in every thread of a workgroup.  flags: nwg + 3 words
+// (flags, claim, epoch, counter), nwg <= kMaxElectFlags.
+//
+// The usual path is one atomic add per workgroup on the counter word, whose
+// upper 48 bits hold a tag derived from epoch and whose low 16 bits count the
+// workgroups that are done: the one that takes the count to nwg is the last.
+// The elected workgroup advances epoch and leaves the counter at the next
+// epoch's tag with a zero count, so the next launch on this workspace finds
+// it ready.  A counter whose tag does not match (the workspace's first build,
+// or one last used with another block count) is seen by every workgroup of
+// the launch, which then elects by the token flags instead.
 constexpr int kMaxElectFlags = 256;
+__device__ __forceinline__ unsigned long long counter_tag(unsigned long long epoch) {
+  return (epoch * 0x9E3779B97F4A7C15ull) >> 16;
+}
 __device__ bool elect_last_workgroup(unsigned long long* flags, int nwg,
                                      unsigned long long host_token, unsigned long long epoch) {
   __shared__ int elected;
@@ -1176,26 +1188,44 @@ __device__ bool elect_last_workgroup(unsigned long long* flags, int nwg,
   wait_vmem();  // this thread's cross-workgroup stores have completed
   __syncthreads();
   if (tid < 64) {
-    const unsigned long long token = host_token + epoch * 0x9E3779B97F4A7C15ull;
-    if (tid == 0) store_coherent(&flags[blockIdx.x], token);
-    wait_vmem();  // the flag store completes before any flag is read
-    unsigned long long f[kMaxElectFlags / 64];  // all loads in flight before any is compared
+    unsigned long long old = 0;
+    if (tid == 0)
+      old = __hip_atomic_fetch_add(&flags[nwg + 2], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(old >> 32), 0) << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)old, 0);
+    bool win;
+    if ((old >> 16) == counter_tag(epoch)) {
+      win = (int)(old & 0xffffu) == nwg - 1;
+    } else {
+      const unsigned long long token = host_token + epoch * 0x9E3779B97F4A7C15ull;
+      if (tid == 0) store_coherent(&flags[blockIdx.x], token);
+      wait_vmem();  // the flag store completes before any flag is read
+      unsigned long long f[kMaxElectFlags / 64];  // all loads in flight before any is compared
 #pragma unroll
-    for (int u = 0; u < kMaxElectFlags / 64; ++u) {
-      const int t = tid + 64 * u;
-      f[u] = (t < nwg && t != (int)blockIdx.x) ? load_coherent(&flags[t]) : token;
-    }
-    bool mine = true;
+      for (int u = 0; u < kMaxElectFlags / 64; ++u) {
+        const int t = tid + 64 * u;
+        f[u] = (t < nwg && t != (int)blockIdx.x) ? load_coherent(&flags[t]) : token;
+      }
+      bool mine = true;
 #pragma unroll
-    for (int u = 0; u < kMaxElectFlags / 64; ++u) mine &= f[u] == token;
-    const bool all = __ballot(!mine) == 0ull;
-    if (tid == 0) {
-      elected = all && __hip_atomic_exchange(&flags[nwg], token, __ATOMIC_RELAXED,
+      for (int u = 0; u < kMaxElectFlags / 64; ++u) mine &= f[u] == token;
+      const bool all = __ballot(!mine) == 0ull;
+      int claim = 0;
+      if (tid == 0)
+        claim = all && __hip_atomic_exchange(&flags[nwg], token, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT) != token;
-      // every workgroup has read epoch: its flag, derived from it, is stored.
-      // Nothing in this launch reads epoch again, so the store is not waited
-      // for (the next launch sees it).
-      if (elected) store_coherent(&flags[nwg + 1], epoch + 1ull);
+      win = __builtin_amdgcn_readlane(claim, 0) != 0;
+    }
+    if (tid == 0) {
+      elected = win;
+      // Every workgroup has read epoch and added to the counter (before its
+      // flag store, on the flag path).  Nothing in this launch reads either
+      // word again, so the stores are not waited for (the next launch sees
+      // them).
+      if (win) {
+        store_coherent(&flags[nwg + 1], epoch + 1ull);
+        store_coherent(&flags[nwg + 2], counter_tag(epoch + 1ull) << 16);
+      }
     }
   }
   __syncthreads();
@@ -1232,19 +1262,22 @@ __host__ __device__ constexpr size_t small_lds_bytes(int nb) {
 // with fma over each quarter of every 64 dims, the quarters then added in
 // order.  Each distance is formed once and stored at (i, j) and (j, i).
 //
-// Then the workgroups elect the one that continues with small_topology.  A
-// workgroup publishes the call's token in its flag once its distances are
-// stored; one that then finds every flag equal to the token tries to swap the
-// token into the claim word, and the one that finds the claim not yet holding
-// it wins.  A workgroup reads the flags only after its own flag store has
-// completed, so the one whose store completes last sees every flag: at least
-// one workgroup reaches the swap, and the swap admits one.  No workgroup waits
-// for another, and no flag needs clearing: stale flags hold older tokens.
-// The token is host_token + epoch * K, with epoch a word of the workspace that
-// every workgroup reads before it publishes its flag and the elected one
-// advances: consecutive calls differ by 1 + K, and so do replays of a captured
-// launch (its host_token frozen) by K.  flags: small_tile_count + 2 words of
-// workspace (flags, claim, epoch).
+// Then the workgroups elect the one that continues with small_topology, without
+// any waiting.  Usually each workgroup adds one to a counter once its
+// distances are stored, and the one that takes the count to the number of
+// workgroups wins (elect_last_workgroup).  When the counter is not set up for
+// the launch (a workspace's first build), a workgroup instead publishes the
+// call's token in its flag; one that then finds every flag equal to the token
+// tries to swap the token into the claim word, and the one that finds the
+// claim not yet holding it wins.  A workgroup reads the flags only after its
+// own flag store has completed, so the one whose store completes last sees
+// every flag: at least one workgroup reaches the swap, and the swap admits one.
+// No flag needs clearing: stale flags hold older tokens.  The token is
+// host_token + epoch * K, with epoch a word of the workspace that every
+// workgroup reads first and the elected one advances: consecutive calls
+// differ by 1 + K, and so do replays of a captured launch (its host_token
+// frozen) by K.  flags: small_tile_count + 3 words of workspace (flags, claim,
+// epoch, counter).
 template <int SLOTS, int TILE, bool BF16>
 __global__ __launch_bounds__(kSmallThreads) void schedule_small(
     const uint16_t* __restrict__ keys, int64_t S, int64_t D, int nb, int block,
@@ -1631,7 +1664,7 @@ __device__ void finish_schedule(int nb, int nedges, const double* edge_d_g, cons
 // elder rule and emits the CSR rows (finish_schedule).  A launch that starts
 // with the tree complete has nothing to hand between workgroups: it returns
 // at once, except workgroup 0 of the last one, which finishes.  flags:
-// ceil(nb / 16) + 2 words of workspace.
+// ceil(nb / 16) + 3 words of workspace.
 template <bool FINISH>
 __global__ __launch_bounds__(kLargeThreads) void boruvka_round(
     const double* __restrict__ dist, int nb, int* __restrict__ comp, int* __restrict__ state,
@@ -1722,7 +1755,7 @@ WorkspaceLayout workspace_layout(int64_t nb, int64_t D) {
   L.flags = take((nb <= kLdsDistBlocks ? (size_t)small_tile_count((int)nb, small_tile_edge((int)nb))
                                        : (size_t)((nb + kLargeThreads / 64 - 1) / (kLargeThreads / 64))) *
                      sizeof(unsigned long long) +
-                 2 * sizeof(unsigned long long));
+                 3 * sizeof(unsigned long long));
   L.total = off;
   return L;
 }

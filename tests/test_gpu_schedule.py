@@ -196,6 +196,32 @@ def test_reused_and_prefilled_workspace(tsa, nb, D):
         assert np.allclose(bufs.salience.cpu().numpy(), sal_o, rtol=1e-12, atol=0), label
 
 
+def test_workspace_shared_across_block_counts(tsa):
+    """One workspace serves builds of several block counts in turn, on both
+    builder paths, with repeats and changes of size: the words one size uses to
+    elect its last workgroup then sit where another size keeps its flags.  Every
+    schedule still matches the oracle."""
+    D = 64
+    seq = [64, 16, 64, 64, 300, 300, 64, 16, 16, 300, 100]
+    need = [int(tsa._lib.tsa_build_schedule_workspace_bytes(64 * nb, D, 64)) for nb in seq]
+    shared = torch.empty(max(need) + 256, dtype=torch.uint8, device="cuda:0")
+    shared.fill_(0x3C)
+    for it, nb in enumerate(seq):
+        S = 64 * nb
+        bufs = tsa.ScheduleBuffers(S, D, 1, 2, 5, "cuda:0", salience=True)
+        bufs.ws_ptr = (shared.data_ptr() + 255) // 256 * 256
+        bufs.ws_bytes = max(need)
+        keys = workloads.random_normal((S, D), "fp16", 4500 + it)
+        tsa.build_schedule_into(keys.to("cuda:0"), bufs)
+        rp_o, ci_o, sal_o = oracle.build_schedule(keys, 64, 1, 2, 5)
+        rp = bufs.row_ptr.cpu().numpy()
+        nnz = int(rp[-1])
+        label = f"build {it} nb {nb}"
+        assert np.array_equal(rp, rp_o), label
+        assert np.array_equal(bufs.col_idx[:nnz].cpu().numpy(), ci_o), label
+        assert np.allclose(bufs.salience.cpu().numpy(), sal_o, rtol=1e-12, atol=0), label
+
+
 @pytest.mark.parametrize("nb", [256, 512])
 def test_more_boruvka_rounds_than_launched(tsa, nb):
     """Block v's rows sit at the point whose coordinate l is 2^l times bit l of v.
