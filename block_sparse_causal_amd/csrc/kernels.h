@@ -22,6 +22,14 @@ hipError_t launch_attention_fwd_pair(const void* q, const void* k, const void* v
                                      const int32_t* col_idx, int64_t nnz, float scale_log2,
                                      hipStream_t stream);
 
+// The same forward at head dim 64 with two adjacent query blocks per workgroup
+// of four waves, each wave taking every key of a block (attention_fwd_duo.hip).
+bool attention_fwd_duo_supported(int D, int64_t S);
+hipError_t launch_attention_fwd_duo(const void* q, const void* k, const void* v, void* out, float* lse,
+                                    bool bf16, int64_t lanes, int64_t S, const int32_t* row_ptr,
+                                    const int32_t* col_idx, int64_t nnz, float scale_log2,
+                                    hipStream_t stream);
+
 // Scheduled attention backward: the dq kernel (CSR rows, also writes the per-row
 // statistics) and then the dkdv kernel (columns of the transposed schedule).
 struct BwdArgs {

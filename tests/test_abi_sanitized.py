@@ -14,8 +14,19 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "block_sparse_causal_amd")
 CSRC = os.path.join(PKG, "csrc")
-KERNEL_SOURCES = ["attention_fwd.hip", "attention_fwd_pair.hip", "attention_bwd.hip", "schedule_build.hip",
-                  "schedule_transpose.hip", "schedule_refine.hip"]
+
+
+def _kernel_sources():
+    """The HIP sources of the library, as its build script lists them."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("_tsa_build_sources", os.path.join(PKG, "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return [s for s in mod.SOURCES if s.endswith(".hip")]
+
+
+KERNEL_SOURCES = _kernel_sources()
 
 
 def _runtime(name):

@@ -1,0 +1,146 @@
+"""Full-output parity of the forward's two-query-block workgroups.
+
+At head dim 64, launches with many workgroups take a kernel in which one
+workgroup serves two adjacent query blocks of a lane: it walks the union of
+the two CSR rows, copies each union block once, and each of its waves takes
+both key halves of the blocks its own row lists.  These cases are sized to
+take that kernel (at least 2048 (lane, query block) pairs), with 17 query
+blocks, so that the last pair has one block past the end, and they cover both
+lane orders (lane counts with and without a factor of 8), both input types,
+topology, dense, random and irregular CSR rows, empty rows, a large softmax
+scale, the lse output and the backward that consumes it.  Every output element
+is compared with the fp64 oracle; output buffers are filled with NaN first,
+so an element the kernel skips fails.  One CSR is shared by every lane (PR
+page "Add topology-derived sparse attention kernel", Summary, third bullet).
+Bars as in the other parity tests: max abs error <= 2e-3 (fp16) / 1e-2
+(bf16); lse within 1e-3 / 4e-3; gradients within 2e-3 / 1e-2 of each
+gradient's largest value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"fp16": 2e-3, "bf16": 1e-2}
+TOL_LSE = {"fp16": 1e-3, "bf16": 4e-3}
+S = 17 * 64  # 17 query blocks: the last pair holds one
+
+
+@pytest.fixture(scope="module")
+def tsa():
+    import block_sparse_causal_amd as m
+
+    return m
+
+
+def _csr(rp, ci):
+    return (torch.from_numpy(np.asarray(rp, np.int32)).to(DEV),
+            torch.from_numpy(np.asarray(ci, np.int32)).to(DEV))
+
+
+def _irregular_csr(nb, seed):
+    """Ascending rows with entries the kernels must skip: negative entries,
+    repeats, future blocks and blocks past the end (a row is read front to
+    back, and an entry is taken only when it lies in 0..i and exceeds the last
+    one taken; the oracle ignores the same entries)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in range(nb):
+        n = int(rng.integers(0, 9))
+        rows.append(np.sort(rng.integers(-2, nb + 3, n)))
+    rp = np.zeros(nb + 1, np.int32)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    ci = np.concatenate(rows).astype(np.int32) if rows else np.zeros(0, np.int32)
+    return rp, ci
+
+
+def _schedule(kind, k, nb, seed):
+    if kind == "topology":
+        rp, ci, _ = oracle.build_schedule(k[0, 0].contiguous(), 64, 1, 2, 3)
+        return rp, ci
+    if kind == "dense":
+        return oracle.dense_causal_schedule(nb)
+    if kind == "random":
+        return workloads.random_csr(nb, seed=seed, density=0.35, allow_empty=True)
+    if kind == "irregular":
+        return _irregular_csr(nb, seed)
+    if kind == "empty":
+        return np.zeros(nb + 1, np.int32), np.zeros(0, np.int32)
+    raise ValueError(kind)
+
+
+CASES = [
+    # (B, H, dtype, schedule, sm_scale)
+    (8, 16, "bf16", "topology", None),   # 128 lanes: per-XCD lane order
+    (3, 43, "fp16", "random", None),     # 129 lanes: plain lane order
+    (2, 64, "bf16", "irregular", None),
+    (8, 16, "fp16", "dense", None),
+    # Nearly one-hot rows: each output is close to one row of v, so v is drawn
+    # with std 0.5 to keep |O| below 4, where half a bf16 ulp of the output
+    # alone would exceed the absolute bar.
+    (8, 17, "bf16", "topology", 30.0),
+    (4, 32, "fp16", "empty", None),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_two_block_workgroups_every_output(tsa, case):
+    B, H, dtype, kind, scale = CASES[case]
+    shape = (B, H, S, 64)
+    w = workloads.Workload("two_block", shape, dtype, seed=800 + case)
+    q, k, v = workloads.make_qkv(w)
+    if scale is not None:
+        v = workloads.random_normal(shape, dtype, 950 + case, std=0.5)
+    nb = S // 64
+    assert B * H * nb >= 2048
+    rp, ci = _schedule(kind, k, nb, 900 + case)
+    rpd, cid = _csr(rp, ci)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.full(qd.shape, float("nan"), dtype=qd.dtype, device=DEV)
+    kwargs = {} if scale is None else {"sm_scale": scale}
+    out, lse = tsa.scheduled_attention(qd, kd, vd, rpd, cid, out=out, return_lse=True, **kwargs)
+    torch.cuda.synchronize()
+    want = oracle.masked_attention(q, k, v, rp, ci, 64, scale=scale)
+    want_lse = oracle.masked_lse(q, k, rp, ci, 64, scale=scale)
+    got = out.double().cpu().numpy()
+    assert np.isfinite(got).all(), "an output element was not written"
+    err = float(np.abs(got - want).max())
+    gl = lse.double().cpu().numpy()
+    assert np.array_equal(np.isneginf(gl), np.isneginf(want_lse)), "rows without a visible key"
+    fin = np.isfinite(want_lse)
+    lerr = float(np.abs(gl[fin] - want_lse[fin]).max()) if fin.any() else 0.0
+    print(f"[{B},{H},{S},64] {dtype} {kind}: nnz {len(ci)}, max abs err {err:.2e}, lse {lerr:.2e}, "
+          f"max|O| {np.abs(want).max():.2f}")
+    assert err <= TOL[dtype]
+    assert lerr <= TOL_LSE[dtype]
+    if kind == "empty":
+        assert torch.count_nonzero(out) == 0
+
+
+def test_backward_after_two_block_forward(tsa):
+    """The backward takes its lse from the forward; at this size the forward runs
+    the two-block kernel."""
+    shape, dtype = (8, 16, S, 64), "bf16"
+    w = workloads.Workload("two_block_bwd", shape, dtype, seed=850)
+    q, k, v = workloads.make_qkv(w)
+    rp, ci, _ = oracle.build_schedule(k[0, 0].contiguous(), 64, 1, 2, 3)
+    rpd, cid = _csr(rp, ci)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    do = workloads.random_normal(shape, dtype, 851)
+    out, lse = tsa.scheduled_attention(qd, kd, vd, rpd, cid, return_lse=True)
+    cp, ri = tsa.schedule_transpose(rpd, cid)
+    dq, dk, dv = tsa.scheduled_attention_backward(qd, kd, vd, out, do.to(DEV), lse, rpd, cid, cp, ri)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, rout, _ = oracle.attention_backward(q, k, v, do, rp, ci)
+    assert float(np.abs(out.double().cpu().numpy() - rout).max()) <= TOL[dtype]
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        gg = g.double().cpu().numpy()
+        assert np.isfinite(gg).all(), name
+        scale = float(np.abs(r).max())
+        gerr = float(np.abs(gg - r).max())
+        print(f"{list(shape)} {dtype} {name}: max err {gerr:.2e} of max|ref| {scale:.2e}")
+        assert gerr <= TOL[dtype] * scale, (name, gerr, scale)
