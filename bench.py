@@ -31,9 +31,9 @@ sys.path.insert(0, ROOT)
 METRIC = "scheduled-attn fwd effective TFLOP/s (% MFMA peak) + sparse/dense-CSR speedup"
 PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}  # MI355X dense MFMA, published
 PARITY_BAR = {"fp16": 2e-3, "bf16": 1e-2}  # max abs error of the output against the fp64 oracle
-# sources of the attention forward kernel (its own file and the shared device helpers)
+# sources of the attention forward kernels (their files and the shared device helpers)
 ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_causal_amd", "csrc", f)
-                for f in ("attention_fwd.hip", "attention_fwd_pair.hip", "mfma_tile.h")]
+                for f in ("attention_fwd.hip", "attention_fwd_duo.hip", "mfma_tile.h")]
 
 
 def _kernel_hash() -> str:

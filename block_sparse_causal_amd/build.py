@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtsa.so")
 ARCH = os.environ.get("TSA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["attention_fwd.hip", "attention_fwd_pair.hip", "attention_fwd_duo.hip", "attention_bwd.hip", "schedule_build.hip", "schedule_transpose.hip", "schedule_refine.hip", "tsa_api.cpp"]
+SOURCES = ["attention_fwd.hip", "attention_fwd_duo.hip", "attention_bwd.hip", "schedule_build.hip", "schedule_transpose.hip", "schedule_refine.hip", "tsa_api.cpp"]
 
 COMMON = [
     f"--offload-arch={ARCH}",
@@ -65,7 +65,7 @@ def _run(cmd: list[str]) -> None:
 # contract (their scores' max then needs no NaN quieting of the MFMA results).
 EXTRA = {
     "attention_fwd.hip": ["-fno-honor-nans"],
-    "attention_fwd_pair.hip": ["-fno-honor-nans"],
+    "attention_fwd_duo.hip": ["-fno-honor-nans"],
 }
 
 

@@ -508,14 +508,14 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
   // the launch has enough (lane, query block) pairs that the halved grid still
   // fills every CU four workgroups deep (256 CUs x 4 x 2 pairs); below that the
   // one-block kernel's twice larger grid is faster.
-  if (D == 128 && attention_fwd_pair_supported(D, S))
-    return launch_attention_fwd_pair(q, k, v, out, lse, bf16, lanes, S, D, row_ptr, col_idx, nnz,
-                                     scale_log2, stream);
+  if (D == 128 && attention_fwd_duo_supported(D, S))
+    return launch_attention_fwd_duo(q, k, v, out, lse, bf16, lanes, S, D, row_ptr, col_idx, nnz,
+                                    scale_log2, stream);
   constexpr int64_t kDuoMinPairs = 2048;
   const int64_t nb = (S + kBlock - 1) / kBlock;
   if (D == 64 && lanes * nb >= kDuoMinPairs && attention_fwd_duo_supported(D, S))
-    return launch_attention_fwd_duo(q, k, v, out, lse, bf16, lanes, S, row_ptr, col_idx, nnz, scale_log2,
-                                    stream);
+    return launch_attention_fwd_duo(q, k, v, out, lse, bf16, lanes, S, D, row_ptr, col_idx, nnz,
+                                    scale_log2, stream);
 #define TSA_FWD_CASE(DD)                                                                              \
   if (D == DD)                                                                                      \
     return bf16 ? launch_typed<DD, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream) \

@@ -93,14 +93,13 @@ struct DuoCursor {
   }
 };
 
-template <bool BF16>
+template <int D, bool BF16>
 __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t nnz,
     int S, int nb, int64_t lane_base, float scale_log2, float inv_scale_log2) {
   using E = Elem<BF16>;
-  constexpr int D = 64;
   constexpr int kStepsD = D / 16;
   constexpr int kTilesD = D / 32;
   constexpr int kRowBytes = D * 2;
@@ -112,6 +111,11 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   constexpr float kRescaleSlack = 8.0f;
   constexpr int kStages = 2;
   constexpr int kHalfKeyBytes = 32 * kRowBytes;  // second key half: 32 rows further
+  // Row sums: at head dim 64 the softmax, not the matrix core, bounds the loop,
+  // so the sums of the rounded P run on the MFMA (two 16x16x32 products against
+  // a 0/1 selector; lane l then holds the sum of query l % 32); at 128 each
+  // lane sums its half-wave's share with v_dot2.
+  constexpr bool kMfmaSums = D <= 64;
   static_assert((kTileBytes / 1024) % kWaves == 0 && kFillOps % 2 == 0, "fill ops split K | V");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
@@ -209,6 +213,7 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   float neg_m = __builtin_inff();     // -m_use (written only on a rescale)
   float thr_raw = -__builtin_inff();  // trigger threshold for the raw-score max
   f32x4 l_acc = f32x4{};              // row sums of the rounded P on the matrix core
+  float l_run = 0.0f;                 // or this half-wave's share of them
   const u32x4 sum_sel = row_sum_selector<E>(l);
   bool started = false;
 
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   auto compute_half = [&](int j, auto T_c, auto KH_c) {
     constexpr int KH = decltype(KH_c)::value;
     constexpr int kOff = decltype(T_c)::value * kStageBytes + KH * kHalfKeyBytes;
-    static_assert(kOff + kStageBytes <= 65536, "offsets fit the LDS offset field");
+    static_assert(kOff + kTileBytes + 20 * kRowBytes < 65536, "offsets fit the LDS offset field");
     if (j == my_i && KH > qh) return;  // diagonal block: this key half is fully masked
     u32x4 ka[kStepsD];
 #pragma unroll
@@ -262,7 +267,10 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
       const float thr = (m_new + kRescaleSlack) * inv_scale_log2;
       thr_raw = thr - __builtin_fabsf(thr) * 0x1p-20f;
       if (started) {
-        l_acc *= alpha;
+        if constexpr (kMfmaSums)
+          l_acc *= alpha;
+        else
+          l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < kTilesD; ++dt) o[dt] *= alpha;
       }
@@ -285,8 +293,15 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * gg + 2 * xx + 1], scale_log2, neg_m));
         pb[gg][xx] = E::pack(p0, p1);
       }
-    l_acc = E::mfma16(sum_sel, pb[0], l_acc);
-    l_acc = E::mfma16(sum_sel, pb[1], l_acc);
+    if constexpr (kMfmaSums) {
+      l_acc = E::mfma16(sum_sel, pb[0], l_acc);
+      l_acc = E::mfma16(sum_sel, pb[1], l_acc);
+    } else {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int xx = 0; xx < 4; ++xx) l_run = E::add_pair(pb[gg][xx], l_run);
+    }
     lds_wait_all(va);
 #pragma unroll
     for (int dt = 0; dt < kTilesD; ++dt)
@@ -337,7 +352,7 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   // O / l rounded to the input type (rows with no visible key get 0).  Lane l
   // holds the row sum of query l % 32 in l_acc[0] and dims 32t + 8(r/4) + 4h +
   // r%4 of that query in register r of o[t].
-  const float l_tot = l_acc[0];
+  const float l_tot = kMfmaSums ? l_acc[0] : sum_with_other_half(l_run);
   // v_rcp_f32 (1 ulp): once a row has a visible key, l_tot >= 1 (the element
   // that set the offset contributes exactly 1), far from the denormal range
   const float inv = l_tot > 0.0f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
@@ -358,7 +373,7 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   }
 }
 
-template <bool BF16>
+template <int D, bool BF16>
 hipError_t launch_duo_typed(const void* q, const void* k, const void* v, void* out, float* lse,
                             int64_t lanes, int64_t S, const int32_t* row_ptr, const int32_t* col_idx,
                             int64_t nnz, float scale_log2, hipStream_t stream) {
@@ -369,7 +384,7 @@ hipError_t launch_duo_typed(const void* q, const void* k, const void* v, void* o
   const int64_t max_lanes = ((int64_t(1) << 31) / kDuoThreads) & ~int64_t(7);
   for (int64_t l0 = 0; l0 < lanes; l0 += max_lanes) {
     const int64_t nl = lanes - l0 < max_lanes ? lanes - l0 : max_lanes;
-    hipLaunchKernelGGL((attention_fwd_duo_kernel<BF16>), dim3((unsigned)nl, (unsigned)npairs),
+    hipLaunchKernelGGL((attention_fwd_duo_kernel<D, BF16>), dim3((unsigned)nl, (unsigned)npairs),
                        dim3(kDuoThreads), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
                        (const uint16_t*)v, (uint16_t*)out, lse, row_ptr, col_idx, nnz, (int)S, (int)nb,
                        l0, scale_log2, 1.0f / scale_log2);
@@ -384,15 +399,20 @@ hipError_t launch_duo_typed(const void* q, const void* k, const void* v, void* o
 // grid.y holds the pair positions: at most 65535 of them (S up to 8 M tokens).
 bool attention_fwd_duo_supported(int D, int64_t S) {
   const int64_t npairs = ((S + kBlock - 1) / kBlock + kDuoRows - 1) / kDuoRows;
-  return D == 64 && npairs <= 65535;
+  return (D == 64 || D == 128) && npairs <= 65535;
 }
 
 hipError_t launch_attention_fwd_duo(const void* q, const void* k, const void* v, void* out, float* lse,
-                                    bool bf16, int64_t lanes, int64_t S, const int32_t* row_ptr,
+                                    bool bf16, int64_t lanes, int64_t S, int D, const int32_t* row_ptr,
                                     const int32_t* col_idx, int64_t nnz, float scale_log2,
                                     hipStream_t stream) {
-  return bf16 ? launch_duo_typed<true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream)
-              : launch_duo_typed<false>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream);
+  if (D == 64)
+    return bf16 ? launch_duo_typed<64, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream)
+                : launch_duo_typed<64, false>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream);
+  if (D == 128)
+    return bf16 ? launch_duo_typed<128, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream)
+                : launch_duo_typed<128, false>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tsa

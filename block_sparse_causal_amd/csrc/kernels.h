@@ -14,19 +14,12 @@ hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, voi
                                 const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                                 float scale_log2, hipStream_t stream);
 
-// The same forward with two adjacent query blocks per workgroup sharing every
-// K/V tile (see attention_fwd_pair.hip); for the head dims it supports.
-bool attention_fwd_pair_supported(int D, int64_t S);
-hipError_t launch_attention_fwd_pair(const void* q, const void* k, const void* v, void* out, float* lse,
-                                     bool bf16, int64_t lanes, int64_t S, int D, const int32_t* row_ptr,
-                                     const int32_t* col_idx, int64_t nnz, float scale_log2,
-                                     hipStream_t stream);
-
-// The same forward at head dim 64 with two adjacent query blocks per workgroup
-// of four waves, each wave taking every key of a block (attention_fwd_duo.hip).
+// The same forward at head dims 64 and 128 with two adjacent query blocks per
+// workgroup of four waves, each wave taking every key of a block
+// (attention_fwd_duo.hip).
 bool attention_fwd_duo_supported(int D, int64_t S);
 hipError_t launch_attention_fwd_duo(const void* q, const void* k, const void* v, void* out, float* lse,
-                                    bool bf16, int64_t lanes, int64_t S, const int32_t* row_ptr,
+                                    bool bf16, int64_t lanes, int64_t S, int D, const int32_t* row_ptr,
                                     const int32_t* col_idx, int64_t nnz, float scale_log2,
                                     hipStream_t stream);
 
