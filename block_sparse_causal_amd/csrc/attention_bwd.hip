@@ -371,6 +371,234 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// dq kernel, two query blocks per workgroup
+// ----------------------------------------------------------------------------
+// The dq kernel's work for the query-block pair (2g, 2g+1) of one lane in one
+// workgroup of 4 waves: wave w owns query half w & 1 of block 2g + (w >> 1) and
+// takes both key halves of every block its row lists, one after the other, into
+// one dQ^T accumulator, so no merge of key halves is needed.  The workgroup
+// walks the union of the two CSR rows (as the forward's two-block kernel);
+// each union block's K and V tiles are copied once and serve both rows, which
+// share most of their blocks.  Used for launches with enough (lane, query
+// block) pairs that the halved grid still fills the CUs.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t nnz, int S,
+    int nb, int npairs, int64_t lane_base, float scale_log2, float scale, float2* __restrict__ stats,
+    uint16_t* __restrict__ dq) {
+  using E = Elem<BF16>;
+  using G = Geo<D>;
+  constexpr int kStepsD = G::kStepsD, kTilesD = G::kTilesD, kTileBytes = G::kTileBytes;
+  constexpr int kStageBytes = 2 * kTileBytes;  // [K tile | V tile]
+  constexpr int kHalfKeyBytes = 32 * G::kRowBytes;  // key half 1: 32 rows further, same swizzle
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rsel = w >> 1;  // which query block of the pair
+  const int qh = w & 1;     // query half of that block
+  const int l = tid & 63, h = l >> 5, n = l & 31, g = l >> 4, gi = l & 15;
+
+  int64_t lane;
+  int pos;
+  grid_position(npairs, lane_base, lane, pos);
+  const int pair = npairs - 1 - pos;  // longest rows first
+  const int my_i = 2 * pair + rsel;   // >= nb: this wave's block is past the end
+  const int64_t lane_off = lane * (int64_t)S * D;
+  const uint16_t* kg = k + lane_off;
+  const uint16_t* vg = v + lane_off;
+
+  // Stationary operands of query row qrow (as in the one-block dq kernel).
+  const int qrow = my_i * kBlock + 32 * qh + n;
+  const int qrow_c = qrow < S ? qrow : S - 1;
+  const int64_t row_off = lane_off + (int64_t)qrow_c * D + 8 * h;
+  u32x4 qop[kStepsD], dop[kStepsD];
+  float delta = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) {
+    qop[c] = *(const u32x4*)(q + row_off + 16 * c);
+    dop[c] = *(const u32x4*)(dout + row_off + 16 * c);
+    const u32x4 oc = *(const u32x4*)(o + row_off + 16 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) delta = E::dot_pair(dop[c][e], oc[e], delta);
+  }
+  delta = sum_with_other_half(delta);
+  float lse2 = lse[lane * (int64_t)S + qrow_c] * kLog2e;
+  if (qrow < S) stats[lane * (int64_t)S + qrow] = float2{lse2, delta};
+
+  // Both rows' walkers: the union of the rows in ascending order.
+  ListWalker walk[2];
+  int head[2], last[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 2 * pair + r;
+    if (row < nb) {
+      walk[r].init(row_ptr, col_idx, nnz, row, 0, row, l);
+    } else {
+      walk[r].p = walk[r].end = walk[r].win = 0;
+      walk[r].cols = -1;
+      walk[r].lo = 0;
+      walk[r].hi = -1;
+      walk[r].idx_ = col_idx;
+      walk[r].l_ = l;
+    }
+    last[r] = -1;
+  }
+  // Every load above has landed before any copy is queued, so the ring's waits
+  // below count copies only.
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) {
+    asm volatile("" : "+v"(qop[c]));
+    asm volatile("" : "+v"(dop[c]));
+  }
+  asm volatile("" : "+v"(lse2), "+v"(delta));
+#pragma unroll
+  for (int r = 0; r < 2; ++r) head[r] = walk[r].next(-1);
+  // Next block of the union (-1: none); `mine` tells whether this wave's row lists it.
+  auto next_block = [&](bool& mine) -> int {
+    int j = -1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (head[r] >= 0 && (j < 0 || head[r] < j)) j = head[r];
+    mine = false;
+    if (j < 0) return -1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (head[r] == j) {
+        if (r == rsel) mine = true;
+        last[r] = j;
+        head[r] = walk[r].next(j);
+      }
+    return j;
+  };
+
+  uint32_t fill_off[G::kTileOps];
+  fill_offsets<D>(fill_off, w, l);
+  auto fill = [&](int j, uint8_t* stage) {
+    const int rows = S - j * kBlock < kBlock ? S - j * kBlock : kBlock;
+    copy_block_to_lds<G::kTileOps, G::kTileOps / 2, kWaves>(kg + (int64_t)j * kBlock * D,
+                                                           vg + (int64_t)j * kBlock * D,
+                                                           rows * G::kRowBytes, fill_off, stage, w);
+  };
+
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)&ring[0];
+  uint32_t a_addr[kStepsD];
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) a_addr[c] = row_read_addr<D>(base, 0, n, h, c);
+  uint32_t t_addr[kTilesD][2];
+#pragma unroll
+  for (int dt = 0; dt < kTilesD; ++dt) tr_read_addrs<D>(t_addr[dt], base, 0, g, gi, dt);
+
+  f32x16 acc[kTilesD];
+#pragma unroll
+  for (int dt = 0; dt < kTilesD; ++dt) acc[dt] = f32x16{};
+
+  // Key half KH of block j, held by ring stage T (both compile-time).
+  auto compute_half = [&](int j, auto T_c, auto KH_c) {
+    constexpr int KH = decltype(KH_c)::value;
+    constexpr int kOff = decltype(T_c)::value * kStageBytes + KH * kHalfKeyBytes;
+    if (j == my_i && KH > qh) return;  // keys of this half all after the queries
+    u32x4 ka[kStepsD], va[kStepsD];
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) {
+      ka[c] = lds_read_b128<kOff>(a_addr[c]);
+      va[c] = lds_read_b128<kOff + kTileBytes>(a_addr[c]);
+    }
+    lds_wait_all(ka);
+    lds_wait_all(va);
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) s = E::mfma(ka[c], qop[c], s);
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) dp = E::mfma(va[c], dop[c], dp);
+    u32x2 kt[kTilesD * 4];
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt) tr_reads<kOff, G::kRowBytes>(&kt[dt * 4], t_addr[dt]);
+    if (j == my_i && KH == qh) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kpos = 16 * (r >> 3) + 8 * h + (r & 7);
+        if (kpos > n) s[r] = -__builtin_inff();
+      }
+    }
+    u32x4 pb[2];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 8 * gg + 2 * x;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -lse2));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, -lse2));
+        pb[gg][x] = E::pack(p0 * (dp[r] - delta), p1 * (dp[r + 1] - delta));
+      }
+    lds_wait_all(kt);
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt)
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) acc[dt] = E::mfma(tr_operand(&kt[dt * 4], gg), pb[gg], acc[dt]);
+  };
+
+  // Ring over the union: the first two blocks are queued here, one per stage;
+  // at step t the wave waits for stage t's copies (the other stage's may stay in
+  // flight), passes the barrier, queues the next union block into the stage
+  // computed one step earlier, and computes both key halves when its row lists
+  // the block.
+  int blk[2];
+  bool mine[2] = {false, false};
+  blk[0] = next_block(mine[0]);
+  blk[1] = blk[0] >= 0 ? next_block(mine[1]) : -1;
+  if (blk[0] >= 0) {
+    fill(blk[0], ring);
+    if (blk[1] >= 0) fill(blk[1], ring + kStageBytes);
+    bool pre = blk[1] >= 0;
+    bool done = false;
+    auto step = [&](auto T_c) {
+      constexpr int t = decltype(T_c)::value;
+      constexpr int refill = t ^ 1;
+      if (pre)
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(G::kTileOps));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      ring_barrier();
+      if (!pre) {
+        blk[refill] = next_block(mine[refill]);
+        if (blk[refill] >= 0) fill(blk[refill], ring + refill * kStageBytes);
+      }
+      pre = false;
+      if (mine[t]) {
+        compute_half(blk[t], T_c, std::integral_constant<int, 0>{});
+        compute_half(blk[t], T_c, std::integral_constant<int, 1>{});
+      }
+      done = blk[refill] < 0;
+    };
+    while (!done) {
+      step(std::integral_constant<int, 0>{});
+      if (!done) step(std::integral_constant<int, 1>{});
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+
+  // The wave holds the whole dQ^T of its 32 query rows: scale, pack, store.
+  if (qrow < S && my_i < nb) {
+    uint16_t* drow = dq + lane_off + (int64_t)qrow * D;
+#pragma unroll
+    for (int gq = 0; gq < kTilesD * 4; ++gq) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[gq / 4][4 * (gq % 4) + e] * scale;
+      u32x2 val;
+      val[0] = E::pack(x[0], x[1]);
+      val[1] = E::pack(x[2], x[3]);
+      // group gq: tile gq / 4, register group gq % 4 -> dims 32 (gq / 4) + 8 (gq % 4) + 4h
+      *(u32x2*)(drow + 32 * (gq / 4) + 8 * (gq % 4) + 4 * h) = val;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // dkdv kernel
 // ----------------------------------------------------------------------------
 template <int D, bool BF16>
@@ -610,6 +838,8 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
     merge(std::integral_constant<int, 1>{});
 }
 
+constexpr int64_t kDqDuoMinPairs = 2048;
+
 template <int D, bool BF16>
 hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
   const int64_t nb = (a.S + kBlock - 1) / kBlock;
@@ -617,11 +847,22 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
   const int64_t lanes_per_launch = max_wg / nb > 0 ? max_wg / nb : 1;
   for (int64_t l0 = 0; l0 < a.lanes; l0 += lanes_per_launch) {
     const int64_t nl = a.lanes - l0 < lanes_per_launch ? a.lanes - l0 : lanes_per_launch;
-    hipLaunchKernelGGL((attention_bwd_dq_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
-                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, a.row_ptr, a.col_idx,
-                       a.nnz, (int)a.S, (int)nb, l0, a.scale_log2, a.scale, (float2*)a.stats,
-                       (uint16_t*)a.dq);
+    // Two query blocks per workgroup once the halved grid still fills every CU
+    // (the forward's rule: 2048 (lane, query block) pairs).
+    if (nl * nb >= kDqDuoMinPairs) {
+      const int64_t npairs = (nb + 1) / 2;
+      hipLaunchKernelGGL((attention_bwd_dq_duo_kernel<D, BF16>), dim3((unsigned)(nl * npairs)), dim3(kThreads),
+                         0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                         (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, a.row_ptr, a.col_idx,
+                         a.nnz, (int)a.S, (int)nb, (int)npairs, l0, a.scale_log2, a.scale,
+                         (float2*)a.stats, (uint16_t*)a.dq);
+    } else {
+      hipLaunchKernelGGL((attention_bwd_dq_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
+                         stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                         (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, a.row_ptr, a.col_idx,
+                         a.nnz, (int)a.S, (int)nb, l0, a.scale_log2, a.scale, (float2*)a.stats,
+                         (uint16_t*)a.dq);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
