@@ -8,7 +8,8 @@ take that kernel (at least 2048 (lane, query block) pairs), with 17 query
 blocks, so that the last pair has one block past the end, and they cover both
 lane orders (lane counts with and without a factor of 8), both input types,
 topology, dense, random and irregular CSR rows, empty rows, a large softmax
-scale, the lse output and the backward that consumes it.  Every output element
+scale, the lse output and the backward that consumes it, whose dq kernel takes
+the same two-block form at these sizes (D 32, 64 and 128).  Every output element
 is compared with the fp64 oracle; output buffers are filled with NaN first,
 so an element the kernel skips fails.  One CSR is shared by every lane (PR
 page "Add topology-derived sparse attention kernel", Summary, third bullet).
@@ -121,16 +122,26 @@ def test_two_block_workgroups_every_output(tsa, case):
         assert torch.count_nonzero(out) == 0
 
 
-def test_backward_after_two_block_forward(tsa):
-    """The backward takes its lse from the forward; at this size the forward runs
-    the two-block kernel."""
-    shape, dtype = (8, 16, S, 64), "bf16"
-    w = workloads.Workload("two_block_bwd", shape, dtype, seed=850)
+BWD_CASES = [
+    # (B, H, D, dtype, schedule)
+    (8, 16, 64, "bf16", "topology"),
+    (4, 32, 128, "fp16", "random"),
+    (8, 16, 32, "bf16", "irregular"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BWD_CASES)))
+def test_backward_after_two_block_forward(tsa, case):
+    """The backward takes its lse from the forward; at these sizes the forward
+    and the dq kernel run in their two-block form."""
+    B, H, D, dtype, kind = BWD_CASES[case]
+    shape = (B, H, S, D)
+    w = workloads.Workload("two_block_bwd", shape, dtype, seed=850 + case)
     q, k, v = workloads.make_qkv(w)
-    rp, ci, _ = oracle.build_schedule(k[0, 0].contiguous(), 64, 1, 2, 3)
+    rp, ci = _schedule(kind, k, S // 64, 860 + case)
     rpd, cid = _csr(rp, ci)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    do = workloads.random_normal(shape, dtype, 851)
+    do = workloads.random_normal(shape, dtype, 870 + case)
     out, lse = tsa.scheduled_attention(qd, kd, vd, rpd, cid, return_lse=True)
     cp, ri = tsa.schedule_transpose(rpd, cid)
     dq, dk, dv = tsa.scheduled_attention_backward(qd, kd, vd, out, do.to(DEV), lse, rpd, cid, cp, ri)
