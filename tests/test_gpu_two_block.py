@@ -122,6 +122,60 @@ def test_two_block_workgroups_every_output(tsa, case):
         assert torch.count_nonzero(out) == 0
 
 
+EDGE_CASES = [
+    # (B, H, S, dtype, schedule, v std): sizes at the edges of the two-block grid.
+    # With one or two blocks per lane many rows see a handful of keys, so outputs
+    # come close to single rows of v; v is drawn with std 0.5 there to keep |O|
+    # below 4, where half an ulp of the output's own rounding nears the bars.
+    (8, 16, 17 * 64 - 37, "bf16", "topology", 1.0),  # ragged last block (rows past S)
+    (32, 64, 64, "fp16", "dense", 0.5),              # one block per lane: every pair's second block is past the end
+    (16, 64, 100, "bf16", "random", 0.5),            # two blocks per lane, the second ragged
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE_CASES)))
+def test_two_block_edge_sizes(tsa, case):
+    B, H, S_, dtype, kind, v_std = EDGE_CASES[case]
+    shape = (B, H, S_, 64)
+    nb = -(-S_ // 64)
+    assert B * H * nb >= 2048
+    w = workloads.Workload("two_block_edge", shape, dtype, seed=880 + case)
+    q, k, v = workloads.make_qkv(w)
+    if v_std != 1.0:
+        v = workloads.random_normal(shape, dtype, 885 + case, std=v_std)
+    rp, ci = _schedule(kind, k, nb, 890 + case)
+    rpd, cid = _csr(rp, ci)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.full(qd.shape, float("nan"), dtype=qd.dtype, device=DEV)
+    out, lse = tsa.scheduled_attention(qd, kd, vd, rpd, cid, out=out, return_lse=True)
+    torch.cuda.synchronize()
+    want = oracle.masked_attention(q, k, v, rp, ci, 64)
+    want_lse = oracle.masked_lse(q, k, rp, ci, 64)
+    got = out.double().cpu().numpy()
+    assert np.isfinite(got).all(), "an output element was not written"
+    err = float(np.abs(got - want).max())
+    gl = lse.double().cpu().numpy()
+    assert np.array_equal(np.isneginf(gl), np.isneginf(want_lse))
+    fin = np.isfinite(want_lse)
+    lerr = float(np.abs(gl[fin] - want_lse[fin]).max()) if fin.any() else 0.0
+    print(f"[{B},{H},{S_},64] {dtype} {kind}: nnz {len(ci)}, max abs err {err:.2e}, lse {lerr:.2e}")
+    assert err <= TOL[dtype]
+    assert lerr <= TOL_LSE[dtype]
+    # the backward at the same size (its dq kernel in the two-block form too)
+    do = workloads.random_normal(shape, dtype, 895 + case)
+    cp, ri = tsa.schedule_transpose(rpd, cid)
+    dq, dk, dv = tsa.scheduled_attention_backward(qd, kd, vd, out, do.to(DEV), lse, rpd, cid, cp, ri)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, _, _ = oracle.attention_backward(q, k, v, do, rp, ci)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        gg = g.double().cpu().numpy()
+        assert np.isfinite(gg).all(), name
+        scale = max(float(np.abs(r).max()), 1e-30)
+        gerr = float(np.abs(gg - r).max())
+        print(f"  {name}: max err {gerr:.2e} of max|ref| {scale:.2e}")
+        assert gerr <= TOL[dtype] * scale, (name, gerr, scale)
+
+
 BWD_CASES = [
     # (B, H, D, dtype, schedule)
     (8, 16, 64, "bf16", "topology"),
