@@ -838,6 +838,288 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
     merge(std::integral_constant<int, 1>{});
 }
 
+// ----------------------------------------------------------------------------
+// dkdv kernel, two key blocks per workgroup
+// ----------------------------------------------------------------------------
+// Columns of a causal schedule are unlike their neighbours (a column lists
+// either most later rows, when its block is one every row picks, or only the
+// rows of its local window), but columns of similar length list mostly the
+// same rows.  col_order_kernel ranks the columns by their number of entries,
+// longest first (ties by index), and the dkdv kernel's two-block form pairs
+// ranks 2p and 2p+1: wave w owns key half w & 1 of column order[2p + (w >> 1)]
+// and takes both query halves of every block its column lists, one after the
+// other, into one dK^T and one dV^T, so no merge of query halves is needed.
+// The workgroup walks the union of the two columns; each union block's Q, dO
+// and statistics are copied once.
+//
+// order: nb int32, a permutation of 0..nb-1.  One thread per column: its rank is
+// the number of columns with more entries, plus those with as many and a lower
+// index.  Entry counts are taken from col_ptr clamped to [0, nnz_t], as the
+// walkers read it.
+constexpr int kOrderChunk = 2048;  // column counts staged in LDS at a time
+__global__ __launch_bounds__(256) void col_order_kernel(const int32_t* __restrict__ col_ptr, int nb,
+                                                        int64_t nnz_t, int32_t* __restrict__ order) {
+  __shared__ int cnt[kOrderChunk];
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  auto count = [&](int c) -> int {
+    const int64_t p = min((int64_t)max(col_ptr[c], 0), nnz_t);
+    const int64_t e = max(min((int64_t)col_ptr[c + 1], nnz_t), p);
+    return (int)(e - p);
+  };
+  const int mine = j < nb ? count(j) : 0;
+  int rank = 0;
+  for (int c0 = 0; c0 < nb; c0 += kOrderChunk) {
+    const int n = nb - c0 < kOrderChunk ? nb - c0 : kOrderChunk;
+    __syncthreads();
+    for (int c = threadIdx.x; c < n; c += 256) cnt[c] = count(c0 + c);
+    __syncthreads();
+    if (j < nb)
+      for (int c = 0; c < n; ++c) {
+        const int o = cnt[c];
+        rank += (o > mine) | ((o == mine) & (c0 + c < j));
+      }
+  }
+  if (j < nb) order[rank] = j;
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float2* __restrict__ stats,
+    const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx, int64_t nnz_t,
+    const int32_t* __restrict__ order, int S, int nb, int npairs, int64_t lane_base, float scale_log2,
+    float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+  using E = Elem<BF16>;
+  using G = Geo<D>;
+  constexpr int kStepsD = G::kStepsD, kTilesD = G::kTilesD, kTileBytes = G::kTileBytes;
+  constexpr int kStatBytes = 1024;  // 4 slots of 256 B; slots 0, 1 hold the block's 64 (lse2, Delta)
+  constexpr int kStageBytes = 2 * kTileBytes + kStatBytes;  // [Q tile | dO tile | stats]
+  constexpr int kFillOps = G::kTileOps + 1;
+  constexpr int kHalfRowBytes = 32 * G::kRowBytes;  // query half 1: 32 rows further, same swizzle
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int csel = w >> 1;  // which column of the pair
+  const int kh = w & 1;     // key half owned
+  const int l = tid & 63, h = l >> 5, n = l & 31, g = l >> 4, gi = l & 15;
+
+  int64_t lane;
+  int pos;
+  grid_position(npairs, lane_base, lane, pos);  // longest columns first
+  const int slot = 2 * pos + csel;
+  const int my_j = slot < nb ? order[slot] : -1;  // -1: the pair's second column is past the end
+  const int64_t lane_off = lane * (int64_t)S * D;
+  const uint16_t* qg = q + lane_off;
+  const uint16_t* dog = dout + lane_off;
+  [[maybe_unused]] const float2* sg = stats + lane * (int64_t)S;
+
+  // Stationary operands of key row krow: K^T and V^T as B operands.
+  const int krow = (my_j >= 0 ? my_j : 0) * kBlock + 32 * kh + n;
+  const int krow_c = krow < S ? krow : S - 1;
+  const int64_t row_off = lane_off + (int64_t)krow_c * D + 8 * h;
+  u32x4 kop[kStepsD], vop[kStepsD];
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) {
+    kop[c] = *(const u32x4*)(k + row_off + 16 * c);
+    vop[c] = *(const u32x4*)(v + row_off + 16 * c);
+  }
+  // Both columns' walkers: the union of their rows in ascending order.
+  ListWalker walk[2];
+  int head[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int sr = 2 * pos + r;
+    const int jr = sr < nb ? order[sr] : -1;
+    if (jr >= 0) {
+      walk[r].init(col_ptr, row_idx, nnz_t, jr, jr, nb - 1, l);
+    } else {
+      walk[r].p = walk[r].end = walk[r].win = 0;
+      walk[r].cols = -1;
+      walk[r].lo = 0;
+      walk[r].hi = -1;
+      walk[r].idx_ = row_idx;
+      walk[r].l_ = l;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) {
+    asm volatile("" : "+v"(kop[c]));
+    asm volatile("" : "+v"(vop[c]));
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) head[r] = walk[r].next(-1);
+  auto next_block = [&](bool& mine) -> int {
+    int i = -1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (head[r] >= 0 && (i < 0 || head[r] < i)) i = head[r];
+    mine = false;
+    if (i < 0) return -1;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (head[r] == i) {
+        if (r == csel) mine = true;
+        head[r] = walk[r].next(i);
+      }
+    return i;
+  };
+
+  uint32_t fill_off[G::kTileOps];
+  fill_offsets<D>(fill_off, w, l);
+  // Queue query block i: Q and dO tiles, and its rows' statistics (wave w copies
+  // the 256 bytes (w & 1) into slot w; rows past S read as zero).
+  auto fill = [&](int i, uint8_t* stage) {
+    const int rows = S - i * kBlock < kBlock ? S - i * kBlock : kBlock;
+    copy_block_to_lds<G::kTileOps, G::kTileOps / 2, kWaves>(qg + (int64_t)i * kBlock * D,
+                                                           dog + (int64_t)i * kBlock * D,
+                                                           rows * G::kRowBytes, fill_off, stage, w);
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(sg + (int64_t)i * kBlock), 0, rows * 8, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(stage + 2 * kTileBytes + 256 * w), 4,
+        (uint32_t)(256 * (w & 1) + 4 * l), 0, 0, 0);
+#endif
+  };
+
+  const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)&ring[0];
+  uint32_t a_addr[kStepsD];
+#pragma unroll
+  for (int c = 0; c < kStepsD; ++c) a_addr[c] = row_read_addr<D>(base, 0, n, h, c);
+  uint32_t t_addr[kTilesD][2];
+#pragma unroll
+  for (int dt = 0; dt < kTilesD; ++dt) tr_read_addrs<D>(t_addr[dt], base, 0, g, gi, dt);
+  // Statistics of the query rows of this lane's result registers: register r
+  // holds query row 32qh + 16 (r >> 3) + 8h + (r & 7).
+  const uint32_t st_addr = base + 2 * kTileBytes + 8 * (8 * h);
+
+  f32x16 adk[kTilesD], adv[kTilesD];
+#pragma unroll
+  for (int dt = 0; dt < kTilesD; ++dt) {
+    adk[dt] = f32x16{};
+    adv[dt] = f32x16{};
+  }
+
+  // Query half QH of block i, held by ring stage T (both compile-time).
+  auto compute_half = [&](int i, auto T_c, auto QH_c) {
+    constexpr int QH = decltype(QH_c)::value;
+    constexpr int kOff = decltype(T_c)::value * kStageBytes + QH * kHalfRowBytes;
+    constexpr int kStOff = decltype(T_c)::value * kStageBytes + QH * 256;
+    if (i == my_j && QH < kh) return;  // queries of this half all before the keys
+    u32x4 qa[kStepsD], da[kStepsD], st[8];
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) {
+      qa[c] = lds_read_b128<kOff>(a_addr[c]);
+      da[c] = lds_read_b128<kOff + kTileBytes>(a_addr[c]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      st[e] = lds_read_b128<kStOff>(st_addr + 16 * e);
+      st[4 + e] = lds_read_b128<kStOff + 128>(st_addr + 16 * e);
+    }
+    lds_wait_all(qa);
+    lds_wait_all(da);
+    lds_wait_all(st);
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) s = E::mfma(qa[c], kop[c], s);
+#pragma unroll
+    for (int c = 0; c < kStepsD; ++c) dp = E::mfma(da[c], vop[c], dp);
+    u32x2 qt[kTilesD * 4], dt_[kTilesD * 4];
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt) {
+      tr_reads<kOff, G::kRowBytes>(&qt[dt * 4], t_addr[dt]);
+      tr_reads<kOff + kTileBytes, G::kRowBytes>(&dt_[dt * 4], t_addr[dt]);
+    }
+    if (i == my_j && QH == kh) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qpos = 16 * (r >> 3) + 8 * h + (r & 7);
+        if (qpos < n) s[r] = -__builtin_inff();
+      }
+    }
+    u32x4 pp[2], pd[2];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = 8 * gg + 2 * x;
+        const u32x4 sv = st[4 * gg + x];  // rows r, r + 1: (lse2, Delta) pairs
+        const float l0 = __uint_as_float(sv[0]), d0 = __uint_as_float(sv[1]);
+        const float l1 = __uint_as_float(sv[2]), d1 = __uint_as_float(sv[3]);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, -l0));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, -l1));
+        pp[gg][x] = E::pack(p0, p1);
+        pd[gg][x] = E::pack(p0 * (dp[r] - d0), p1 * (dp[r + 1] - d1));
+      }
+    lds_wait_all(qt);
+    lds_wait_all(dt_);
+#pragma unroll
+    for (int dt = 0; dt < kTilesD; ++dt)
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        adv[dt] = E::mfma(tr_operand(&dt_[dt * 4], gg), pp[gg], adv[dt]);
+        adk[dt] = E::mfma(tr_operand(&qt[dt * 4], gg), pd[gg], adk[dt]);
+      }
+  };
+
+  // Ring over the union, as in the one-column kernel.
+  int blk[2];
+  bool mine[2] = {false, false};
+  blk[0] = next_block(mine[0]);
+  blk[1] = blk[0] >= 0 ? next_block(mine[1]) : -1;
+  if (blk[0] >= 0) {
+    fill(blk[0], ring);
+    if (blk[1] >= 0) fill(blk[1], ring + kStageBytes);
+    bool pre = blk[1] >= 0;
+    bool done = false;
+    auto step = [&](auto T_c) {
+      constexpr int t = decltype(T_c)::value;
+      constexpr int refill = t ^ 1;
+      if (pre)
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(kFillOps));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      ring_barrier();
+      if (!pre) {
+        blk[refill] = next_block(mine[refill]);
+        if (blk[refill] >= 0) fill(blk[refill], ring + refill * kStageBytes);
+      }
+      pre = false;
+      if (mine[t]) {
+        compute_half(blk[t], T_c, std::integral_constant<int, 0>{});
+        compute_half(blk[t], T_c, std::integral_constant<int, 1>{});
+      }
+      done = blk[refill] < 0;
+    };
+    while (!done) {
+      step(std::integral_constant<int, 0>{});
+      if (!done) step(std::integral_constant<int, 1>{});
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+
+  // The wave holds the whole dK^T and dV^T of its 32 key rows: scale dK, pack, store.
+  if (my_j >= 0 && krow < S) {
+    uint16_t* krow_dk = dk + lane_off + (int64_t)krow * D;
+    uint16_t* krow_dv = dv + lane_off + (int64_t)krow * D;
+#pragma unroll
+    for (int gq = 0; gq < kTilesD * 4; ++gq) {
+      float xk[4], xv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xk[e] = adk[gq / 4][4 * (gq % 4) + e] * scale;
+        xv[e] = adv[gq / 4][4 * (gq % 4) + e];
+      }
+      const int col = 32 * (gq / 4) + 8 * (gq % 4) + 4 * h;
+      *(u32x2*)(krow_dk + col) = u32x2{E::pack(xk[0], xk[1]), E::pack(xk[2], xk[3])};
+      *(u32x2*)(krow_dv + col) = u32x2{E::pack(xv[0], xv[1]), E::pack(xv[2], xv[3])};
+    }
+  }
+}
+
 constexpr int64_t kDqDuoMinPairs = 2048;
 
 template <int D, bool BF16>
@@ -866,12 +1148,29 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  // Two key blocks per workgroup under the same rule, paired by entry count.
+  const bool dkdv_duo = a.lanes * nb >= kDqDuoMinPairs;
+  if (dkdv_duo) {
+    hipLaunchKernelGGL(col_order_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, a.col_ptr,
+                       (int)nb, a.nnz_t, a.col_order);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   for (int64_t l0 = 0; l0 < a.lanes; l0 += lanes_per_launch) {
     const int64_t nl = a.lanes - l0 < lanes_per_launch ? a.lanes - l0 : lanes_per_launch;
-    hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
-                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, (const float2*)a.stats, a.col_ptr, a.row_idx, a.nnz_t,
-                       (int)a.S, (int)nb, l0, a.scale_log2, a.scale, (uint16_t*)a.dk, (uint16_t*)a.dv);
+    if (dkdv_duo) {
+      const int64_t npairs = (nb + 1) / 2;
+      hipLaunchKernelGGL((attention_bwd_dkdv_duo_kernel<D, BF16>), dim3((unsigned)(nl * npairs)), dim3(kThreads),
+                         0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                         (const uint16_t*)a.dout, (const float2*)a.stats, a.col_ptr, a.row_idx, a.nnz_t,
+                         (const int32_t*)a.col_order, (int)a.S, (int)nb, (int)npairs, l0, a.scale_log2, a.scale,
+                         (uint16_t*)a.dk, (uint16_t*)a.dv);
+    } else {
+      hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
+                         stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                         (const uint16_t*)a.dout, (const float2*)a.stats, a.col_ptr, a.row_idx, a.nnz_t,
+                         (int)a.S, (int)nb, l0, a.scale_log2, a.scale, (uint16_t*)a.dk, (uint16_t*)a.dv);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

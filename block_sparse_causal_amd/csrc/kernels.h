@@ -34,6 +34,7 @@ struct BwdArgs {
   int64_t nnz_t;
   void *dq, *dk, *dv;
   void* stats;                    // [lanes, S] float2 workspace
+  int32_t* col_order;             // [nb] workspace: columns ranked by entry count
   bool bf16;
   int64_t lanes, S;
   int D;

@@ -469,12 +469,19 @@ int tsa_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* co
   return ok();
 }
 
+// Backward workspace: each row's (lse, Delta) as float2 [lanes, S], then, from
+// the next 16-byte boundary, the column ranking [nb] int32.
+static int64_t bwd_order_offset(int64_t lanes, int64_t S) { return (lanes * S * 8 + 15) / 16 * 16; }
+static int64_t bwd_workspace(int64_t lanes, int64_t S) {
+  return bwd_order_offset(lanes, S) + ((S + 63) / 64) * 4;
+}
+
 size_t tsa_scheduled_attention_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S) {
   if (B < 0 || H < 0 || S < 0) return 0;
   if (B > 0 && H > INT64_MAX / B) return 0;
   const int64_t lanes = B * H;
-  if (lanes > 0 && S > INT64_MAX / 8 / lanes) return 0;
-  return (size_t)(lanes * S * 8);
+  if (lanes > 0 && S > (INT64_MAX / 2) / 8 / lanes) return 0;
+  return (size_t)bwd_workspace(lanes, S);
 }
 
 int tsa_scheduled_attention_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -498,7 +505,7 @@ int tsa_scheduled_attention_bwd(const void* q, const void* k, const void* v, con
       return fail(TSA_ERR_INVALID_ARG, "%s: q, k, v, out, dout, dq, dk and dv must be 16-byte aligned", fn);
   if (((uintptr_t)lse) % 4 != 0 || ((uintptr_t)workspace) % 16 != 0)
     return fail(TSA_ERR_INVALID_ARG, "%s: lse must be 4-byte and workspace 16-byte aligned", fn);
-  const size_t ws = (size_t)(lanes * S * 8);
+  const size_t ws = (size_t)bwd_workspace(lanes, S);
   if (workspace_bytes < ws)
     return fail(TSA_ERR_INVALID_ARG, "%s: workspace of %zu bytes < required %zu", fn,
                 workspace_bytes, ws);
@@ -532,6 +539,7 @@ int tsa_scheduled_attention_bwd(const void* q, const void* k, const void* v, con
   a.row_ptr = row_ptr; a.col_idx = col_idx; a.nnz = nnz;
   a.col_ptr = col_ptr; a.row_idx = row_idx; a.nnz_t = nnz_t;
   a.dq = dq; a.dk = dk; a.dv = dv; a.stats = workspace;
+  a.col_order = (int32_t*)((char*)workspace + bwd_order_offset(lanes, S));
   a.bf16 = dtype == TSA_BF16;
   a.lanes = lanes; a.S = S; a.D = (int)D;
   const double scale = sm_scale > 0.0f ? (double)sm_scale : 1.0 / std::sqrt((double)D);

@@ -345,7 +345,8 @@ int tsa_schedule_transpose(int64_t nb, const int32_t* row_ptr, const int32_t* co
 
 /*
  * Device workspace, in bytes, of tsa_scheduled_attention_bwd: 8 bytes per query
- * row of every lane (B * H * S * 8).  Host-only; 0 for negative or overflowing sizes.
+ * row of every lane (B * H * S * 8), rounded up to 16, plus 4 bytes per key
+ * block (ceil(S / 64) * 4).  Host-only; 0 for negative or overflowing sizes.
  */
 size_t tsa_scheduled_attention_bwd_workspace_bytes(int64_t B, int64_t H, int64_t S);
 
@@ -370,7 +371,8 @@ size_t tsa_scheduled_attention_bwd_workspace_bytes(int64_t B, int64_t H, int64_t
  *   dq, dk, dv  device, q's shape and dtype, written (rounded to nearest even).
  *   workspace   device, >= tsa_scheduled_attention_bwd_workspace_bytes(B, H, S)
  *               bytes, 16-byte aligned, any contents on entry; it holds each
- *               row's (lse, Delta) between the two kernels.
+ *               row's (lse, Delta) between the two kernels and an order of the
+ *               key blocks by column length.
  * All 16-bit tensors 16-byte aligned; dq, dk, dv and the workspace must not
  * overlap each other or any input.  Scores, statistics and accumulators are
  * fp32; P and dS are rounded to the input dtype as MFMA operands.  B, H or S

@@ -247,7 +247,9 @@ def _bwd(lib, **kw):
 
 
 def test_backward_workspace_and_checks_before_gpu(lib):
-    assert lib.tsa_scheduled_attention_bwd_workspace_bytes(4, 16, 4096) == 4 * 16 * 4096 * 8
+    assert lib.tsa_scheduled_attention_bwd_workspace_bytes(4, 16, 4096) == 4 * 16 * 4096 * 8 + 64 * 4
+    assert lib.tsa_scheduled_attention_bwd_workspace_bytes(1, 1, 100) == 800 + 2 * 4
+    assert lib.tsa_scheduled_attention_bwd_workspace_bytes(1, 1, 3) == 32 + 4
     assert lib.tsa_scheduled_attention_bwd_workspace_bytes(-1, 1, 1) == 0
     assert lib.tsa_scheduled_attention_bwd_workspace_bytes(1, 1, 1 << 62) == 0
     assert _bwd(lib, dtype=7) == -1
