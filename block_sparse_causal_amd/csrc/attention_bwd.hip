@@ -1148,8 +1148,11 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // Two key blocks per workgroup under the same rule, paired by entry count.
-  const bool dkdv_duo = a.lanes * nb >= kDqDuoMinPairs;
+  // Two key blocks per workgroup under the same rule, paired by entry count, up
+  // to 4096 key blocks (the ranking compares every pair of columns: at most 16.8 M
+  // comparisons; longer sequences keep one column per workgroup).
+  constexpr int64_t kDkdvDuoMaxBlocks = 4096;
+  const bool dkdv_duo = a.lanes * nb >= kDqDuoMinPairs && nb <= kDkdvDuoMaxBlocks;
   if (dkdv_duo) {
     hipLaunchKernelGGL(col_order_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, a.col_ptr,
                        (int)nb, a.nnz_t, a.col_order);
