@@ -1,6 +1,6 @@
-// Scheduled block-sparse causal attention forward for gfx950 (CDNA4), head dim
-// 64: two adjacent query blocks per workgroup of four waves, each wave taking
-// every key of a visited block.
+// Scheduled block-sparse causal attention forward for gfx950 (CDNA4), head dims
+// 64 and 128: two adjacent query blocks per workgroup of four waves, each wave
+// taking every key of a visited block.
 //
 // Same operation as attention_fwd.hip ("Add topology-derived sparse attention
 // kernel", triton-lang/kernels PR 22, Summary: each 64-row query block visits
@@ -29,7 +29,8 @@
 // kernel's (attention_fwd.hip): S^T = K . Q^T with Q^T in registers, O^T +=
 // V^T . P^T with transposing V reads, key rows permuted so that the S^T
 // registers are the P^T operand, a two-stage ring of [K | V] tiles filled by
-// direct global->LDS copies, lazy rescale, row sums on the matrix core.
+// direct global->LDS copies, lazy rescale, row sums on the matrix core at head
+// dim 64.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
