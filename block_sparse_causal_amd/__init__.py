@@ -35,6 +35,7 @@ from ._abi import declare_signatures
 
 __all__ = [
     "BLOCK",
+    "SUB_BLOCK",
     "TsaError",
     "library_path",
     "schedule_max_nnz",
@@ -51,6 +52,7 @@ __all__ = [
 ]
 
 BLOCK = 64
+SUB_BLOCK = 32  # the smaller block the builder and the forward also take
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtsa.so")
 
@@ -128,8 +130,9 @@ def build_schedule(keys: torch.Tensor, block: int = BLOCK, sink: int = 1, local_
     keys: [S, D] or [B, H, S, D] float16/bfloat16 on a GPU.  Returns int32
     (row_ptr [nb+1], col_idx [nnz]) on the keys' device, nb = ceil(S / block),
     plus the fp64 salience [nb] when ``return_salience``.  Waits for the stream
-    to read back nnz.  block: a multiple of 64; schedules over blocks larger than
-    64 reach the attention entry points through ``refine_schedule``.
+    to read back nnz.  block: 32 or a multiple of 64; schedules over blocks larger
+    than 64 reach the attention entry points through ``refine_schedule``, those
+    over 32-row blocks go to ``scheduled_attention(..., block=32)`` as they are.
     per_row: each row takes its own top-k among its blocks j <= i instead of
     one global top-k set (TSA_TOPK_PER_ROW).
     """
@@ -338,6 +341,12 @@ def _check_index(name, t, device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _check_block(block):
+    # the row_ptr length check needs a positive block; the library decides the rest
+    if not isinstance(block, int) or block <= 0:
+        raise ValueError(f"block must be a positive int, got {block!r}")
+
+
 def _scale_arg(sm_scale):
     scale = 0.0 if sm_scale is None else float(sm_scale)
     if sm_scale is not None and scale <= 0:
@@ -354,12 +363,14 @@ def scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_p
 
     q, k, v: [S, D] or [B, H, S, D], one float16/bfloat16 dtype, contiguous, on
     one GPU.  row_ptr/col_idx: int32 CSR on the same device, shared by every
-    (b, h) lane.  sm_scale defaults to 1/sqrt(D).
+    (b, h) lane, over blocks of ``block`` rows: 64, or SUB_BLOCK (32) at head
+    dims 32, 64 and 128.  sm_scale defaults to 1/sqrt(D).
     """
     code, B, H, S, D = _attention_shape(q, k, v)
     for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
         _check_index(name, t, q.device)
-    nb = -(-S // BLOCK)
+    _check_block(block)
+    nb = -(-S // block)
     if row_ptr.numel() != nb + 1:
         raise ValueError(f"row_ptr must have nb+1 = {nb + 1} entries for S={S}, got {row_ptr.numel()}")
     if out is None:
@@ -384,22 +395,24 @@ def scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_p
 
 
 def prepare_scheduled_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
-                                col_idx: torch.Tensor, out: torch.Tensor, sm_scale: float | None = None):
-    """``scheduled_attention(q, k, v, row_ptr, col_idx, out=out)`` with the
-    arguments checked and marshalled once: returns a callable that queues the
-    forward on the current stream of q's device with one C ABI call (which
-    still validates its arguments).  For loops that launch the same call many
-    times, where the per-call Python work would otherwise set the pace."""
+                                col_idx: torch.Tensor, out: torch.Tensor, sm_scale: float | None = None,
+                                block: int = BLOCK):
+    """``scheduled_attention(q, k, v, row_ptr, col_idx, out=out, block=block)``
+    with the arguments checked and marshalled once: returns a callable that
+    queues the forward on the current stream of q's device with one C ABI call
+    (which still validates its arguments).  For loops that launch the same call
+    many times, where the per-call Python work would otherwise set the pace."""
     code, B, H, S, D = _attention_shape(q, k, v)
     for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
         _check_index(name, t, q.device)
-    if row_ptr.numel() != -(-S // BLOCK) + 1:
+    _check_block(block)
+    if row_ptr.numel() != -(-S // block) + 1:
         raise ValueError("row_ptr must have nb+1 entries")
     if out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor of q's shape, dtype and device")
     keep = (q, k, v, row_ptr, col_idx, out)  # the callable holds the tensors alive
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), code, B, H, S, D, _ptr(row_ptr), _ptr(col_idx),
-            col_idx.numel(), BLOCK, _scale_arg(sm_scale))
+            col_idx.numel(), block, _scale_arg(sm_scale))
     fn, dev = _lib.tsa_scheduled_attention_fwd, q.device
 
     def call():

@@ -500,22 +500,29 @@ hipError_t launch_typed(const void* q, const void* k, const void* v, void* out, 
 }  // namespace
 
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                                bool bf16, int64_t lanes, int64_t S, int D, const int32_t* row_ptr,
-                                const int32_t* col_idx, int64_t nnz, float scale_log2,
-                                hipStream_t stream) {
+                                bool bf16, int64_t lanes, int64_t S, int D, int block,
+                                const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                float scale_log2, hipStream_t stream) {
+  // 32-row blocks: only the two-block kernel walks them (one CSR row per wave).
+  if (block == 32)
+    return attention_fwd_duo_supported(D, S)
+               ? launch_attention_fwd_duo(q, k, v, out, lse, bf16, lanes, S, D, 32, row_ptr,
+                                          col_idx, nnz, scale_log2, stream)
+               : hipErrorInvalidValue;
+  if (block != kBlock) return hipErrorInvalidValue;
   // Head dim 128: two query blocks per workgroup of eight waves share each 32 KB
   // K/V stage.  Head dim 64: two query blocks per workgroup of four waves, once
   // the launch has enough (lane, query block) pairs that the halved grid still
   // fills every CU four workgroups deep (256 CUs x 4 x 2 pairs); below that the
   // one-block kernel's twice larger grid is faster.
   if (D == 128 && attention_fwd_duo_supported(D, S))
-    return launch_attention_fwd_duo(q, k, v, out, lse, bf16, lanes, S, D, row_ptr, col_idx, nnz,
-                                    scale_log2, stream);
+    return launch_attention_fwd_duo(q, k, v, out, lse, bf16, lanes, S, D, kBlock, row_ptr, col_idx,
+                                    nnz, scale_log2, stream);
   constexpr int64_t kDuoMinPairs = 2048;
   const int64_t nb = (S + kBlock - 1) / kBlock;
   if (D == 64 && lanes * nb >= kDuoMinPairs && attention_fwd_duo_supported(D, S))
-    return launch_attention_fwd_duo(q, k, v, out, lse, bf16, lanes, S, D, row_ptr, col_idx, nnz,
-                                    scale_log2, stream);
+    return launch_attention_fwd_duo(q, k, v, out, lse, bf16, lanes, S, D, kBlock, row_ptr, col_idx,
+                                    nnz, scale_log2, stream);
 #define TSA_FWD_CASE(DD)                                                                              \
   if (D == DD)                                                                                      \
     return bf16 ? launch_typed<DD, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream) \

@@ -1,6 +1,6 @@
 // Scheduled block-sparse causal attention forward for gfx950 (CDNA4), head dims
-// 64 and 128: two adjacent query blocks per workgroup of four waves, each wave
-// taking every key of a visited block.
+// 64 and 128 (and 32 with 32-row blocks): two adjacent query blocks per
+// workgroup of four waves, each wave taking every key of a visited block.
 //
 // Same operation as attention_fwd.hip ("Add topology-derived sparse attention
 // kernel", triton-lang/kernels PR 22, Summary: each 64-row query block visits
@@ -24,6 +24,14 @@
 //   Grid: x = lane (remapped so that each of the 8 XCDs holds a contiguous range
 //   of lanes when the lane count is a multiple of 8; workgroup x + y * lanes
 //   runs on XCD x % 8), y = pair position, last pairs (longest rows) first.
+//
+// Schedules over 32-row blocks (SUB): the same workgroup serves the four
+//   32-row query blocks 4g .. 4g+3, which are its waves' query halves, and
+//   each wave walks its own CSR row.  The tiles stay 64 keys: the workgroup
+//   walks the union of the 64-key blocks its four rows touch, and a wave takes
+//   the key half 2J + h of 64-key block J only when its row lists that 32-key
+//   block.  Each wave's work is then exactly a 32 x 32 tile per listed block,
+//   with the causal mask on the tile whose key block equals its query block.
 //
 // Contractions, tile layouts, staging and the softmax are the one-block
 // kernel's (attention_fwd.hip): S^T = K . Q^T with Q^T in registers, O^T +=
@@ -94,12 +102,13 @@ struct DuoCursor {
   }
 };
 
-template <int D, bool BF16>
+// nrows: the CSR's rows (ceil(S / 64), or ceil(S / 32) when SUB).
+template <int D, bool BF16, bool SUB>
 __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ out, float* __restrict__ lse,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t nnz,
-    int S, int nb, int64_t lane_base, float scale_log2, float inv_scale_log2) {
+    int S, int nrows, int64_t lane_base, float scale_log2, float inv_scale_log2) {
   using E = Elem<BF16>;
   constexpr int kStepsD = D / 16;
   constexpr int kTilesD = D / 32;
@@ -117,6 +126,8 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   // a 0/1 selector; lane l then holds the sum of query l % 32); at 128 each
   // lane sums its half-wave's share with v_dot2.
   constexpr bool kMfmaSums = D <= 64;
+  // CSR rows a workgroup walks: the two 64-row blocks, or the four 32-row ones.
+  constexpr int kCursors = SUB ? 4 : kDuoRows;
   static_assert((kTileBytes / 1024) % kWaves == 0 && kFillOps % 2 == 0, "fill ops split K | V");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
@@ -139,7 +150,8 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
     lane = lane_base + (int64_t)x;
   const int npairs = (int)gridDim.y;
   const int pair = npairs - 1 - (int)blockIdx.y;
-  const int my_i = kDuoRows * pair + rsel;  // >= nb: this wave's block is past the end
+  const int my_i = kDuoRows * pair + rsel;  // this wave's 64-row block (past the end: no rows)
+  const int my_q32 = 4 * pair + w;         // and its 32-row query block
 
   const int64_t lane_off = lane * (int64_t)S * D;
   const uint16_t* kg = k + lane_off;
@@ -148,9 +160,9 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   // Column windows of both rows first, then the Q^T operands (lane: query row
   // qrow, dims 16c + 8h .. +7 for step c); the first wait below covers the
   // windows and lets the Q loads stay in flight.
-  DuoCursor rows[kDuoRows];
+  DuoCursor rows[kCursors];
 #pragma unroll
-  for (int r = 0; r < kDuoRows; ++r) rows[r].start(row_ptr, col_idx, nnz, kDuoRows * pair + r, nb, l);
+  for (int r = 0; r < kCursors; ++r) rows[r].start(row_ptr, col_idx, nnz, kCursors * pair + r, nrows, l);
   const int qrow = my_i * kBlock + 32 * qh + n;
   const int qrow_c = qrow < S ? qrow : S - 1;
   u32x4 qop[kStepsD];
@@ -160,23 +172,36 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(kStepsD));  // the windows (older than the Q loads)
 #pragma unroll
-  for (int r = 0; r < kDuoRows; ++r) rows[r].advance(col_idx, l);
+  for (int r = 0; r < kCursors; ++r) rows[r].advance(col_idx, l);
 
-  // Next block of the union of the two rows (-1: none); `mine` tells whether
-  // this wave's row lists it.
-  auto next_block = [&](bool& mine) -> int {
+  // Next 64-key block of the union of the rows (-1: none); `mine` gets bit h
+  // set when this wave computes key half h of it: both halves when its 64-row
+  // block's row lists the block, or (SUB) the halves its 32-row row lists.
+  auto next_block = [&](int& mine) -> int {
     int j = INT_MAX;
 #pragma unroll
-    for (int r = 0; r < kDuoRows; ++r) j = min(j, rows[r].head);
-    mine = false;
+    for (int r = 0; r < kCursors; ++r) j = min(j, SUB ? (rows[r].head == INT_MAX ? INT_MAX : rows[r].head >> 1) : rows[r].head);
+    mine = 0;
     if (j == INT_MAX) return -1;
 #pragma unroll
-    for (int r = 0; r < kDuoRows; ++r)
-      if (rows[r].head == j) {
-        if (r == rsel) mine = true;
-        rows[r].last = j;
-        rows[r].advance(col_idx, l);
+    for (int r = 0; r < kCursors; ++r) {
+      if constexpr (SUB) {
+        // at most the two 32-key blocks of j, in ascending order
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (rows[r].head != INT_MAX && (rows[r].head >> 1) == j) {
+            if (r == w) mine |= 1 << (rows[r].head & 1);
+            rows[r].last = rows[r].head;
+            rows[r].advance(col_idx, l);
+          }
+      } else {
+        if (rows[r].head == j) {
+          if (r == rsel) mine = 3;
+          rows[r].last = j;
+          rows[r].advance(col_idx, l);
+        }
       }
+    }
     return j;
   };
 
@@ -242,7 +267,10 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
     constexpr int KH = decltype(KH_c)::value;
     constexpr int kOff = decltype(T_c)::value * kStageBytes + KH * kHalfKeyBytes;
     static_assert(kOff + kTileBytes + 20 * kRowBytes < 65536, "offsets fit the LDS offset field");
-    if (j == my_i && KH > qh) return;  // diagonal block: this key half is fully masked
+    // 32-row key block 2j + KH against this wave's 32-row query block: later
+    // ones are fully masked (the acceptance rule never lists them under SUB;
+    // on the 64-row diagonal key half 1 is later than query half 0).
+    if (2 * j + KH > my_q32) return;
     u32x4 ka[kStepsD];
 #pragma unroll
     for (int c = 0; c < kStepsD; ++c) ka[c] = lds_read_b128<kOff>(k_addr[c]);
@@ -250,7 +278,7 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
     f32x16 s = f32x16{};
 #pragma unroll
     for (int c = 0; c < kStepsD; ++c) s = E::mfma(ka[c], qop[c], s);
-    if (j == my_i && KH == qh) {  // key position must not exceed query position
+    if (2 * j + KH == my_q32) {  // key position must not exceed query position
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (16 * (r >> 3) + (r & 7) > diag_lim) s[r] = -__builtin_inff();
@@ -320,9 +348,9 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   // the next union block into the stage computed one step earlier, and
   // computes both key halves.
   int blk[kStages];
-  bool mine[kStages];
+  int mine[kStages];
   blk[1] = -1;
-  mine[1] = false;
+  mine[1] = 0;
   blk[0] = next_block(mine[0]);
   if (blk[0] >= 0) fill(blk[0], 0);
   bool done = blk[0] < 0;
@@ -339,10 +367,8 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
     for (int c = 0; c < kStepsD; ++c) asm volatile("" : "+v"(qop[c]));  // loaded (waited above)
     blk[refill] = next_block(mine[refill]);
     if (blk[refill] >= 0) fill(blk[refill], refill);
-    if (mine[t]) {
-      compute_half(blk[t], T_c, std::integral_constant<int, 0>{});
-      compute_half(blk[t], T_c, std::integral_constant<int, 1>{});
-    }
+    if (mine[t] & 1) compute_half(blk[t], T_c, std::integral_constant<int, 0>{});
+    if (mine[t] & 2) compute_half(blk[t], T_c, std::integral_constant<int, 1>{});
   };
   while (!done) {
     step(std::integral_constant<int, 0>{});
@@ -357,10 +383,10 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   // v_rcp_f32 (1 ulp): once a row has a visible key, l_tot >= 1 (the element
   // that set the offset contributes exactly 1), far from the denormal range
   const float inv = l_tot > 0.0f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
-  if (h == 0 && lse != nullptr && qrow < S && my_i < nb)
+  if (h == 0 && lse != nullptr && qrow < S)
     lse[lane * (int64_t)S + qrow] =
         l_tot > 0.0f ? (m_use + __builtin_log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
-  if (qrow < S && my_i < nb) {
+  if (qrow < S) {
     uint16_t* orow = out + lane_off + (int64_t)qrow * D;
 #pragma unroll
     for (int t = 0; t < kTilesD; ++t)
@@ -374,21 +400,22 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool SUB>
 hipError_t launch_duo_typed(const void* q, const void* k, const void* v, void* out, float* lse,
                             int64_t lanes, int64_t S, const int32_t* row_ptr, const int32_t* col_idx,
                             int64_t nnz, float scale_log2, hipStream_t stream) {
   const int64_t nb = (S + kBlock - 1) / kBlock;
+  const int64_t nrows = SUB ? (S + 31) / 32 : nb;
   const int64_t npairs = (nb + kDuoRows - 1) / kDuoRows;
   // grid.x holds lanes; keep grid.x * block below 2^31 work-items per launch, in
   // multiples of 8 lanes so that every launch keeps the per-XCD lane order.
   const int64_t max_lanes = ((int64_t(1) << 31) / kDuoThreads) & ~int64_t(7);
   for (int64_t l0 = 0; l0 < lanes; l0 += max_lanes) {
     const int64_t nl = lanes - l0 < max_lanes ? lanes - l0 : max_lanes;
-    hipLaunchKernelGGL((attention_fwd_duo_kernel<D, BF16>), dim3((unsigned)nl, (unsigned)npairs),
+    hipLaunchKernelGGL((attention_fwd_duo_kernel<D, BF16, SUB>), dim3((unsigned)nl, (unsigned)npairs),
                        dim3(kDuoThreads), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (uint16_t*)out, lse, row_ptr, col_idx, nnz, (int)S, (int)nb,
-                       l0, scale_log2, 1.0f / scale_log2);
+                       (const uint16_t*)v, (uint16_t*)out, lse, row_ptr, col_idx, nnz, (int)S,
+                       (int)nrows, l0, scale_log2, 1.0f / scale_log2);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -400,19 +427,25 @@ hipError_t launch_duo_typed(const void* q, const void* k, const void* v, void* o
 // grid.y holds the pair positions: at most 65535 of them (S up to 8 M tokens).
 bool attention_fwd_duo_supported(int D, int64_t S) {
   const int64_t npairs = ((S + kBlock - 1) / kBlock + kDuoRows - 1) / kDuoRows;
-  return (D == 64 || D == 128) && npairs <= 65535;
+  return (D == 32 || D == 64 || D == 128) && npairs <= 65535;
 }
 
 hipError_t launch_attention_fwd_duo(const void* q, const void* k, const void* v, void* out, float* lse,
-                                    bool bf16, int64_t lanes, int64_t S, int D, const int32_t* row_ptr,
-                                    const int32_t* col_idx, int64_t nnz, float scale_log2,
-                                    hipStream_t stream) {
-  if (D == 64)
-    return bf16 ? launch_duo_typed<64, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream)
-                : launch_duo_typed<64, false>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream);
-  if (D == 128)
-    return bf16 ? launch_duo_typed<128, true>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream)
-                : launch_duo_typed<128, false>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, scale_log2, stream);
+                                    bool bf16, int64_t lanes, int64_t S, int D, int block,
+                                    const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                    float scale_log2, hipStream_t stream) {
+#define TSA_DUO_CASE(DD, SUBB)                                                                          \
+  if (D == DD && (block == 32) == SUBB)                                                               \
+    return bf16 ? launch_duo_typed<DD, true, SUBB>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, \
+                                                   scale_log2, stream)                                 \
+                : launch_duo_typed<DD, false, SUBB>(q, k, v, out, lse, lanes, S, row_ptr, col_idx, nnz, \
+                                                    scale_log2, stream);
+  TSA_DUO_CASE(64, false)
+  TSA_DUO_CASE(128, false)
+  TSA_DUO_CASE(32, true)
+  TSA_DUO_CASE(64, true)
+  TSA_DUO_CASE(128, true)
+#undef TSA_DUO_CASE
   return hipErrorInvalidValue;
 }
 

@@ -7,21 +7,23 @@
 
 namespace tsa {
 
-// Scheduled attention forward over `lanes` lanes of [S, D] (D = 64 or 128);
-// lse [lanes, S] (natural log of each row's denominator) is written when not null.
+// Scheduled attention forward over `lanes` lanes of [S, D] (D = 32, 64, 128 or
+// 256) with a CSR over blocks of `block` rows (64, or 32 at D <= 128); lse
+// [lanes, S] (natural log of each row's denominator) is written when not null.
 hipError_t launch_attention_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                                bool bf16, int64_t lanes, int64_t S, int D,
+                                bool bf16, int64_t lanes, int64_t S, int D, int block,
                                 const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
                                 float scale_log2, hipStream_t stream);
 
-// The same forward at head dims 64 and 128 with two adjacent query blocks per
-// workgroup of four waves, each wave taking every key of a block
-// (attention_fwd_duo.hip).
+// The same forward at head dims 32, 64 and 128 with two adjacent 64-row query
+// blocks per workgroup of four waves (attention_fwd_duo.hip); with block 32 the
+// CSR is over 32-row blocks and each wave walks the row of its 32 queries.
+// Supported when D is one of those and the grid's pair count fits (S <= 8 M).
 bool attention_fwd_duo_supported(int D, int64_t S);
 hipError_t launch_attention_fwd_duo(const void* q, const void* k, const void* v, void* out, float* lse,
-                                    bool bf16, int64_t lanes, int64_t S, int D, const int32_t* row_ptr,
-                                    const int32_t* col_idx, int64_t nnz, float scale_log2,
-                                    hipStream_t stream);
+                                    bool bf16, int64_t lanes, int64_t S, int D, int block,
+                                    const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                                    float scale_log2, hipStream_t stream);
 
 // Scheduled attention backward: the dq kernel (CSR rows, also writes the per-row
 // statistics) and then the dkdv kernel (columns of the transposed schedule).

@@ -164,12 +164,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<FIRST + 1, LAST>(f);
   }
 }
-__device__ __forceinline__ double read_lane(double v, int lane) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, lane);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
 
 // Value of per-block register array `a` for block x (x uniform; block x lives
 // in lane x % 64, slot x / 64).

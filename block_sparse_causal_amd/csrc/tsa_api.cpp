@@ -54,10 +54,14 @@ int check_device_ptr(const void* p, const char* name) {
   return TSA_OK;
 }
 
-// Block sizes the schedule builder and the refinement accept.
+// Block sizes the refinement accepts: multiples of the kernels' 64-row block.
 bool block_ok(int32_t block) {
   return block >= TSA_BLOCK && block <= TSA_MAX_SCHEDULE_BLOCK && block % TSA_BLOCK == 0;
 }
+
+// Block sizes the schedule builder accepts: those, and 32-row blocks, which the
+// forward takes directly.
+bool build_block_ok(int32_t block) { return block == TSA_SUB_BLOCK || block_ok(block); }
 
 int64_t row_cap(int32_t sink, int32_t local_radius, int32_t topk) {
   return (int64_t)sink + (int64_t)local_radius + 1 + (int64_t)topk;
@@ -66,18 +70,25 @@ int64_t row_cap(int32_t sink, int32_t local_radius, int32_t topk) {
 
 // Checks shared by the attention entry points (no GPU call); sets *lanes.
 // max_d: the largest head dim the entry point takes (256 forward, 128 backward);
-// the others are 32, 64 and 128.
+// the others are 32, 64 and 128.  sub_block: the entry point also takes
+// schedules over 32-row blocks (the forward, at head dims up to 128).
 int check_attention_args(const char* fn, int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D,
-                         int64_t nnz, int32_t block, float sm_scale, int64_t max_d, int64_t* lanes) {
+                         int64_t nnz, int32_t block, float sm_scale, int64_t max_d, bool sub_block,
+                         int64_t* lanes) {
   if (dtype != TSA_F16 && dtype != TSA_BF16)
     return fail(TSA_ERR_INVALID_ARG, "%s: dtype must be TSA_F16 or TSA_BF16", fn);
   if (B < 0 || H < 0 || S < 0 || nnz < 0)
     return fail(TSA_ERR_INVALID_ARG, "%s: B, H, S and nnz must be >= 0", fn);
-  if (block != TSA_BLOCK)
-    return fail(TSA_ERR_UNSUPPORTED, "%s: block must be %d, got %d", fn, TSA_BLOCK, block);
+  if (block != TSA_BLOCK && !(sub_block && block == TSA_SUB_BLOCK))
+    return fail(TSA_ERR_UNSUPPORTED, "%s: block must be %d%s, got %d", fn, TSA_BLOCK,
+                sub_block ? " or 32" : "", block);
   if (!(D == 32 || D == 64 || D == 128 || D == 256) || D > max_d)
     return fail(TSA_ERR_UNSUPPORTED, "%s: head dim must be 32, 64, 128%s, got %lld", fn,
                 max_d >= 256 ? " or 256" : "", (long long)D);
+  if (block == TSA_SUB_BLOCK && !tsa::attention_fwd_duo_supported((int)D, S))
+    return fail(TSA_ERR_UNSUPPORTED,
+                "%s: 32-row blocks need head dim 32, 64 or 128 and S <= %lld, got D=%lld S=%lld",
+                fn, (long long)65535 * 128, (long long)D, (long long)S);
   if (std::isnan(sm_scale) || std::isinf(sm_scale))
     return fail(TSA_ERR_INVALID_ARG, "%s: sm_scale must be finite", fn);
   if (S > INT32_MAX - TSA_BLOCK) return fail(TSA_ERR_SHAPE, "%s: S=%lld too large", fn, (long long)S);
@@ -93,7 +104,7 @@ int attention_fwd(const char* fn, const void* q, const void* k, const void* v, v
                   bool lse_required, int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D, const int32_t* row_ptr,
                   const int32_t* col_idx, int64_t nnz, int32_t block, float sm_scale, void* stream) {
   int64_t lanes = 0;
-  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, 256, &lanes);
+  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, 256, true, &lanes);
   if (rc != TSA_OK) return rc;
   if (lanes == 0 || S == 0) return ok();  // empty problem: nothing to read or write
   if (!q || !k || !v || !out || !row_ptr || (nnz > 0 && !col_idx) || (lse_required && !lse))
@@ -126,7 +137,8 @@ int attention_fwd(const char* fn, const void* q, const void* k, const void* v, v
   const double scale = sm_scale > 0.0f ? (double)sm_scale : 1.0 / std::sqrt((double)D);
   const float scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
   hipError_t e = tsa::launch_attention_fwd(q, k, v, out, lse, dtype == TSA_BF16, lanes, S, (int)D,
-                                           row_ptr, col_idx, nnz, scale_log2, (hipStream_t)stream);
+                                           block, row_ptr, col_idx, nnz, scale_log2,
+                                           (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "attention kernel");
   return ok();
 }
@@ -151,7 +163,7 @@ int64_t tsa_schedule_max_nnz(int64_t nb, int32_t sink, int32_t local_radius, int
 }
 
 size_t tsa_build_schedule_workspace_bytes(int64_t S, int64_t D, int32_t block) {
-  if (S < 0 || D <= 0 || !block_ok(block)) return 0;
+  if (S < 0 || D <= 0 || !build_block_ok(block)) return 0;
   const int64_t nb = (S + block - 1) / block;
   if (nb > TSA_MAX_SCHEDULE_BLOCKS) return 0;
   return tsa::schedule_workspace_bytes(nb, D) + 256;
@@ -185,10 +197,10 @@ int check_build_args(const void* keys, int32_t dtype, int64_t S, int64_t D, int3
     return fail(TSA_ERR_INVALID_ARG,
                 "tsa_build_schedule: sink, local_radius and topk must be >= 0 (%d, %d, %d)", sink,
                 local_radius, topk);
-  if (!block_ok(block))
+  if (!build_block_ok(block))
     return fail(TSA_ERR_UNSUPPORTED,
-                "tsa_build_schedule: block must be a multiple of %d up to %d, got %d", TSA_BLOCK,
-                TSA_MAX_SCHEDULE_BLOCK, block);
+                "tsa_build_schedule: block must be 32 or a multiple of %d up to %d, got %d",
+                TSA_BLOCK, TSA_MAX_SCHEDULE_BLOCK, block);
   const int64_t nb = (S + block - 1) / block;
   if (nb > TSA_MAX_SCHEDULE_BLOCKS)
     return fail(TSA_ERR_UNSUPPORTED, "tsa_build_schedule: %lld blocks exceed the limit of %d",
@@ -493,7 +505,7 @@ int tsa_scheduled_attention_bwd(const void* q, const void* k, const void* v, con
                                 size_t workspace_bytes, void* stream) {
   const char* fn = "tsa_scheduled_attention_bwd";
   int64_t lanes = 0;
-  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, 128, &lanes);
+  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, 128, false, &lanes);
   if (rc != TSA_OK) return rc;
   if (nnz_t < 0) return fail(TSA_ERR_INVALID_ARG, "%s: nnz_t must be >= 0", fn);
   if (lanes == 0 || S == 0) return ok();

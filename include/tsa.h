@@ -61,8 +61,12 @@ extern "C" {
 
 /* Block size of the attention kernels (rows per query block and per key block).
  * The schedule builder and tsa_refine_schedule also take schedules over blocks of
- * any multiple of it up to TSA_MAX_SCHEDULE_BLOCK rows. */
+ * any multiple of it up to TSA_MAX_SCHEDULE_BLOCK rows; the builder and the
+ * forward also take TSA_SUB_BLOCK. */
 #define TSA_BLOCK 64
+/* The smaller block the forward entry points and the schedule builder also take
+ * (head dims 32, 64 and 128): rows per query block and per key block. */
+#define TSA_SUB_BLOCK 32
 #define TSA_MAX_SCHEDULE_BLOCK 4096
 /* Largest number of key blocks the schedule builder accepts (S <= 262144 at block 64). */
 #define TSA_MAX_SCHEDULE_BLOCKS 4096
@@ -96,10 +100,12 @@ size_t tsa_build_schedule_workspace_bytes(int64_t S, int64_t D, int32_t block);
  *
  *   keys        device, [S, D] of `dtype` (TSA_F16 / TSA_BF16), row-major.
  *               For [B, H, S, D] inputs pass lane (0, 0).
- *   block       rows per block: a multiple of 64 up to TSA_MAX_SCHEDULE_BLOCK.
- *               nb = ceil(S / block); a partial last block's centroid is the mean
- *               of its valid rows.  A schedule over blocks larger than 64 is
- *               handed to the attention entry points through tsa_refine_schedule.
+ *   block       rows per block: TSA_SUB_BLOCK (32) or a multiple of 64 up to
+ *               TSA_MAX_SCHEDULE_BLOCK.  nb = ceil(S / block); a partial last
+ *               block's centroid is the mean of its valid rows.  A schedule over
+ *               blocks larger than 64 is handed to the attention entry points
+ *               through tsa_refine_schedule; one over 32-row blocks goes to the
+ *               forward entry points as it is (block = 32 there).
  *   sink, local_radius, topk   >= 0.  Row i lists every block j <= i with
  *               j < sink, or j >= i - local_radius, or j among the topk blocks
  *               of highest salience (ties: lower index; topk >= nb: all).
@@ -266,13 +272,16 @@ int tsa_segment_schedule(int64_t nb, int32_t segment_blocks, int32_t* row_ptr, i
  *                 [S, D] inputs are B = H = 1.  out must not overlap q, k, v; all four
  *                 must be 16-byte aligned.
  *   D             32, 64, 128 or 256.
- *   row_ptr, col_idx  device int32 CSR with nb = ceil(S/64) rows; `nnz` is the
- *                 number of readable col_idx entries.  Row i must list key
+ *   row_ptr, col_idx  device int32 CSR with nb = ceil(S/block) rows; `nnz` is
+ *                 the number of readable col_idx entries.  Row i must list key
  *                 blocks strictly ascending within 0..i.  For memory safety the
  *                 kernel clamps row bounds to [0, nnz] and skips entries that
  *                 are negative, greater than i, or not greater than the
  *                 previous accepted entry.
- *   block         must be 64.
+ *   block         rows per query block and per key block: TSA_BLOCK (64), or
+ *                 TSA_SUB_BLOCK (32) at D 32, 64 or 128 with S <= 65535 * 128
+ *                 (TSA_ERR_UNSUPPORTED otherwise).  The row_ptr array must hold
+ *                 nb + 1 entries for this block size; the library cannot check it.
  *   sm_scale      softmax scale; <= 0 selects 1/sqrt(D).
  * For query row t in block i the output is the softmax-weighted mean of v over
  * keys u <= t whose block is listed in row i; a row with no such key is 0.

@@ -128,7 +128,8 @@ def test_workspace_bytes(lib):
     # centroids always; the distance matrix only when it does not stay in LDS (nb > 128)
     assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 64) >= 64 * 64 * 8
     assert lib.tsa_build_schedule_workspace_bytes(64 * 200, 64, 64) >= 200 * 64 * 8 + 200 * 200 * 8
-    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 32) == 0
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 32) >= 128 * 64 * 8  # 32-row blocks
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 16) == 0
     assert lib.tsa_build_schedule_workspace_bytes(64 * 5000, 64, 64) == 0
 
 
@@ -146,7 +147,14 @@ def _fwd(lib, **kw):
 def test_attention_argument_checks_before_gpu(lib):
     assert _fwd(lib, dtype=5) == -1
     assert _fwd(lib, B=-1) == -1
-    assert _fwd(lib, block=32) == -2
+    assert _fwd(lib, block=32) == -1  # 32-row blocks at D 64: the NULL pointers are what fail
+    for d in (32, 128):
+        assert _fwd(lib, block=32, D=d) == -1
+    assert _fwd(lib, block=32, D=256) == -2  # 32-row blocks stop at head dim 128
+    assert b"32-row blocks" in lib.tsa_last_error()
+    assert _fwd(lib, block=32, S=65535 * 128 + 1) == -2  # past the grid's pair count
+    assert _fwd(lib, block=16) == -2
+    assert _fwd(lib, block=128) == -2
     assert _fwd(lib, D=96) == -2
     assert b"32, 64, 128 or 256" in lib.tsa_last_error()
     assert _fwd(lib, D=512) == -2
@@ -257,6 +265,7 @@ def test_backward_workspace_and_checks_before_gpu(lib):
     assert _bwd(lib, D=256) == -2  # the backward takes 32, 64 and 128
     assert _bwd(lib, D=32) == -1
     assert _bwd(lib, block=128) == -2
+    assert _bwd(lib, block=32) == -2  # the backward walks 64-row blocks only
     assert _bwd(lib, nnz_t=-1) == -1
     assert _bwd(lib, scale=float("inf")) == -1
     assert _bwd(lib) == -1 and b"NULL" in lib.tsa_last_error()
@@ -283,6 +292,13 @@ def test_block_sizes_accepted_by_builder_and_refinement(lib):
     assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 4096) > 0
     assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 96) == 0
     assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 8192) == 0
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 32) > 0
+    assert lib.tsa_build_schedule_workspace_bytes(4096, 64, 48) == 0
+    # block 32 is valid: the NULL row_ptr is what fails
+    assert lib.tsa_build_schedule(vp(None), 0, 4096, 64, 32, 1, 1, 2, vp(None), vp(None), 1000, vp(None),
+                                  vp(None), 1 << 20, None, vp(None)) == -1
+    # the refinement keeps to multiples of 64
+    assert lib.tsa_refine_schedule_max_nnz(4096, 32, 10) == -1
     # block 96 is not a multiple of 64: unsupported before any GPU call
     assert lib.tsa_build_schedule(vp(None), 0, 4096, 64, 96, 1, 1, 2, vp(None), vp(None), 1000, vp(None),
                                   vp(None), 1 << 20, None, vp(None)) == -2

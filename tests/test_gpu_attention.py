@@ -158,8 +158,14 @@ def test_validation_errors(tsa):
     q96 = torch.zeros(128, 96, dtype=torch.float16, device="cuda:0")
     with pytest.raises(ValueError, match="UNSUPPORTED"):
         tsa.scheduled_attention(q96, q96, q96, rp, ci)
-    with pytest.raises(ValueError, match="UNSUPPORTED"):
+    with pytest.raises(ValueError, match="UNSUPPORTED"):  # one 128-row block: a valid CSR length
+        tsa.scheduled_attention(q, q, q, rp[:2].contiguous(), ci, block=128)
+    with pytest.raises(ValueError, match="nb\\+1"):  # 32-row blocks: a 64-row CSR has too few rows
         tsa.scheduled_attention(q, q, q, rp, ci, block=32)
+    q256 = torch.zeros(128, 256, dtype=torch.float16, device="cuda:0")
+    rp4, ci4 = _csr_dev(*oracle.dense_causal_schedule(4))
+    with pytest.raises(ValueError, match="UNSUPPORTED"):  # 32-row blocks stop at head dim 128
+        tsa.scheduled_attention(q256, q256, q256, rp4, ci4, block=32)
 
 
 def test_host_pointer_is_rejected_by_the_abi(tsa):
