@@ -56,49 +56,75 @@ using namespace tile;
 constexpr int kDuoThreads = 256;  // 2 query blocks x 2 query halves
 constexpr int kDuoRows = 2;
 
-// Cursor over the accepted entries of one CSR row (wave-uniform state, plus one
-// per-lane register holding a window of 64 column indices).  An entry is
-// accepted when it lies in 0..i and exceeds the previous accepted entry: the
-// rule of the one-block kernel.
+// Inclusive prefix maximum across the wave's 64 lanes (lane l: the maximum over
+// lanes 0..l): shifts by 1, 2, 4 and 8 lanes within each row of 16, then the
+// last lane of rows 0 and 2 into rows 1 and 3, and lane 31 into rows 2 and 3.
+// Lanes a step does not write take INT_MIN, which leaves the maximum unchanged.
+__device__ __forceinline__ int wave_prefix_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(INT_MIN, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
+}
+
+// Cursor over the accepted entries of one CSR row.  An entry is accepted when it
+// lies in 0..i and exceeds the previous accepted entry (the rule of the
+// one-block kernel); equivalently, when it lies in 0..i and exceeds every
+// earlier entry of the row that does, which a wave evaluates for a window of
+// 64 entries at once with one prefix maximum.  The accepted lanes of the
+// window form a wave-uniform bit mask, and taking the next entry is a
+// find-first-set and one lane read.
 struct DuoCursor {
-  int i;      // query block, or -1 when the pair's second block is past the end
-  int p, end; // next entry, end of the row (clamped to the readable entries)
-  int win;    // first entry held in `cols`
-  int cols;   // lane l: entry win + l (or -1)
-  int last;   // last accepted block
-  int head;   // next accepted block (INT_MAX: none left)
+  int i;         // CSR row, or -1 when it lies past the last row
+  int p, end;    // start of the next window, end of the row (clamped to the readable entries)
+  int cols;      // lane l: entry l of the current window (or -1)
+  uint64_t acc;  // accepted lanes of the current window not yet taken
+  int last;      // largest accepted entry so far (-1: none)
+  int head;      // next accepted entry (INT_MAX: none left)
+  // Issues the load of the first window; scan() reads it once it has arrived.
   __device__ __forceinline__ void start(const int32_t* __restrict__ row_ptr,
                                         const int32_t* __restrict__ col_idx, int64_t nnz, int row,
-                                        int nb, int l) {
-    i = row < nb ? row : -1;
+                                        int nrows, int l) {
+    i = row < nrows ? row : -1;
     if (i >= 0) {
       p = (int)min((int64_t)max(row_ptr[i], 0), nnz);
       end = (int)max(min((int64_t)row_ptr[i + 1], nnz), (int64_t)p);
     } else {
       p = end = 0;
     }
-    win = p;
     cols = (p + l < end) ? col_idx[p + l] : -1;
+    acc = 0;
     last = -1;
     head = INT_MAX;
+  }
+  // Accepted lanes of the window loaded at p.  Entries are ranked by (value,
+  // earlier lane first), so that a repeated value is never a new maximum; the
+  // key fits 32 bits since rows are below 2^18 (the grid's pair limit).
+  __device__ __forceinline__ void scan(int l) {
+    const int x = (cols >= 0 && cols <= i) ? cols : -1;
+    const int key = x * 64 + (63 - l);
+    const int run = wave_prefix_max(key);
+    acc = __builtin_amdgcn_ballot_w64(x > last && key == run);
+    last = max(last, __builtin_amdgcn_readlane(run, 63) >> 6);  // -1 when nothing is valid
+    p += 64;
   }
   // Moves `head` to the next accepted entry.  A window reload waits for every
   // outstanding vector load of the wave (only rows of more than 64 entries).
   __device__ __forceinline__ void advance(const int32_t* __restrict__ col_idx, int l) {
-    while (p < end) {
-      if (p - win >= 64) {
-        win = p;
-        cols = (p + l < end) ? col_idx[p + l] : -1;
-        __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-      }
-      const int c = __builtin_amdgcn_readlane(cols, p - win);
-      ++p;
-      if (c > last && c <= i) {
-        head = c;
+    while (acc == 0) {
+      if (p >= end) {
+        head = INT_MAX;
         return;
       }
+      cols = (p + l < end) ? col_idx[p + l] : -1;
+      __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
+      scan(l);
     }
-    head = INT_MAX;
+    head = __builtin_amdgcn_readlane(cols, (int)__builtin_ctzll(acc));
+    acc &= acc - 1;
   }
 };
 
@@ -172,32 +198,34 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(kStepsD));  // the windows (older than the Q loads)
 #pragma unroll
-  for (int r = 0; r < kCursors; ++r) rows[r].advance(col_idx, l);
+  for (int r = 0; r < kCursors; ++r) {
+    rows[r].scan(l);
+    rows[r].advance(col_idx, l);
+  }
 
   // Next 64-key block of the union of the rows (-1: none); `mine` gets bit h
   // set when this wave computes key half h of it: both halves when its 64-row
   // block's row lists the block, or (SUB) the halves its 32-row row lists.
   auto next_block = [&](int& mine) -> int {
-    int j = INT_MAX;
+    int hmin = INT_MAX;
 #pragma unroll
-    for (int r = 0; r < kCursors; ++r) j = min(j, SUB ? (rows[r].head == INT_MAX ? INT_MAX : rows[r].head >> 1) : rows[r].head);
+    for (int r = 0; r < kCursors; ++r) hmin = min(hmin, rows[r].head);
     mine = 0;
-    if (j == INT_MAX) return -1;
+    if (hmin == INT_MAX) return -1;
+    const int j = SUB ? hmin >> 1 : hmin;  // (INT_MAX >> 1 is no block index)
 #pragma unroll
     for (int r = 0; r < kCursors; ++r) {
       if constexpr (SUB) {
         // at most the two 32-key blocks of j, in ascending order
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-          if (rows[r].head != INT_MAX && (rows[r].head >> 1) == j) {
+          if ((rows[r].head >> 1) == j) {
             if (r == w) mine |= 1 << (rows[r].head & 1);
-            rows[r].last = rows[r].head;
             rows[r].advance(col_idx, l);
           }
       } else {
         if (rows[r].head == j) {
           if (r == rsel) mine = 3;
-          rows[r].last = j;
           rows[r].advance(col_idx, l);
         }
       }

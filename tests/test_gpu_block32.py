@@ -10,7 +10,8 @@ walks its own CSR row, and the 64-key tiles it copies are the union of the
   bit-exact, salience to a relative 1e-12 (ragged S, the LDS and the larger
   path, both top-k scopes);
 * every output element and lse against the fp64 oracle at block 32: topology,
-  dense, random, irregular (entries the kernel must skip) and empty schedules,
+  dense, random, irregular (entries the kernel must skip, also in rows of up
+  to 200 entries and in rows out of order) and empty schedules,
   lane counts with and without a factor of 8, ragged S, one- and two-row
   sequences, fp16 and bf16, head dims 32, 64 and 128, a large softmax scale;
 * at the batched workload's full size ([4, 16, 4096, 64] bf16, the schedule
@@ -48,15 +49,38 @@ def _dev(x):
     return torch.as_tensor(np.asarray(x)).to(DEV)
 
 
-def _irregular_csr(nb, seed):
+def _irregular_csr(nb, seed, max_len=12, shuffle=False):
     """Ascending rows with entries the kernel must skip: negative entries,
-    repeats, future blocks and blocks past the end."""
+    repeats, future blocks and blocks past the end.  With ``shuffle`` the rows
+    are in random order, so that earlier larger entries hide later ones."""
     rng = np.random.default_rng(seed)
-    rows = [np.sort(rng.integers(-2, nb + 3, int(rng.integers(0, 12)))) for _ in range(nb)]
+    rows = []
+    for _ in range(nb):
+        r = np.sort(rng.integers(-2, nb + 3, int(rng.integers(0, max_len))))
+        rows.append(rng.permutation(r) if shuffle else r)
     rp = np.zeros(nb + 1, np.int32)
     rp[1:] = np.cumsum([len(r) for r in rows])
     ci = np.concatenate(rows).astype(np.int32) if rows else np.zeros(0, np.int32)
     return rp, ci
+
+
+def _accepted_csr(rp, ci):
+    """The entries the kernel takes from each row (the rule in include/tsa.h):
+    within 0..i and above every earlier entry of the row that lies in 0..i.
+    For rows in ascending order these are the row's entries in 0..i; the oracle
+    gets this CSR for rows that are not in order."""
+    rows, nnz = [], len(ci)
+    for i in range(len(rp) - 1):
+        lo = min(max(int(rp[i]), 0), nnz)
+        hi = max(min(int(rp[i + 1]), nnz), lo)
+        best, keep = -1, []
+        for c in ci[lo:hi]:
+            if 0 <= int(c) <= i and int(c) > best:
+                keep.append(int(c))
+                best = int(c)
+        rows.append(keep)
+    out_rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    return out_rp, np.array([c for r in rows for c in r], np.int32)
 
 
 def _schedule(kind, k, nb, seed):
@@ -69,6 +93,10 @@ def _schedule(kind, k, nb, seed):
         return workloads.random_csr(nb, seed=seed, density=0.35, allow_empty=True)
     if kind == "irregular":
         return _irregular_csr(nb, seed)
+    if kind == "irregular_long":  # rows of up to 200 entries: several 64-entry windows
+        return _irregular_csr(nb, seed, max_len=200)
+    if kind == "unordered_long":
+        return _irregular_csr(nb, seed, max_len=200, shuffle=True)
     if kind == "empty":
         return np.zeros(nb + 1, np.int32), np.zeros(0, np.int32)
     raise ValueError(kind)
@@ -114,6 +142,9 @@ CASES = [
     (2, 8, 512, 64, "bf16", "topology", 30.0, 0.5),    # nearly one-hot rows
     (2, 4, 200, 64, "fp16", "empty", None, 1.0),
     (8, 16, 1088, 64, "fp16", "random", None, 1.0),    # 128 lanes, 34 rows per lane
+    (1, 4, 2500, 64, "fp16", "dense", None, 1.0),      # rows of up to 79 entries
+    (2, 2, 3000, 128, "bf16", "irregular_long", None, 1.0),
+    (1, 8, 3000, 32, "fp16", "unordered_long", None, 1.0),
 ]
 
 
@@ -132,6 +163,8 @@ def test_forward_at_32_row_blocks_every_output(tsa, case):
     out, lse = tsa.scheduled_attention(qd, kd, vd, _dev(rp), _dev(ci), block=32, out=out,
                                        return_lse=True, **kwargs)
     torch.cuda.synchronize()
+    if kind.startswith("unordered"):
+        rp, ci = _accepted_csr(rp, ci)
     want = oracle.masked_attention(q, k, v, rp, ci, 32, scale=scale)
     want_lse = oracle.masked_lse(q, k, rp, ci, 32, scale=scale)
     got = out.double().cpu().numpy()

@@ -7,7 +7,8 @@ both key halves of the blocks its own row lists.  These cases are sized to
 take that kernel (at least 2048 (lane, query block) pairs), with 17 query
 blocks, so that the last pair has one block past the end, and they cover both
 lane orders (lane counts with and without a factor of 8), both input types,
-topology, dense, random and irregular CSR rows, empty rows, a large softmax
+topology, dense, random and irregular CSR rows (also rows of up to 200
+entries out of order), empty rows, a large softmax
 scale, the lse output and the backward that consumes it, whose dq kernel takes
 the same two-block form at these sizes (D 32, 64 and 128).  Every output element
 is compared with the fp64 oracle; output buffers are filled with NaN first,
@@ -43,20 +44,40 @@ def _csr(rp, ci):
             torch.from_numpy(np.asarray(ci, np.int32)).to(DEV))
 
 
-def _irregular_csr(nb, seed):
+def _irregular_csr(nb, seed, max_len=9, shuffle=False):
     """Ascending rows with entries the kernels must skip: negative entries,
     repeats, future blocks and blocks past the end (a row is read front to
     back, and an entry is taken only when it lies in 0..i and exceeds the last
-    one taken; the oracle ignores the same entries)."""
+    one taken; the oracle ignores the same entries).  With ``shuffle`` the rows
+    are in random order."""
     rng = np.random.default_rng(seed)
     rows = []
     for i in range(nb):
-        n = int(rng.integers(0, 9))
-        rows.append(np.sort(rng.integers(-2, nb + 3, n)))
+        n = int(rng.integers(0, max_len))
+        r = np.sort(rng.integers(-2, nb + 3, n))
+        rows.append(rng.permutation(r) if shuffle else r)
     rp = np.zeros(nb + 1, np.int32)
     rp[1:] = np.cumsum([len(r) for r in rows])
     ci = np.concatenate(rows).astype(np.int32) if rows else np.zeros(0, np.int32)
     return rp, ci
+
+
+def _accepted_csr(rp, ci):
+    """The entries the kernels take from each row (the rule in include/tsa.h):
+    within 0..i and above every earlier entry of the row that lies in 0..i.
+    The oracle gets this CSR for rows that are not in order."""
+    rows, nnz = [], len(ci)
+    for i in range(len(rp) - 1):
+        lo = min(max(int(rp[i]), 0), nnz)
+        hi = max(min(int(rp[i + 1]), nnz), lo)
+        best, keep = -1, []
+        for c in ci[lo:hi]:
+            if 0 <= int(c) <= i and int(c) > best:
+                keep.append(int(c))
+                best = int(c)
+        rows.append(keep)
+    out_rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    return out_rp, np.array([c for r in rows for c in r], np.int32)
 
 
 def _schedule(kind, k, nb, seed):
@@ -69,6 +90,8 @@ def _schedule(kind, k, nb, seed):
         return workloads.random_csr(nb, seed=seed, density=0.35, allow_empty=True)
     if kind == "irregular":
         return _irregular_csr(nb, seed)
+    if kind == "unordered_long":  # rows of up to 200 entries in random order: several windows
+        return _irregular_csr(nb, seed, max_len=200, shuffle=True)
     if kind == "empty":
         return np.zeros(nb + 1, np.int32), np.zeros(0, np.int32)
     raise ValueError(kind)
@@ -85,6 +108,7 @@ CASES = [
     # alone would exceed the absolute bar.
     (8, 17, "bf16", "topology", 30.0),
     (4, 32, "fp16", "empty", None),
+    (2, 64, "fp16", "unordered_long", None),
 ]
 
 
@@ -105,6 +129,8 @@ def test_two_block_workgroups_every_output(tsa, case):
     kwargs = {} if scale is None else {"sm_scale": scale}
     out, lse = tsa.scheduled_attention(qd, kd, vd, rpd, cid, out=out, return_lse=True, **kwargs)
     torch.cuda.synchronize()
+    if kind.startswith("unordered"):
+        rp, ci = _accepted_csr(rp, ci)
     want = oracle.masked_attention(q, k, v, rp, ci, 64, scale=scale)
     want_lse = oracle.masked_lse(q, k, rp, ci, 64, scale=scale)
     got = out.double().cpu().numpy()
