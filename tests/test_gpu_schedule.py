@@ -112,8 +112,9 @@ def test_dense_schedule(tsa, nb):
 
 def test_builder_validation(tsa):
     keys = torch.zeros(128, 64, dtype=torch.float16, device="cuda:0")
-    with pytest.raises(ValueError, match="UNSUPPORTED"):
-        tsa.build_schedule(keys, 32, 1, 1, 2)
+    for bad_block in (16, 48, 96):  # 32 and multiples of 64 are the accepted sizes
+        with pytest.raises(ValueError, match="UNSUPPORTED"):
+            tsa.build_schedule(keys, bad_block, 1, 1, 2)
     with pytest.raises(ValueError, match="INVALID_ARG"):
         tsa.build_schedule(keys, 64, -1, 1, 2)
     with pytest.raises(TypeError):
