@@ -23,7 +23,10 @@
 //
 //   Grid: x = lane (remapped so that each of the 8 XCDs holds a contiguous range
 //   of lanes when the lane count is a multiple of 8; workgroup x + y * lanes
-//   runs on XCD x % 8), y = pair position, last pairs (longest rows) first.
+//   runs on XCD x % 8), y = pair position, last pairs (longest rows) first.  At
+//   head dim 128 each XCD runs its lanes two at a time instead (all pair
+//   positions of a lane pair, longest first), which keeps the K/V blocks its
+//   workgroups share within its L2.
 //
 // Schedules over 32-row blocks (SUB): the same workgroup serves the four
 //   32-row query blocks 4g .. 4g+3, which are its waves' query halves, and
@@ -154,6 +157,11 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   constexpr bool kMfmaSums = D <= 64;
   // CSR rows a workgroup walks: the two 64-row blocks, or the four 32-row ones.
   constexpr int kCursors = SUB ? 4 : kDuoRows;
+  // Lanes an XCD works on at a time at head dim 128 (0: all of its range, the
+  // pair positions running across them).  Measured at [2,32,8192,128] over the
+  // dense causal CSR: 1081 -> 1046 us with 2, 1056 with 4, 1075 with 1; at head
+  // dim 64 every grouping was slower (57.0 -> 62.4 us at [4,16,4096,64]).
+  constexpr uint32_t kLaneGroup = D == 128 ? 2u : 0u;
   static_assert((kTileBytes / 1024) % kWaves == 0 && kFillOps % 2 == 0, "fill ops split K | V");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
@@ -167,15 +175,28 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
   const int g = l >> 4;
   const int gi = l & 15;
 
-  // Lane and pair position (see the header comment): no division.
+  // Lane and pair position (see the header comment).
   const uint32_t X = gridDim.x, x = blockIdx.x;
-  int64_t lane;
-  if (X % 8u == 0u)
-    lane = lane_base + (int64_t)((x % 8u) * (X / 8u) + x / 8u);
-  else
-    lane = lane_base + (int64_t)x;
   const int npairs = (int)gridDim.y;
-  const int pair = npairs - 1 - (int)blockIdx.y;
+  int64_t lane;
+  int pair;
+  if (kLaneGroup > 0 && X % (8u * kLaneGroup) == 0u) {
+    // Head dim 128: XCD k (= workgroup id % 8) takes its lanes kLaneGroup at a
+    // time, each group's pair positions longest first, so that the K/V blocks
+    // its workgroups share fit its L2 (4 MB of K/V per lane of 8192 keys).
+    const uint32_t id = x + (uint32_t)blockIdx.y * X;
+    const uint32_t xcd = id % 8u, seq = id / 8u;
+    const uint32_t per_group = kLaneGroup * (uint32_t)npairs;
+    const uint32_t grp = seq / per_group, rem = seq % per_group;
+    lane = lane_base + (int64_t)(xcd * (X / 8u) + grp * kLaneGroup + rem % kLaneGroup);
+    pair = npairs - 1 - (int)(rem / kLaneGroup);
+  } else if (X % 8u == 0u) {
+    lane = lane_base + (int64_t)((x % 8u) * (X / 8u) + x / 8u);
+    pair = npairs - 1 - (int)blockIdx.y;
+  } else {
+    lane = lane_base + (int64_t)x;
+    pair = npairs - 1 - (int)blockIdx.y;
+  }
   const int my_i = kDuoRows * pair + rsel;  // this wave's 64-row block (past the end: no rows)
   const int my_q32 = 4 * pair + w;         // and its 32-row query block
 
