@@ -12,7 +12,9 @@ at 32:
 * a 64-row CSR and its 32-row expansion (row 2I + a lists 2J + b for every J
   of row I, b = 0, 1, kept within the row's causal range) allow the same keys,
   so the outputs agree;
-* the 64-row centroids are the means of the two 32-row centroids they cover.
+* the 64-row centroids are the means of the two 32-row centroids they cover;
+* the gradients over a 32-row CSR = torch's autograd through that routine under
+  the explicit mask, and those of a 64-row CSR = those of its 32-row expansion.
 """
 import numpy as np
 import pytest
@@ -114,3 +116,35 @@ def test_64_row_centroids_are_means_of_32_row_ones(S):
         parts = [2 * J, 2 * J + 1][: c32.shape[0] - 2 * J]
         w = rows32[parts]
         np.testing.assert_allclose(c64[J], (c32[parts] * w[:, None]).sum(0) / w.sum(), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_gradients_at_32_row_blocks_equal_masked_sdpa_autograd(seed):
+    """dq, dk and dv over a 32-row CSR equal torch's autograd through its own
+    scaled-dot-product attention under the explicit 32-row mask (float64 on the
+    CPU; ragged S, two lanes; every row lists at least one block)."""
+    S, D = 32 * 5 + 11, 16
+    rng = np.random.default_rng(70 + seed)
+    q, k, v, do = (rng.standard_normal((1, 2, S, D)) for _ in range(4))
+    nb = -(-S // 32)
+    rp, ci = workloads.random_csr(nb, seed=seed + 7, density=0.4)
+    dq, dk, dv, out, _ = oracle.attention_backward(q, k, v, do, rp, ci, block=32)
+    mask = torch.from_numpy(_kron_mask(rp, ci, S, 32))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    to.backward(torch.tensor(do))
+    np.testing.assert_allclose(out, to.detach().numpy(), rtol=1e-12, atol=1e-12)
+    for got, want in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("S", [256, 300])
+def test_gradients_of_64_row_csr_and_its_32_row_expansion_agree(S):
+    q, k, v, do = _qkv((S, 32), seed=S + 3) + [np.random.default_rng(S).standard_normal((S, 32))]
+    nb = -(-S // 64)
+    rp, ci = workloads.random_csr(nb, seed=S + 1, density=0.5)
+    rp32, ci32 = _expand_to_32(rp, ci, S)
+    a = oracle.attention_backward(q, k, v, do, rp, ci, block=64)[:3]
+    b = oracle.attention_backward(q, k, v, do, rp32, ci32, block=32)[:3]
+    for x, y in zip(a, b):
+        assert np.max(np.abs(x - y)) < 1e-12
