@@ -457,8 +457,9 @@ def scheduled_attention_backward(q, k, v, out, dout, lse, row_ptr, col_idx, col_
                                  block: int = BLOCK, sm_scale: float | None = None):
     """Gradients (dq, dk, dv) of ``scheduled_attention`` for the upstream gradient
     ``dout``; ``out`` and ``lse`` are the forward's (``return_lse=True``) and
-    (col_ptr, row_idx) is ``schedule_transpose(row_ptr, col_idx)``.  Returns
-    tensors of q's shape and dtype."""
+    (col_ptr, row_idx) is ``schedule_transpose(row_ptr, col_idx)``.  The schedule
+    is over blocks of ``block`` rows: 64, or SUB_BLOCK (32) at head dims up to
+    128.  Returns tensors of q's shape and dtype."""
     code, B, H, S, D = _attention_shape(q, k, v)
     for name, t in (("out", out), ("dout", dout)):
         if not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype != q.dtype:
@@ -471,7 +472,8 @@ def scheduled_attention_backward(q, k, v, out, dout, lse, row_ptr, col_idx, col_
         raise ValueError("lse must be contiguous on q's device")
     for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx), ("col_ptr", col_ptr), ("row_idx", row_idx)):
         _check_index(name, t, q.device)
-    nb = -(-S // BLOCK)
+    _check_block(block)
+    nb = -(-S // block)
     if row_ptr.numel() != nb + 1 or col_ptr.numel() != nb + 1:
         raise ValueError(f"row_ptr and col_ptr must have nb+1 = {nb + 1} entries for S={S}")
     scale = _scale_arg(sm_scale)
@@ -491,25 +493,28 @@ def scheduled_attention_backward(q, k, v, out, dout, lse, row_ptr, col_idx, col_
 
 class _ScheduledAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, row_ptr, col_idx, col_ptr, row_idx, sm_scale):
-        out, lse = scheduled_attention(q, k, v, row_ptr, col_idx, sm_scale=sm_scale, return_lse=True)
+    def forward(ctx, q, k, v, row_ptr, col_idx, col_ptr, row_idx, sm_scale, block):
+        out, lse = scheduled_attention(q, k, v, row_ptr, col_idx, block=block, sm_scale=sm_scale,
+                                       return_lse=True)
         ctx.save_for_backward(q, k, v, out, lse, row_ptr, col_idx, col_ptr, row_idx)
         ctx.sm_scale = sm_scale
+        ctx.block = block
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, out, lse, row_ptr, col_idx, col_ptr, row_idx = ctx.saved_tensors
         dq, dk, dv = scheduled_attention_backward(q, k, v, out, dout.contiguous(), lse, row_ptr, col_idx,
-                                                  col_ptr, row_idx, sm_scale=ctx.sm_scale)
-        return dq, dk, dv, None, None, None, None, None
+                                                  col_ptr, row_idx, block=ctx.block, sm_scale=ctx.sm_scale)
+        return dq, dk, dv, None, None, None, None, None, None
 
 
-def attention(q, k, v, row_ptr, col_idx, col_ptr=None, row_idx=None, sm_scale: float | None = None):
+def attention(q, k, v, row_ptr, col_idx, col_ptr=None, row_idx=None, sm_scale: float | None = None,
+              block: int = BLOCK):
     """Scheduled attention that torch autograd can differentiate: the forward
     keeps lse, the backward runs ``scheduled_attention_backward``.  Pass the
     schedule's column view (``schedule_transpose``) to reuse it across calls;
-    otherwise it is built here."""
+    otherwise it is built here.  ``block``: the schedule's block rows (64, or 32)."""
     if col_ptr is None or row_idx is None:
         col_ptr, row_idx = schedule_transpose(row_ptr, col_idx)
-    return _ScheduledAttention.apply(q, k, v, row_ptr, col_idx, col_ptr, row_idx, sm_scale)
+    return _ScheduledAttention.apply(q, k, v, row_ptr, col_idx, col_ptr, row_idx, sm_scale, block)

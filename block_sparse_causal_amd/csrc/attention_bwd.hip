@@ -154,6 +154,15 @@ struct ListWalker {
     }
     return -1;
   }
+  // A walker with no entries.
+  __device__ __forceinline__ void clear(const int32_t* idx, int l) {
+    p = end = win = 0;
+    cols = -1;
+    lo = 0;
+    hi = -1;
+    idx_ = idx;
+    l_ = l;
+  }
   const int32_t* idx_;
   int l_;
 };
@@ -381,13 +390,13 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
 // each union block's K and V tiles are copied once and serve both rows, which
 // share most of their blocks.  Used for launches with enough (lane, query
 // block) pairs that the halved grid still fills the CUs.
-template <int D, bool BF16>
+template <int D, bool BF16, bool SUB>
 __global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int64_t nnz, int S,
-    int nb, int npairs, int64_t lane_base, float scale_log2, float scale, float2* __restrict__ stats,
-    uint16_t* __restrict__ dq) {
+    int nb, int nrows, int npairs, int64_t lane_base, float scale_log2, float scale,
+    float2* __restrict__ stats, uint16_t* __restrict__ dq) {
   using E = Elem<BF16>;
   using G = Geo<D>;
   constexpr int kStepsD = G::kStepsD, kTilesD = G::kTilesD, kTileBytes = G::kTileBytes;
@@ -406,6 +415,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
   grid_position(npairs, lane_base, lane, pos);
   const int pair = npairs - 1 - pos;  // longest rows first
   const int my_i = 2 * pair + rsel;   // >= nb: this wave's block is past the end
+  const int my_q32 = 4 * pair + w;    // and its 32-row query block (2 my_i + qh)
   const int64_t lane_off = lane * (int64_t)S * D;
   const uint16_t* kg = k + lane_off;
   const uint16_t* vg = v + lane_off;
@@ -428,23 +438,18 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
   float lse2 = lse[lane * (int64_t)S + qrow_c] * kLog2e;
   if (qrow < S) stats[lane * (int64_t)S + qrow] = float2{lse2, delta};
 
-  // Both rows' walkers: the union of the rows in ascending order.
-  ListWalker walk[2];
-  int head[2], last[2];
+  // The rows' walkers (the two 64-row blocks, or with SUB the four 32-row
+  // ones, wave w's being walker w): the union of the rows in ascending order.
+  constexpr int kWalk = SUB ? 4 : 2;
+  ListWalker walk[kWalk];
+  int head[kWalk];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int row = 2 * pair + r;
-    if (row < nb) {
+  for (int r = 0; r < kWalk; ++r) {
+    const int row = kWalk * pair + r;
+    if (row < nrows)
       walk[r].init(row_ptr, col_idx, nnz, row, 0, row, l);
-    } else {
-      walk[r].p = walk[r].end = walk[r].win = 0;
-      walk[r].cols = -1;
-      walk[r].lo = 0;
-      walk[r].hi = -1;
-      walk[r].idx_ = col_idx;
-      walk[r].l_ = l;
-    }
-    last[r] = -1;
+    else
+      walk[r].clear(col_idx, l);
   }
   // Every load above has landed before any copy is queued, so the ring's waits
   // below count copies only.
@@ -456,22 +461,32 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
   }
   asm volatile("" : "+v"(lse2), "+v"(delta));
 #pragma unroll
-  for (int r = 0; r < 2; ++r) head[r] = walk[r].next(-1);
-  // Next block of the union (-1: none); `mine` tells whether this wave's row lists it.
-  auto next_block = [&](bool& mine) -> int {
-    int j = -1;
+  for (int r = 0; r < kWalk; ++r) head[r] = walk[r].next(-1);
+  // Next 64-key block of the union (-1: none); `mine` gets bit h set when this
+  // wave computes key half h of it: both when its 64-row block's row lists the
+  // block, or (SUB) the halves its 32-row row lists.
+  auto next_block = [&](int& mine) -> int {
+    int hmin = INT_MAX;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      if (head[r] >= 0 && (j < 0 || head[r] < j)) j = head[r];
-    mine = false;
-    if (j < 0) return -1;
+    for (int r = 0; r < kWalk; ++r)
+      if (head[r] >= 0) hmin = min(hmin, head[r]);
+    mine = 0;
+    if (hmin == INT_MAX) return -1;
+    const int j = SUB ? hmin >> 1 : hmin;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      if (head[r] == j) {
-        if (r == rsel) mine = true;
-        last[r] = j;
+    for (int r = 0; r < kWalk; ++r) {
+      if constexpr (SUB) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)  // at most the two 32-key blocks of j, ascending
+          if (head[r] >= 0 && (head[r] >> 1) == j) {
+            if (r == w) mine |= 1 << (head[r] & 1);
+            head[r] = walk[r].next(head[r]);
+          }
+      } else if (head[r] == j) {
+        if (r == rsel) mine = 3;
         head[r] = walk[r].next(j);
       }
+    }
     return j;
   };
 
@@ -500,7 +515,9 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
   auto compute_half = [&](int j, auto T_c, auto KH_c) {
     constexpr int KH = decltype(KH_c)::value;
     constexpr int kOff = decltype(T_c)::value * kStageBytes + KH * kHalfKeyBytes;
-    if (j == my_i && KH > qh) return;  // keys of this half all after the queries
+    // 32-row key block 2j + KH against this wave's 32-row query block: later
+    // ones are fully masked (the acceptance rule never lists them under SUB).
+    if (2 * j + KH > my_q32) return;
     u32x4 ka[kStepsD], va[kStepsD];
 #pragma unroll
     for (int c = 0; c < kStepsD; ++c) {
@@ -517,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
     u32x2 kt[kTilesD * 4];
 #pragma unroll
     for (int dt = 0; dt < kTilesD; ++dt) tr_reads<kOff, G::kRowBytes>(&kt[dt * 4], t_addr[dt]);
-    if (j == my_i && KH == qh) {
+    if (2 * j + KH == my_q32) {  // key position must not exceed query position
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kpos = 16 * (r >> 3) + 8 * h + (r & 7);
@@ -547,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
   // computed one step earlier, and computes both key halves when its row lists
   // the block.
   int blk[2];
-  bool mine[2] = {false, false};
+  int mine[2] = {0, 0};
   blk[0] = next_block(mine[0]);
   blk[1] = blk[0] >= 0 ? next_block(mine[1]) : -1;
   if (blk[0] >= 0) {
@@ -568,10 +585,8 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
         if (blk[refill] >= 0) fill(blk[refill], ring + refill * kStageBytes);
       }
       pre = false;
-      if (mine[t]) {
-        compute_half(blk[t], T_c, std::integral_constant<int, 0>{});
-        compute_half(blk[t], T_c, std::integral_constant<int, 1>{});
-      }
+      if (mine[t] & 1) compute_half(blk[t], T_c, std::integral_constant<int, 0>{});
+      if (mine[t] & 2) compute_half(blk[t], T_c, std::integral_constant<int, 1>{});
       done = blk[refill] < 0;
     };
     while (!done) {
@@ -882,13 +897,18 @@ __global__ __launch_bounds__(256) void col_order_kernel(const int32_t* __restric
   if (j < nb) order[rank] = j;
 }
 
-template <int D, bool BF16>
+// ncols: the column view's columns (nb, or ceil(S / 32) with SUB).  With SUB
+// the workgroup at position pos takes 32-key columns 4 pos .. 4 pos + 3 (the
+// 64-key blocks 2 pos and 2 pos + 1, no ranking), wave w column 4 pos + w, and
+// walks the union of the 64-row query blocks they touch; a wave takes query
+// half 2I + h of 64-row block I only when its column lists that 32-row block.
+template <int D, bool BF16, bool SUB>
 __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float2* __restrict__ stats,
     const int32_t* __restrict__ col_ptr, const int32_t* __restrict__ row_idx, int64_t nnz_t,
-    const int32_t* __restrict__ order, int S, int nb, int npairs, int64_t lane_base, float scale_log2,
-    float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+    const int32_t* __restrict__ order, int S, int nb, int ncols, int npairs, int64_t lane_base,
+    float scale_log2, float scale, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   using E = Elem<BF16>;
   using G = Geo<D>;
   constexpr int kStepsD = G::kStepsD, kTilesD = G::kTilesD, kTileBytes = G::kTileBytes;
@@ -913,7 +933,9 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
   int pos;
   grid_position(npairs, lane_base, lane, pos);  // longest columns first
   const int slot = 2 * pos + csel;
-  const int my_j = slot < nb ? order[slot] : -1;  // -1: the pair's second column is past the end
+  // -1: the pair's second column is past the end
+  const int my_j = slot < nb ? (SUB ? slot : order[slot]) : -1;
+  const int my_k32 = 2 * my_j + kh;  // this wave's 32-key block
   const int64_t lane_off = lane * (int64_t)S * D;
   const uint16_t* qg = q + lane_off;
   const uint16_t* dog = dout + lane_off;
@@ -929,23 +951,24 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
     kop[c] = *(const u32x4*)(k + row_off + 16 * c);
     vop[c] = *(const u32x4*)(v + row_off + 16 * c);
   }
-  // Both columns' walkers: the union of their rows in ascending order.
-  ListWalker walk[2];
-  int head[2];
+  // The columns' walkers (the pair's two columns, or with SUB the four 32-key
+  // ones, wave w's being walker w): the union of their rows in ascending order.
+  constexpr int kWalk = SUB ? 4 : 2;
+  ListWalker walk[kWalk];
+  int head[kWalk];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int sr = 2 * pos + r;
-    const int jr = sr < nb ? order[sr] : -1;
-    if (jr >= 0) {
-      walk[r].init(col_ptr, row_idx, nnz_t, jr, jr, nb - 1, l);
+  for (int r = 0; r < kWalk; ++r) {
+    int jr;
+    if constexpr (SUB) {
+      jr = 4 * pos + r < ncols ? 4 * pos + r : -1;
     } else {
-      walk[r].p = walk[r].end = walk[r].win = 0;
-      walk[r].cols = -1;
-      walk[r].lo = 0;
-      walk[r].hi = -1;
-      walk[r].idx_ = row_idx;
-      walk[r].l_ = l;
+      const int sr = 2 * pos + r;
+      jr = sr < nb ? order[sr] : -1;
     }
+    if (jr >= 0)
+      walk[r].init(col_ptr, row_idx, nnz_t, jr, jr, ncols - 1, l);
+    else
+      walk[r].clear(row_idx, l);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
 #pragma unroll
@@ -954,20 +977,31 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
     asm volatile("" : "+v"(vop[c]));
   }
 #pragma unroll
-  for (int r = 0; r < 2; ++r) head[r] = walk[r].next(-1);
-  auto next_block = [&](bool& mine) -> int {
-    int i = -1;
+  for (int r = 0; r < kWalk; ++r) head[r] = walk[r].next(-1);
+  // Next 64-row query block of the union (-1: none); `mine` gets bit h set when
+  // this wave computes query half h of it.
+  auto next_block = [&](int& mine) -> int {
+    int hmin = INT_MAX;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      if (head[r] >= 0 && (i < 0 || head[r] < i)) i = head[r];
-    mine = false;
-    if (i < 0) return -1;
+    for (int r = 0; r < kWalk; ++r)
+      if (head[r] >= 0) hmin = min(hmin, head[r]);
+    mine = 0;
+    if (hmin == INT_MAX) return -1;
+    const int i = SUB ? hmin >> 1 : hmin;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-      if (head[r] == i) {
-        if (r == csel) mine = true;
+    for (int r = 0; r < kWalk; ++r) {
+      if constexpr (SUB) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)  // at most the two 32-row blocks of i, ascending
+          if (head[r] >= 0 && (head[r] >> 1) == i) {
+            if (r == w) mine |= 1 << (head[r] & 1);
+            head[r] = walk[r].next(head[r]);
+          }
+      } else if (head[r] == i) {
+        if (r == csel) mine = 3;
         head[r] = walk[r].next(i);
       }
+    }
     return i;
   };
 
@@ -1012,7 +1046,9 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
     constexpr int QH = decltype(QH_c)::value;
     constexpr int kOff = decltype(T_c)::value * kStageBytes + QH * kHalfRowBytes;
     constexpr int kStOff = decltype(T_c)::value * kStageBytes + QH * 256;
-    if (i == my_j && QH < kh) return;  // queries of this half all before the keys
+    // 32-row query block 2i + QH against this wave's 32-key block: earlier ones
+    // are fully masked (the acceptance rule never lists them under SUB).
+    if (2 * i + QH < my_k32) return;
     if constexpr (kFewLive) {
       // Head dim 128: phase by phase, so that fewer values are live at once
       // (398 -> 308 registers): the Q and dO operands only until the S and dP
@@ -1034,7 +1070,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
         for (int c = 0; c < kStepsD; ++c) dp = E::mfma(da[c], vop[c], dp);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (i == my_j && QH == kh) {
+      if (2 * i + QH == my_k32) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qpos = 16 * (r >> 3) + 8 * h + (r & 7);
@@ -1102,7 +1138,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
         tr_reads<kOff, G::kRowBytes>(&qt[dt * 4], t_addr[dt]);
         tr_reads<kOff + kTileBytes, G::kRowBytes>(&dt_[dt * 4], t_addr[dt]);
       }
-      if (i == my_j && QH == kh) {
+      if (2 * i + QH == my_k32) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qpos = 16 * (r >> 3) + 8 * h + (r & 7);
@@ -1137,7 +1173,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
 
   // Ring over the union, as in the one-column kernel.
   int blk[2];
-  bool mine[2] = {false, false};
+  int mine[2] = {0, 0};
   blk[0] = next_block(mine[0]);
   blk[1] = blk[0] >= 0 ? next_block(mine[1]) : -1;
   if (blk[0] >= 0) {
@@ -1158,10 +1194,8 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_duo_kernel(
         if (blk[refill] >= 0) fill(blk[refill], ring + refill * kStageBytes);
       }
       pre = false;
-      if (mine[t]) {
-        compute_half(blk[t], T_c, std::integral_constant<int, 0>{});
-        compute_half(blk[t], T_c, std::integral_constant<int, 1>{});
-      }
+      if (mine[t] & 1) compute_half(blk[t], T_c, std::integral_constant<int, 0>{});
+      if (mine[t] & 2) compute_half(blk[t], T_c, std::integral_constant<int, 1>{});
       done = blk[refill] < 0;
     };
     while (!done) {
@@ -1197,17 +1231,22 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
   const int64_t nb = (a.S + kBlock - 1) / kBlock;
   const int64_t max_wg = (int64_t(1) << 31) / kThreads;
   const int64_t lanes_per_launch = max_wg / nb > 0 ? max_wg / nb : 1;
+  const int64_t npairs = (nb + 1) / 2;
+  // Schedules over 32-row blocks always take the two-block kernels, whose four
+  // waves are the four 32-row blocks of a pair of 64-row blocks.
+  const bool sub = a.block == 32;
+  const int64_t nrows = sub ? (a.S + 31) / 32 : nb;
   for (int64_t l0 = 0; l0 < a.lanes; l0 += lanes_per_launch) {
     const int64_t nl = a.lanes - l0 < lanes_per_launch ? a.lanes - l0 : lanes_per_launch;
     // Two query blocks per workgroup once the halved grid still fills every CU
     // (the forward's rule: 2048 (lane, query block) pairs).
-    if (nl * nb >= kDqDuoMinPairs) {
-      const int64_t npairs = (nb + 1) / 2;
-      hipLaunchKernelGGL((attention_bwd_dq_duo_kernel<D, BF16>), dim3((unsigned)(nl * npairs)), dim3(kThreads),
-                         0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                         (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, a.row_ptr, a.col_idx,
-                         a.nnz, (int)a.S, (int)nb, (int)npairs, l0, a.scale_log2, a.scale,
-                         (float2*)a.stats, (uint16_t*)a.dq);
+    if (sub || nl * nb >= kDqDuoMinPairs) {
+      auto kern = sub ? attention_bwd_dq_duo_kernel<D, BF16, true> : attention_bwd_dq_duo_kernel<D, BF16, false>;
+      hipLaunchKernelGGL(kern, dim3((unsigned)(nl * npairs)), dim3(kThreads), 0, stream, (const uint16_t*)a.q,
+                         (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.out,
+                         (const uint16_t*)a.dout, a.lse, a.row_ptr, a.col_idx, a.nnz, (int)a.S, (int)nb,
+                         (int)nrows, (int)npairs, l0, a.scale_log2, a.scale, (float2*)a.stats,
+                         (uint16_t*)a.dq);
     } else {
       hipLaunchKernelGGL((attention_bwd_dq_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
                          stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
@@ -1220,10 +1259,12 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
   }
   // Two key blocks per workgroup under the same rule, paired by entry count, up
   // to 4096 key blocks (the ranking compares every pair of columns: at most 16.8 M
-  // comparisons; longer sequences keep one column per workgroup).
+  // comparisons; longer sequences keep one column per workgroup).  With 32-row
+  // blocks the workgroup takes the four 32-key columns of two adjacent 64-key
+  // blocks, unranked.
   constexpr int64_t kDkdvDuoMaxBlocks = 4096;
-  const bool dkdv_duo = a.lanes * nb >= kDqDuoMinPairs && nb <= kDkdvDuoMaxBlocks;
-  if (dkdv_duo) {
+  const bool dkdv_duo = sub || (a.lanes * nb >= kDqDuoMinPairs && nb <= kDkdvDuoMaxBlocks);
+  if (dkdv_duo && !sub) {
     hipLaunchKernelGGL(col_order_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, a.col_ptr,
                        (int)nb, a.nnz_t, a.col_order);
     hipError_t err = hipGetLastError();
@@ -1232,11 +1273,11 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
   for (int64_t l0 = 0; l0 < a.lanes; l0 += lanes_per_launch) {
     const int64_t nl = a.lanes - l0 < lanes_per_launch ? a.lanes - l0 : lanes_per_launch;
     if (dkdv_duo) {
-      const int64_t npairs = (nb + 1) / 2;
-      hipLaunchKernelGGL((attention_bwd_dkdv_duo_kernel<D, BF16>), dim3((unsigned)(nl * npairs)), dim3(kThreads),
-                         0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                         (const uint16_t*)a.dout, (const float2*)a.stats, a.col_ptr, a.row_idx, a.nnz_t,
-                         (const int32_t*)a.col_order, (int)a.S, (int)nb, (int)npairs, l0, a.scale_log2, a.scale,
+      auto kern = sub ? attention_bwd_dkdv_duo_kernel<D, BF16, true> : attention_bwd_dkdv_duo_kernel<D, BF16, false>;
+      hipLaunchKernelGGL(kern, dim3((unsigned)(nl * npairs)), dim3(kThreads), 0, stream, (const uint16_t*)a.q,
+                         (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                         (const float2*)a.stats, a.col_ptr, a.row_idx, a.nnz_t, (const int32_t*)a.col_order,
+                         (int)a.S, (int)nb, (int)nrows, (int)npairs, l0, a.scale_log2, a.scale,
                          (uint16_t*)a.dk, (uint16_t*)a.dv);
     } else {
       hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,

@@ -40,6 +40,7 @@ struct BwdArgs {
   bool bf16;
   int64_t lanes, S;
   int D;
+  int block;                      // 64, or 32 (schedules over 32-row blocks)
   float scale, scale_log2;
 };
 hipError_t launch_attention_bwd(const BwdArgs& args, hipStream_t stream);

@@ -376,7 +376,9 @@ size_t tsa_scheduled_attention_bwd_workspace_bytes(int64_t B, int64_t H, int64_t
  *               column that are outside j..nb-1 or not above the previous accepted
  *               one; a column view that is not the CSR's transpose gives
  *               unspecified gradients (never an out-of-bounds access).
- *   block       must be 64;  D 32, 64 or 128;  sm_scale as in the forward.
+ *   block       64, or TSA_SUB_BLOCK (32) for a schedule over 32-row blocks,
+ *               whose column view is then over 32-key blocks (nb = ceil(S / 32)
+ *               in both);  D 32, 64 or 128;  sm_scale as in the forward.
  *   dq, dk, dv  device, q's shape and dtype, written (rounded to nearest even).
  *   workspace   device, >= tsa_scheduled_attention_bwd_workspace_bytes(B, H, S)
  *               bytes, 16-byte aligned, any contents on entry; it holds each

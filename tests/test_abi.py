@@ -265,7 +265,8 @@ def test_backward_workspace_and_checks_before_gpu(lib):
     assert _bwd(lib, D=256) == -2  # the backward takes 32, 64 and 128
     assert _bwd(lib, D=32) == -1
     assert _bwd(lib, block=128) == -2
-    assert _bwd(lib, block=32) == -2  # the backward walks 64-row blocks only
+    assert _bwd(lib, block=48) == -2
+    assert _bwd(lib, block=32) == -1  # 32-row blocks pass the block check; the NULL pointers fail
     assert _bwd(lib, nnz_t=-1) == -1
     assert _bwd(lib, scale=float("inf")) == -1
     assert _bwd(lib) == -1 and b"NULL" in lib.tsa_last_error()

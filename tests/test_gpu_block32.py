@@ -18,7 +18,11 @@ walks its own CSR row, and the 64-key tiles it copies are the union of the
   built from lane (0, 0) at block 32), sampled rows of every lane;
 * a 64-row CSR and its 32-row expansion allow the same keys, and on the
   two-block kernel they take the same tiles in the same order, so their
-  outputs and lse are bitwise equal.
+  outputs and lse are bitwise equal;
+* the backward at block 32 (the two-block dq and dk/dv kernels with four
+  32-row rows or 32-key columns per workgroup): every dq, dk and dv against the
+  fp64 oracle at block 32 over the same kinds of schedule, the autograd
+  wrapper, and bitwise equality with the 64-row backward of the expanded CSR.
 
 Bars as in the other parity tests: max abs error <= 2e-3 (fp16) / 1e-2
 (bf16); lse within 1e-3 / 4e-3.  Output buffers are filled with NaN first, so
@@ -241,3 +245,99 @@ def test_32_row_expansion_is_bitwise_equal_on_the_two_block_kernel(tsa, B, H, S,
     torch.cuda.synchronize()
     assert torch.equal(o64.view(torch.int16), o32.view(torch.int16))
     assert torch.equal(l64.view(torch.int32), l32.view(torch.int32))
+
+
+# ---------------------------------------------------------------- backward
+
+BWD_CASES = [
+    # (B, H, S, D, dtype, schedule)
+    (2, 4, 1000, 64, "bf16", "topology"),   # 8 lanes: per-XCD lane order; ragged S
+    (1, 3, 1088, 32, "fp16", "random"),     # 3 lanes: plain order; empty rows
+    (2, 8, 777, 128, "fp16", "irregular"),  # entries the kernels must skip
+    (1, 5, 256, 64, "bf16", "dense"),
+    (1, 2, 33, 64, "fp16", "dense"),        # two 32-row blocks, the second of one row
+    (1, 2, 31, 32, "bf16", "dense"),        # one partial block
+    (3, 3, 300, 128, "bf16", "random"),
+    (2, 4, 200, 64, "fp16", "empty"),
+    (1, 2, 3000, 64, "bf16", "irregular_long"),  # rows and columns of many windows
+]
+
+
+def _grad_bar_check(name, got, ref, dtype):
+    g = got.double().cpu().numpy()
+    assert np.isfinite(g).all(), f"{name}: an element was not written"
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    err = float(np.abs(g - ref).max()) if ref.size else 0.0
+    assert err <= TOL[dtype] * max(scale, 1e-30), (name, err, scale)
+    return err, scale
+
+
+@pytest.mark.parametrize("case", range(len(BWD_CASES)))
+def test_backward_at_32_row_blocks_every_gradient(tsa, case):
+    """dq, dk and dv of every element over a 32-row CSR against the fp64 oracle
+    at block 32 (bars relative to each gradient's largest value)."""
+    B, H, S, D, dtype, kind = BWD_CASES[case]
+    shape = (B, H, S, D)
+    q, k, v = workloads.make_qkv(workloads.Workload("block32_bwd", shape, dtype, seed=1500 + case))
+    do = workloads.random_normal(shape, dtype, 1550 + case)
+    nb = -(-S // 32)
+    rp, ci = _schedule(kind, k, nb, 1600 + case)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    rpd, cid = _dev(rp), _dev(ci)
+    out, lse = tsa.scheduled_attention(qd, kd, vd, rpd, cid, block=32, return_lse=True)
+    cp, ri = tsa.schedule_transpose(rpd, cid)
+    dq, dk, dv = tsa.scheduled_attention_backward(qd, kd, vd, out, do.to(DEV), lse, rpd, cid, cp, ri,
+                                                  block=32)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, _, _ = oracle.attention_backward(q, k, v, do, rp, ci, block=32)
+    msg = []
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        err, scale = _grad_bar_check(name, g, r, dtype)
+        msg.append(f"{name} {err:.2e}/{scale:.2e}")
+    print(f"[{B},{H},{S},{D}] {dtype} {kind} block 32 backward: nnz {len(ci)}; " + ", ".join(msg))
+    if kind == "empty":
+        assert all(torch.count_nonzero(g) == 0 for g in (dq, dk, dv))
+
+
+def test_backward_at_32_row_blocks_through_autograd(tsa):
+    """The autograd wrapper at block 32 gives the direct call's gradients bit for bit."""
+    shape = (2, 4, 520, 64)
+    q, k, v = workloads.make_qkv(workloads.Workload("block32_ag", shape, "bf16", seed=1700))
+    do = workloads.random_normal(shape, "bf16", 1701).to(DEV)
+    rp, ci = workloads.random_csr(-(-520 // 32), seed=1702, density=0.4)
+    rpd, cid = _dev(rp), _dev(ci)
+    qd, kd, vd = (t.to(DEV).requires_grad_(True) for t in (q, k, v))
+    tsa.attention(qd, kd, vd, rpd, cid, block=32).backward(do)
+    out, lse = tsa.scheduled_attention(qd.detach(), kd.detach(), vd.detach(), rpd, cid, block=32,
+                                       return_lse=True)
+    cp, ri = tsa.schedule_transpose(rpd, cid)
+    ref = tsa.scheduled_attention_backward(qd.detach(), kd.detach(), vd.detach(), out, do, lse, rpd, cid,
+                                           cp, ri, block=32)
+    torch.cuda.synchronize()
+    for g, r in zip((qd.grad, kd.grad, vd.grad), ref):
+        assert torch.equal(g.view(torch.int16), r.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,H,S,D,dtype", [(2, 16, 4096, 64, "bf16"), (2, 16, 4096, 128, "fp16")])
+def test_backward_32_row_expansion_is_bitwise_equal_on_the_two_block_kernels(tsa, B, H, S, D, dtype):
+    """A 64-row CSR and its 32-row expansion give bitwise-equal gradients where
+    the 64-row backward also takes the two-block kernels (from 2048 (lane, block)
+    pairs up, here 32 lanes x 64 blocks): each wave walks the same tiles in the
+    same order."""
+    shape = (B, H, S, D)
+    q, k, v = workloads.make_qkv(workloads.Workload("block32_bwd_eq", shape, dtype, seed=1800 + D))
+    do = workloads.random_normal(shape, dtype, 1801 + D).to(DEV)
+    nb = -(-S // 64)
+    assert B * H * nb >= 2048
+    rp, ci = workloads.random_csr(nb, seed=1810 + D, density=0.4)
+    rp32, ci32 = _expand_to_32(rp, ci, S)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    grads = []
+    for rpn, cin, block in ((rp, ci, 64), (rp32, ci32, 32)):
+        rpd, cid = _dev(rpn), _dev(cin)
+        out, lse = tsa.scheduled_attention(qd, kd, vd, rpd, cid, block=block, return_lse=True)
+        cp, ri = tsa.schedule_transpose(rpd, cid)
+        grads.append(tsa.scheduled_attention_backward(qd, kd, vd, out, do, lse, rpd, cid, cp, ri, block=block))
+    torch.cuda.synchronize()
+    for a, b in zip(*grads):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
