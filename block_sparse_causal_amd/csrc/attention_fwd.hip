@@ -428,6 +428,10 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
     // v_rcp_f32 (1 ulp): l_tot >= 2^-8 here, far from the denormal range
     const float inv = l_tot > 0.0f ? __builtin_amdgcn_rcpf(l_tot) : 0.0f;
     const float cs = fs * inv, cp = fp * inv;
+    // A row with no visible key (l_tot = 0) is written as +0 by a select, so its
+    // output does not depend on what the accumulators or the exchange area hold
+    // (products with a zero factor would carry their sign).
+    const bool live = l_tot > 0.0f;
     // log of the row's denominator in natural units: log2(sum 2^(z log2 e)) = m + log2(l_tot)
     if (KH == 0 && lse != nullptr && qrow < S)
       lse[lane * (int64_t)S + qrow] =
@@ -443,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
             const f32x4 y = *(const f32x4*)(recv + t * 16 + 4 * gg);
             float x[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = o[kKeepBase + t][4 * gg + e] * cs + y[e] * cp;
+            for (int e = 0; e < 4; ++e) x[e] = live ? o[kKeepBase + t][4 * gg + e] * cs + y[e] * cp : 0.0f;
             u32x2 val;
             val[0] = E::pack(x[0], x[1]);
             val[1] = E::pack(x[2], x[3]);
@@ -457,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void attention_fwd_kernel(
           const f32x4 y = *(const f32x4*)(recv + 4 * gl);
           float x[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = o[0][4 * (kKeepGroup + gl) + e] * cs + y[e] * cp;
+          for (int e = 0; e < 4; ++e) x[e] = live ? o[0][4 * (kKeepGroup + gl) + e] * cs + y[e] * cp : 0.0f;
           u32x2 val;
           val[0] = E::pack(x[0], x[1]);
           val[1] = E::pack(x[2], x[3]);

@@ -444,6 +444,7 @@ __global__ __launch_bounds__(kDuoThreads) void attention_fwd_duo_kernel(
         u32x2 val;
         val[0] = E::pack(o[t][4 * gg] * inv, o[t][4 * gg + 1] * inv);
         val[1] = E::pack(o[t][4 * gg + 2] * inv, o[t][4 * gg + 3] * inv);
+        if (!(l_tot > 0.0f)) val = u32x2{0u, 0u};  // no visible key: +0, whatever o holds
         *(u32x2*)(orow + 32 * t + 8 * gg + 4 * h) = val;
       }
   }
