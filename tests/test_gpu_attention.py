@@ -134,6 +134,22 @@ def test_all_empty_rows_give_zeros(tsa):
     assert torch.count_nonzero(out) == 0
 
 
+@pytest.mark.parametrize("shape,block", [((4, 4, 2112, 64), 64), ((8, 32, 1024, 64), 64), ((2, 4, 1000, 128), 64),
+                                         ((2, 4, 640, 32), 32), ((4, 8, 700, 256), 64)])
+def test_empty_rows_are_positive_zero_bits(tsa, shape, block):
+    """Rows with no visible key are +0 bit for bit (no -0), on launches of both
+    forward kernels that fill many workgroup slots; lse is -inf there."""
+    q = workloads.random_normal(shape, "bf16", 21)
+    nrows = -(-shape[2] // block)
+    rp, ci = _csr_dev(np.zeros(nrows + 1, np.int32), np.zeros(0, np.int32))
+    qd = q.to("cuda:0")
+    out = torch.full_like(qd, 7.0)
+    out, lse = tsa.scheduled_attention(qd, qd, qd, rp, ci, block=block, out=out, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out.view(torch.int16)) == 0
+    assert bool(torch.isneginf(lse).all())
+
+
 def test_invalid_entries_are_skipped_like_the_oracle(tsa):
     """Future blocks, duplicates-after-sort and out-of-range entries are skipped."""
     q, k, v = (workloads.random_normal((256, 64), "fp16", s) for s in (13, 14, 15))
