@@ -8,7 +8,8 @@ compared here with the fp64 oracle (a dropped or doubled lane range would leave
 unwritten memory, which these tests fill with NaN first).
 
 Cases: [2, 4, 1088, D] for D = 32, 64, 128, 256 (17 query blocks, a ragged
-count), forward output and lse; the backward's dq, dk and dv at [1, 8, 1024, 64]
+count), forward output and lse; 16 and 32 lanes at D = 128, where each XCD runs
+its lanes two at a time (64- and 32-row blocks); the backward's dq, dk and dv at [1, 8, 1024, 64]
 and [2, 4, 640, 128]; and the batched workload (64 lanes x 4096 rows) in full.
 One CSR, built from lane (0, 0)'s keys, is shared by every lane (PR page
 "Add topology-derived sparse attention kernel", Summary, third bullet).
@@ -66,6 +67,31 @@ def test_forward_every_lane_and_row(tsa, D, dtype):
     lerr = float(np.abs(lse.double().cpu().numpy() - want_lse).max())
     print(f"[2,4,1088,{D}] {dtype}: nnz {len(ci)}, max abs err {err:.2e}, lse {lerr:.2e}, "
           f"max|O| {np.abs(want_out).max():.2f}")
+    assert err <= TOL[dtype]
+    assert lerr <= TOL_LSE[dtype]
+
+
+@pytest.mark.parametrize("shape,dtype,block", [((2, 8, 1088, 128), "bf16", 64), ((4, 8, 700, 128), "fp16", 64),
+                                               ((2, 8, 1000, 128), "bf16", 32)])
+def test_forward_lane_pairs_per_xcd_every_output(tsa, shape, dtype, block):
+    """At head dim 128 with a lane count that is a multiple of 16, each XCD runs
+    its lanes two at a time (pairs of lanes, every pair position longest first):
+    every output and lse element of such launches against the oracle."""
+    w = workloads.Workload("lane_pairs", shape, dtype, seed=650 + shape[0] + block)
+    q, k, v = workloads.make_qkv(w)
+    rp, ci, _ = oracle.build_schedule(k[0, 0].contiguous(), block, 1, 2, 4)
+    rpd, cid = _csr(rp, ci)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = _poisoned(qd)
+    out, lse = tsa.scheduled_attention(qd, kd, vd, rpd, cid, block=block, out=out, return_lse=True)
+    torch.cuda.synchronize()
+    want_out = oracle.masked_attention(q, k, v, rp, ci, block)
+    want_lse = oracle.masked_lse(q, k, rp, ci, block)
+    got = out.double().cpu().numpy()
+    assert np.isfinite(got).all(), "an output element was not written"
+    err = float(np.abs(got - want_out).max())
+    lerr = float(np.abs(lse.double().cpu().numpy() - want_lse).max())
+    print(f"{list(shape)} {dtype} block {block}: nnz {len(ci)}, max abs err {err:.2e}, lse {lerr:.2e}")
     assert err <= TOL[dtype]
     assert lerr <= TOL_LSE[dtype]
 
