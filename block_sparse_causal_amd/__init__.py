@@ -458,8 +458,9 @@ def scheduled_attention_backward(q, k, v, out, dout, lse, row_ptr, col_idx, col_
     """Gradients (dq, dk, dv) of ``scheduled_attention`` for the upstream gradient
     ``dout``; ``out`` and ``lse`` are the forward's (``return_lse=True``) and
     (col_ptr, row_idx) is ``schedule_transpose(row_ptr, col_idx)``.  The schedule
-    is over blocks of ``block`` rows: 64, or SUB_BLOCK (32) at head dims up to
-    128.  Returns tensors of q's shape and dtype."""
+    is over blocks of ``block`` rows: 64 (head dims 32, 64, 128 and 256), or
+    SUB_BLOCK (32) at head dims up to 128.  Returns tensors of q's shape and
+    dtype."""
     code, B, H, S, D = _attention_shape(q, k, v)
     for name, t in (("out", out), ("dout", dout)):
         if not isinstance(t, torch.Tensor) or t.shape != q.shape or t.dtype != q.dtype:

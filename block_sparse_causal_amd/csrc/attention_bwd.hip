@@ -170,7 +170,7 @@ struct ListWalker {
 // ----------------------------------------------------------------------------
 // dq kernel
 // ----------------------------------------------------------------------------
-template <int D, bool BF16>
+template <int D, bool BF16, int DO>
 __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
@@ -181,6 +181,10 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
   using G = Geo<D>;
   constexpr int kStepsD = G::kStepsD, kTilesD = G::kTilesD, kTileBytes = G::kTileBytes;
   constexpr int kStageBytes = 2 * kTileBytes;  // [K tile | V tile]
+  // Head dims of dQ written here: all D, or the half of D = 256 that blockIdx.y
+  // selects (S and dP always contract over all D).
+  constexpr int kTilesO = DO / 32;
+  const int d0 = DO < D ? (int)blockIdx.y * DO : 0;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kStageBytes];
 
   const int tid = threadIdx.x;
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
   }
   delta = sum_with_other_half(delta);
   float lse2 = lse[lane * (int64_t)S + qrow_c] * kLog2e;
-  if (kh == 0 && qrow < S) stats[lane * (int64_t)S + qrow] = float2{lse2, delta};
+  if (kh == 0 && qrow < S && d0 == 0) stats[lane * (int64_t)S + qrow] = float2{lse2, delta};
   // Every load above has landed before any copy is queued, so the ring's waits
   // below count copies only.
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
@@ -242,35 +246,47 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
   uint32_t a_addr[kStepsD];
 #pragma unroll
   for (int c = 0; c < kStepsD; ++c) a_addr[c] = row_read_addr<D>(base, kh, n, h, c);
-  uint32_t t_addr[kTilesD][2];
+  uint32_t t_addr[kTilesO][2];
 #pragma unroll
-  for (int dt = 0; dt < kTilesD; ++dt) tr_read_addrs<D>(t_addr[dt], base, kh, g, gi, dt);
+  for (int dt = 0; dt < kTilesO; ++dt) tr_read_addrs<D>(t_addr[dt], base, kh, g, gi, d0 / 32 + dt);
 
-  f32x16 acc[kTilesD];
+  f32x16 acc[kTilesO];
 #pragma unroll
-  for (int dt = 0; dt < kTilesD; ++dt) acc[dt] = f32x16{};
+  for (int dt = 0; dt < kTilesO; ++dt) acc[dt] = f32x16{};
 
   auto compute = [&](int j, auto T_c) {
-    constexpr int kOff = decltype(T_c)::value * kStageBytes;
+    // Stage offset: in the reads' 16-bit offset field when it fits, else (D = 256,
+    // second stage at 64 KB) added to the lane addresses.
+    constexpr int kStageAll = decltype(T_c)::value * kStageBytes;
+    constexpr int kOff = kStageAll + kTileBytes + 16 * G::kRowBytes < 65536 ? kStageAll : 0;
+    constexpr uint32_t kReg = (uint32_t)(kStageAll - kOff);
+    // Operand reads in flight at once: all of them, or four steps at D = 256.
+    constexpr int kChunk = kStepsD > 8 ? 4 : kStepsD;
     if (j == i && kh > qh) return;  // keys of this half all after the queries
-    u32x4 ka[kStepsD], va[kStepsD];
-#pragma unroll
-    for (int c = 0; c < kStepsD; ++c) {
-      ka[c] = lds_read_b128<kOff>(a_addr[c]);
-      va[c] = lds_read_b128<kOff + kTileBytes>(a_addr[c]);
-    }
-    lds_wait_all(ka);
-    lds_wait_all(va);
     // S^T = K . Q^T and dP^T = V . dO^T: MFMA row m holds key 32kh + pi(m).
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int c = 0; c < kStepsD; ++c) s = E::mfma(ka[c], qop[c], s);
+    for (int c0 = 0; c0 < kStepsD; c0 += kChunk) {
+      u32x4 ka[kChunk], va[kChunk];
 #pragma unroll
-    for (int c = 0; c < kStepsD; ++c) dp = E::mfma(va[c], dop[c], dp);
+      for (int c = 0; c < kChunk; ++c) {
+        ka[c] = lds_read_b128<kOff>(a_addr[c0 + c] + kReg);
+        va[c] = lds_read_b128<kOff + kTileBytes>(a_addr[c0 + c] + kReg);
+      }
+      lds_wait_all(ka);
+      lds_wait_all(va);
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) s = E::mfma(ka[c], qop[c0 + c], s);
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) dp = E::mfma(va[c], dop[c0 + c], dp);
+    }
     // K^T operands of dQ^T += K^T . dS^T, landing while dS is formed.
-    u32x2 kt[kTilesD * 4];
+    u32x2 kt[kTilesO * 4];
 #pragma unroll
-    for (int dt = 0; dt < kTilesD; ++dt) tr_reads<kOff, G::kRowBytes>(&kt[dt * 4], t_addr[dt]);
+    for (int dt = 0; dt < kTilesO; ++dt) {
+      const uint32_t ta[2] = {t_addr[dt][0] + kReg, t_addr[dt][1] + kReg};
+      tr_reads<kOff, G::kRowBytes>(&kt[dt * 4], ta);
+    }
     if (j == i && kh == qh) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -290,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
       }
     lds_wait_all(kt);
 #pragma unroll
-    for (int dt = 0; dt < kTilesD; ++dt)
+    for (int dt = 0; dt < kTilesO; ++dt)
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) acc[dt] = E::mfma(tr_operand(&kt[dt * 4], gg), pb[gg], acc[dt]);
   };
@@ -331,12 +347,12 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
     __syncthreads();
   }
 
-  // Sum the two key halves: wave kh keeps tiles [kh, kh + 1) * kTilesD / 2 and
+  // Sum the two key halves: wave kh keeps tiles [kh, kh + 1) * kTilesO / 2 and
   // hands the others to its partner through LDS, then stores scale * sum.
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-  // Register groups of 4 (4 consecutive head dims each): kTilesD * 4 per lane.
+  // Register groups of 4 (4 consecutive head dims each): kTilesO * 4 per lane.
   // Wave kh keeps groups [kh, kh + 1) * kGroups / 2 and sends the others.
-  constexpr int kGroups = kTilesD * 4;
+  constexpr int kGroups = kTilesO * 4;
   constexpr int kHalfGroups = kGroups / 2;
   constexpr int kSendStride = kHalfGroups * 4 + 4;
   static_assert(4 * 64 * kSendStride * 4 <= 2 * kStageBytes, "merge area exceeds the ring");
@@ -368,8 +384,8 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
         u32x2 val;
         val[0] = E::pack(x[0], x[1]);
         val[1] = E::pack(x[2], x[3]);
-        // group gq: tile gq / 4, register group gq % 4 -> dims 32 (gq / 4) + 8 (gq % 4) + 4h
-        *(u32x2*)(drow + 32 * (gq / 4) + 8 * (gq % 4) + 4 * h) = val;
+        // group gq: tile gq / 4, register group gq % 4 -> dims d0 + 32 (gq / 4) + 8 (gq % 4) + 4h
+        *(u32x2*)(drow + d0 + 32 * (gq / 4) + 8 * (gq % 4) + 4 * h) = val;
       }
     }
   };
@@ -616,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_duo_kernel(
 // ----------------------------------------------------------------------------
 // dkdv kernel
 // ----------------------------------------------------------------------------
-template <int D, bool BF16>
+template <int D, bool BF16, int DO>
 __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float2* __restrict__ stats,
@@ -629,8 +645,12 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
   constexpr int kStatBytes = 1024;  // 4 slots of 256 B; slots 0, 1 hold the block's 64 (lse2, Delta)
   constexpr int kStageBytes = 2 * kTileBytes + kStatBytes;  // [Q tile | dO tile | stats]
   constexpr int kFillOps = G::kTileOps + 1;
+  // Head dims of dK and dV written here: all D, or the half of D = 256 that
+  // blockIdx.y selects (S and dP always contract over all D).
+  constexpr int kTilesO = DO / 32;
+  const int d0 = DO < D ? (int)blockIdx.y * DO : 0;
   // The ring, reused after the loop for the merge of the two query halves.
-  constexpr int kMergeBytes = 4 * 64 * (G::kTilesD * 16 + 4) * 4;  // 2 accumulators x half the groups
+  constexpr int kMergeBytes = 4 * 64 * (kTilesO * 16 + 4) * 4;  // 2 accumulators x half the groups
   constexpr int kRingBytes = 2 * kStageBytes > kMergeBytes ? 2 * kStageBytes : kMergeBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
 
@@ -690,48 +710,61 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
   uint32_t a_addr[kStepsD];
 #pragma unroll
   for (int c = 0; c < kStepsD; ++c) a_addr[c] = row_read_addr<D>(base, qh, n, h, c);
-  uint32_t t_addr[kTilesD][2];
+  uint32_t t_addr[kTilesO][2];
 #pragma unroll
-  for (int dt = 0; dt < kTilesD; ++dt) tr_read_addrs<D>(t_addr[dt], base, qh, g, gi, dt);
+  for (int dt = 0; dt < kTilesO; ++dt) tr_read_addrs<D>(t_addr[dt], base, qh, g, gi, d0 / 32 + dt);
   // Statistics of the query rows of this lane's result registers: register r
   // holds query row 32qh + 16 (r >> 3) + 8h + (r & 7).
   const uint32_t st_addr = base + 2 * kTileBytes + 8 * (32 * qh + 8 * h);
 
-  f32x16 adk[kTilesD], adv[kTilesD];
+  f32x16 adk[kTilesO], adv[kTilesO];
 #pragma unroll
-  for (int dt = 0; dt < kTilesD; ++dt) {
+  for (int dt = 0; dt < kTilesO; ++dt) {
     adk[dt] = f32x16{};
     adv[dt] = f32x16{};
   }
 
   auto compute = [&](int i, auto T_c) {
-    constexpr int kOff = decltype(T_c)::value * kStageBytes;
+    // Stage offset: in the reads' 16-bit offset field when it fits, else (D = 256,
+    // second stage past 64 KB) added to the lane addresses.
+    constexpr int kStageAll = decltype(T_c)::value * kStageBytes;
+    constexpr int kOff = kStageAll + kTileBytes + 16 * G::kRowBytes < 65536 ? kStageAll : 0;
+    constexpr uint32_t kReg = (uint32_t)(kStageAll - kOff);
+    // Operand reads in flight at once: all of them, or four steps at D = 256.
+    constexpr int kChunk = kStepsD > 8 ? 4 : kStepsD;
     if (i == j && qh < kh) return;  // queries of this half all before the keys
-    u32x4 qa[kStepsD], da[kStepsD], st[8];
-#pragma unroll
-    for (int c = 0; c < kStepsD; ++c) {
-      qa[c] = lds_read_b128<kOff>(a_addr[c]);
-      da[c] = lds_read_b128<kOff + kTileBytes>(a_addr[c]);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      st[e] = lds_read_b128<kOff>(st_addr + 16 * e);
-      st[4 + e] = lds_read_b128<kOff + 128>(st_addr + 16 * e);
-    }
-    lds_wait_all(qa);
-    lds_wait_all(da);
-    lds_wait_all(st);
+    u32x4 st[8];
     // S = Q . K^T and dP = dO . V^T: MFMA row m holds query 32qh + pi(m), column n key 32kh + n.
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int c = 0; c < kStepsD; ++c) s = E::mfma(qa[c], kop[c], s);
+    for (int c0 = 0; c0 < kStepsD; c0 += kChunk) {
+      u32x4 qa[kChunk], da[kChunk];
 #pragma unroll
-    for (int c = 0; c < kStepsD; ++c) dp = E::mfma(da[c], vop[c], dp);
-    u32x2 qt[kTilesD * 4], dt_[kTilesD * 4];
+      for (int c = 0; c < kChunk; ++c) {
+        qa[c] = lds_read_b128<kOff>(a_addr[c0 + c] + kReg);
+        da[c] = lds_read_b128<kOff + kTileBytes>(a_addr[c0 + c] + kReg);
+      }
+      if (c0 == 0) {
 #pragma unroll
-    for (int dt = 0; dt < kTilesD; ++dt) {
-      tr_reads<kOff, G::kRowBytes>(&qt[dt * 4], t_addr[dt]);
-      tr_reads<kOff + kTileBytes, G::kRowBytes>(&dt_[dt * 4], t_addr[dt]);
+        for (int e = 0; e < 4; ++e) {
+          st[e] = lds_read_b128<kOff>(st_addr + kReg + 16 * e);
+          st[4 + e] = lds_read_b128<kOff + 128>(st_addr + kReg + 16 * e);
+        }
+      }
+      lds_wait_all(qa);
+      lds_wait_all(da);
+      if (c0 == 0) lds_wait_all(st);
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) s = E::mfma(qa[c], kop[c0 + c], s);
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) dp = E::mfma(da[c], vop[c0 + c], dp);
+    }
+    u32x2 qt[kTilesO * 4], dt_[kTilesO * 4];
+#pragma unroll
+    for (int dt = 0; dt < kTilesO; ++dt) {
+      const uint32_t ta[2] = {t_addr[dt][0] + kReg, t_addr[dt][1] + kReg};
+      tr_reads<kOff, G::kRowBytes>(&qt[dt * 4], ta);
+      tr_reads<kOff + kTileBytes, G::kRowBytes>(&dt_[dt * 4], ta);
     }
     if (i == j && qh == kh) {
 #pragma unroll
@@ -757,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
     lds_wait_all(qt);
     lds_wait_all(dt_);
 #pragma unroll
-    for (int dt = 0; dt < kTilesD; ++dt)
+    for (int dt = 0; dt < kTilesO; ++dt)
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         adv[dt] = E::mfma(tr_operand(&dt_[dt * 4], gg), pp[gg], adv[dt]);
@@ -800,11 +833,11 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
   }
 
   // Sum the two query halves: wave qh keeps head-dim tiles [qh, qh + 1) *
-  // kTilesD / 2 of dK and dV and hands the others to its partner.
+  // kTilesO / 2 of dK and dV and hands the others to its partner.
   __builtin_amdgcn_s_waitcnt(vmcnt_wait(0));
-  // Register groups of 4 head dims, kTilesD * 4 per accumulator; wave qh keeps
+  // Register groups of 4 head dims, kTilesO * 4 per accumulator; wave qh keeps
   // groups [qh, qh + 1) * kGroups / 2 of dK and dV and sends the others.
-  constexpr int kGroups = kTilesD * 4;
+  constexpr int kGroups = kTilesO * 4;
   constexpr int kHalfGroups = kGroups / 2;
   constexpr int kSendStride = 2 * kHalfGroups * 4 + 4;
   static_assert(4 * 64 * kSendStride * 4 <= kRingBytes, "merge area exceeds the ring");
@@ -841,7 +874,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
           xk[e] = (adk[gq / 4][4 * (gq % 4) + e] + yk[e]) * scale;
           xv[e] = adv[gq / 4][4 * (gq % 4) + e] + yv[e];
         }
-        const int col = 32 * (gq / 4) + 8 * (gq % 4) + 4 * h;
+        const int col = d0 + 32 * (gq / 4) + 8 * (gq % 4) + 4 * h;
         *(u32x2*)(krow_dk + col) = u32x2{E::pack(xk[0], xk[1]), E::pack(xk[2], xk[3])};
         *(u32x2*)(krow_dv + col) = u32x2{E::pack(xv[0], xv[1]), E::pack(xv[2], xv[3])};
       }
@@ -1236,19 +1269,31 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
   // waves are the four 32-row blocks of a pair of 64-row blocks.
   const bool sub = a.block == 32;
   const int64_t nrows = sub ? (a.S + 31) / 32 : nb;
+  // At D = 256 the dQ, dK and dV accumulators of all the head dims do not fit a
+  // wave's registers: the one-block kernels run twice as wide a grid, blockIdx.y
+  // selecting the half of the head dims each workgroup writes, and recompute S
+  // and dP (over all D) in both halves.
+  constexpr bool kSplit = D > 128;
+  constexpr int kDO = kSplit ? D / 2 : D;
+  const unsigned halves = kSplit ? 2u : 1u;
   for (int64_t l0 = 0; l0 < a.lanes; l0 += lanes_per_launch) {
     const int64_t nl = a.lanes - l0 < lanes_per_launch ? a.lanes - l0 : lanes_per_launch;
     // Two query blocks per workgroup once the halved grid still fills every CU
     // (the forward's rule: 2048 (lane, query block) pairs).
-    if (sub || nl * nb >= kDqDuoMinPairs) {
-      auto kern = sub ? attention_bwd_dq_duo_kernel<D, BF16, true> : attention_bwd_dq_duo_kernel<D, BF16, false>;
-      hipLaunchKernelGGL(kern, dim3((unsigned)(nl * npairs)), dim3(kThreads), 0, stream, (const uint16_t*)a.q,
-                         (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.out,
-                         (const uint16_t*)a.dout, a.lse, a.row_ptr, a.col_idx, a.nnz, (int)a.S, (int)nb,
-                         (int)nrows, (int)npairs, l0, a.scale_log2, a.scale, (float2*)a.stats,
-                         (uint16_t*)a.dq);
-    } else {
-      hipLaunchKernelGGL((attention_bwd_dq_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
+    bool duo = false;
+    if constexpr (!kSplit) {
+      if (sub || nl * nb >= kDqDuoMinPairs) {
+        duo = true;
+        auto kern = sub ? attention_bwd_dq_duo_kernel<D, BF16, true> : attention_bwd_dq_duo_kernel<D, BF16, false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)(nl * npairs)), dim3(kThreads), 0, stream, (const uint16_t*)a.q,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.out,
+                           (const uint16_t*)a.dout, a.lse, a.row_ptr, a.col_idx, a.nnz, (int)a.S, (int)nb,
+                           (int)nrows, (int)npairs, l0, a.scale_log2, a.scale, (float2*)a.stats,
+                           (uint16_t*)a.dq);
+      }
+    }
+    if (!duo) {
+      hipLaunchKernelGGL((attention_bwd_dq_kernel<D, BF16, kDO>), dim3((unsigned)(nl * nb), halves), dim3(kThreads), 0,
                          stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                          (const uint16_t*)a.out, (const uint16_t*)a.dout, a.lse, a.row_ptr, a.col_idx,
                          a.nnz, (int)a.S, (int)nb, l0, a.scale_log2, a.scale, (float2*)a.stats,
@@ -1263,7 +1308,7 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
   // blocks the workgroup takes the four 32-key columns of two adjacent 64-key
   // blocks, unranked.
   constexpr int64_t kDkdvDuoMaxBlocks = 4096;
-  const bool dkdv_duo = sub || (a.lanes * nb >= kDqDuoMinPairs && nb <= kDkdvDuoMaxBlocks);
+  const bool dkdv_duo = !kSplit && (sub || (a.lanes * nb >= kDqDuoMinPairs && nb <= kDkdvDuoMaxBlocks));
   if (dkdv_duo && !sub) {
     hipLaunchKernelGGL(col_order_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, stream, a.col_ptr,
                        (int)nb, a.nnz_t, a.col_order);
@@ -1272,15 +1317,20 @@ hipError_t launch_bwd_typed(const BwdArgs& a, hipStream_t stream) {
   }
   for (int64_t l0 = 0; l0 < a.lanes; l0 += lanes_per_launch) {
     const int64_t nl = a.lanes - l0 < lanes_per_launch ? a.lanes - l0 : lanes_per_launch;
-    if (dkdv_duo) {
-      auto kern = sub ? attention_bwd_dkdv_duo_kernel<D, BF16, true> : attention_bwd_dkdv_duo_kernel<D, BF16, false>;
-      hipLaunchKernelGGL(kern, dim3((unsigned)(nl * npairs)), dim3(kThreads), 0, stream, (const uint16_t*)a.q,
-                         (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                         (const float2*)a.stats, a.col_ptr, a.row_idx, a.nnz_t, (const int32_t*)a.col_order,
-                         (int)a.S, (int)nb, (int)nrows, (int)npairs, l0, a.scale_log2, a.scale,
-                         (uint16_t*)a.dk, (uint16_t*)a.dv);
-    } else {
-      hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D, BF16>), dim3((unsigned)(nl * nb)), dim3(kThreads), 0,
+    bool duo = false;
+    if constexpr (!kSplit) {
+      if (dkdv_duo) {
+        duo = true;
+        auto kern = sub ? attention_bwd_dkdv_duo_kernel<D, BF16, true> : attention_bwd_dkdv_duo_kernel<D, BF16, false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)(nl * npairs)), dim3(kThreads), 0, stream, (const uint16_t*)a.q,
+                           (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                           (const float2*)a.stats, a.col_ptr, a.row_idx, a.nnz_t, (const int32_t*)a.col_order,
+                           (int)a.S, (int)nb, (int)nrows, (int)npairs, l0, a.scale_log2, a.scale,
+                           (uint16_t*)a.dk, (uint16_t*)a.dv);
+      }
+    }
+    if (!duo) {
+      hipLaunchKernelGGL((attention_bwd_dkdv_kernel<D, BF16, kDO>), dim3((unsigned)(nl * nb), halves), dim3(kThreads), 0,
                          stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                          (const uint16_t*)a.dout, (const float2*)a.stats, a.col_ptr, a.row_idx, a.nnz_t,
                          (int)a.S, (int)nb, l0, a.scale_log2, a.scale, (uint16_t*)a.dk, (uint16_t*)a.dv);
@@ -1297,6 +1347,8 @@ hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t stream) {
   if (a.D == 64) return a.bf16 ? launch_bwd_typed<64, true>(a, stream) : launch_bwd_typed<64, false>(a, stream);
   if (a.D == 128) return a.bf16 ? launch_bwd_typed<128, true>(a, stream) : launch_bwd_typed<128, false>(a, stream);
   if (a.D == 32) return a.bf16 ? launch_bwd_typed<32, true>(a, stream) : launch_bwd_typed<32, false>(a, stream);
+  if (a.D == 256 && a.block == 64)
+    return a.bf16 ? launch_bwd_typed<256, true>(a, stream) : launch_bwd_typed<256, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

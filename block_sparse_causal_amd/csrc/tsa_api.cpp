@@ -69,10 +69,10 @@ int64_t row_cap(int32_t sink, int32_t local_radius, int32_t topk) {
 
 
 // Checks shared by the attention entry points (no GPU call); sets *lanes.
-// max_d: the largest head dim the entry point takes (256 forward, 128 backward);
-// the others are 32, 64 and 128.  sub_block: the entry point also takes
-// schedules over 32-row blocks (the forward and the backward, at head dims up to
-// 128).
+// max_d: the largest head dim the entry point takes (256 for the forward and the
+// backward); the others are 32, 64 and 128.  sub_block: the entry point also
+// takes schedules over 32-row blocks (the forward and the backward, at head dims
+// up to 128).
 int check_attention_args(const char* fn, int32_t dtype, int64_t B, int64_t H, int64_t S, int64_t D,
                          int64_t nnz, int32_t block, float sm_scale, int64_t max_d, bool sub_block,
                          int64_t* lanes) {
@@ -506,7 +506,7 @@ int tsa_scheduled_attention_bwd(const void* q, const void* k, const void* v, con
                                 size_t workspace_bytes, void* stream) {
   const char* fn = "tsa_scheduled_attention_bwd";
   int64_t lanes = 0;
-  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, 128, true, &lanes);
+  int rc = check_attention_args(fn, dtype, B, H, S, D, nnz, block, sm_scale, 256, true, &lanes);
   if (rc != TSA_OK) return rc;
   if (nnz_t < 0) return fail(TSA_ERR_INVALID_ARG, "%s: nnz_t must be >= 0", fn);
   if (lanes == 0 || S == 0) return ok();

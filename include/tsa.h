@@ -378,7 +378,10 @@ size_t tsa_scheduled_attention_bwd_workspace_bytes(int64_t B, int64_t H, int64_t
  *               unspecified gradients (never an out-of-bounds access).
  *   block       64, or TSA_SUB_BLOCK (32) for a schedule over 32-row blocks,
  *               whose column view is then over 32-key blocks (nb = ceil(S / 32)
- *               in both);  D 32, 64 or 128;  sm_scale as in the forward.
+ *               in both; D up to 128 there);  D 32, 64, 128 or 256 at block
+ *               64 (at 256 each workgroup writes half the head dims and forms S
+ *               and dP over all of them, so those two products run twice);
+ *               sm_scale as in the forward.
  *   dq, dk, dv  device, q's shape and dtype, written (rounded to nearest even).
  *   workspace   device, >= tsa_scheduled_attention_bwd_workspace_bytes(B, H, S)
  *               bytes, 16-byte aligned, any contents on entry; it holds each

@@ -262,7 +262,8 @@ def test_backward_workspace_and_checks_before_gpu(lib):
     assert lib.tsa_scheduled_attention_bwd_workspace_bytes(1, 1, 1 << 62) == 0
     assert _bwd(lib, dtype=7) == -1
     assert _bwd(lib, D=96) == -2
-    assert _bwd(lib, D=256) == -2  # the backward takes 32, 64 and 128
+    assert _bwd(lib, D=256) == -1  # head dim 256 passes the checks; the NULL pointers fail
+    assert _bwd(lib, D=256, block=32) == -2  # 32-row blocks stop at head dim 128
     assert _bwd(lib, D=32) == -1
     assert _bwd(lib, block=128) == -2
     assert _bwd(lib, block=48) == -2
