@@ -3,8 +3,8 @@ head dim 32, 64, 128 or 256, fp16 or bf16, 1, 2 or 4 batches x 1, 2 or 4 heads
 (so that lane counts of 8 and 16 take the kernels' per-XCD lane order), S from 1 to
 about 2200 (ragged tails, single partial blocks), and random, dense causal,
 fixed-segment or GPU-built topology schedules.  Each case checks the forward
-output, and for D <= 128 the lse and the three gradients, to the bars of the
-other parity tests: forward max abs error <= 2e-3 (fp16) / 1e-2 (bf16); lse
+output, the lse and the three gradients, to the bars of the other parity
+tests: forward max abs error <= 2e-3 (fp16) / 1e-2 (bf16); lse
 within 1e-3 (fp16) / 4e-3 (bf16); gradients within 2e-3 / 1e-2 of each
 gradient's largest value.  The configuration of case c comes from a generator
 seeded with c, so every case is reproducible on its own.
@@ -64,11 +64,6 @@ def test_sweep_case(tsa, case):
     cid = torch.from_numpy(np.asarray(ci, np.int32)).to(DEV)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     out, lse = tsa.scheduled_attention(qd, kd, vd, rpd, cid, return_lse=True)
-    if D > 128:
-        ref = oracle.masked_attention(q, k, v, rp, ci)
-        err = float(np.abs(out.double().cpu().numpy() - ref).max())
-        assert err <= TOL[dtype], (label, err)
-        return
     do = workloads.random_normal((B, H, S, D), dtype, 8500 + case)
     rdq, rdk, rdv, rout, rlse = oracle.attention_backward(q, k, v, do, rp, ci)
     err = float(np.abs(out.double().cpu().numpy() - rout).max())
