@@ -9,8 +9,9 @@ unwritten memory, which these tests fill with NaN first).
 
 Cases: [2, 4, 1088, D] for D = 32, 64, 128, 256 (17 query blocks, a ragged
 count), forward output and lse; 16 and 32 lanes at D = 128, where each XCD runs
-its lanes two at a time (64- and 32-row blocks); the backward's dq, dk and dv at [1, 8, 1024, 64]
-and [2, 4, 640, 128]; and the batched workload (64 lanes x 4096 rows) in full.
+its lanes two at a time (64- and 32-row blocks); the backward's dq, dk and dv at [1, 8, 1024, 64],
+[2, 4, 640, D] for D = 32, 128, 256 and [1, 8, 700, 256] (two head-dim halves per
+key or query block); and the batched workload (64 lanes x 4096 rows) in full.
 One CSR, built from lane (0, 0)'s keys, is shared by every lane (PR page
 "Add topology-derived sparse attention kernel", Summary, third bullet).
 Bars as in the other parity tests: forward max abs error <= 2e-3 (fp16) /
@@ -97,7 +98,8 @@ def test_forward_lane_pairs_per_xcd_every_output(tsa, shape, dtype, block):
 
 
 @pytest.mark.parametrize("shape,dtype", [((1, 8, 1024, 64), "bf16"), ((2, 4, 640, 128), "fp16"),
-                                         ((2, 4, 640, 32), "bf16")])
+                                         ((2, 4, 640, 32), "bf16"), ((2, 4, 640, 256), "bf16"),
+                                         ((1, 8, 700, 256), "fp16")])
 def test_backward_every_lane_and_row(tsa, shape, dtype):
     w = workloads.Workload("lanes_bwd", shape, dtype, seed=700 + shape[-1])
     q, k, v = workloads.make_qkv(w)
