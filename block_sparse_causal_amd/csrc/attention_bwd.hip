@@ -183,6 +183,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dq_kernel(
   constexpr int kStageBytes = 2 * kTileBytes;  // [K tile | V tile]
   // Head dims of dQ written here: all D, or the half of D = 256 that blockIdx.y
   // selects (S and dP always contract over all D).
+  static_assert(DO == D || 2 * DO == D, "a workgroup writes all the head dims or one of two halves");
   constexpr int kTilesO = DO / 32;
   const int d0 = DO < D ? (int)blockIdx.y * DO : 0;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kStageBytes];
@@ -647,6 +648,7 @@ __global__ __launch_bounds__(kThreads) void attention_bwd_dkdv_kernel(
   constexpr int kFillOps = G::kTileOps + 1;
   // Head dims of dK and dV written here: all D, or the half of D = 256 that
   // blockIdx.y selects (S and dP always contract over all D).
+  static_assert(DO == D || 2 * DO == D, "a workgroup writes all the head dims or one of two halves");
   constexpr int kTilesO = DO / 32;
   const int d0 = DO < D ? (int)blockIdx.y * DO : 0;
   // The ring, reused after the loop for the merge of the two query halves.
